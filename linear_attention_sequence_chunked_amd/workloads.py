@@ -1,0 +1,108 @@
+"""Seeded synthetic inputs for the gated-delta-rule chunk forward.
+
+This module draws random inputs and nothing else: it holds none of the
+recurrence's arithmetic, so both the HIP path's tests/benchmark and the fp64
+oracle can take their inputs from it.
+
+Shapes follow the operator contract of "OpenGDN 0.1.0" (section "Core operator
+reference"): q, k [B,T,H,K], v [B,T,H,V], alpha, beta [B,T,H], state [B,H,V,K].
+Distributions follow the workloads the pages describe: q and k are L2-normalised
+over the key axis (the mixer of "OpenGDN 0.1.0", section "Mixer"), beta is a
+sigmoid, and alpha is either a sigmoid (OpenGDN's documented default) or the
+decay exp(-0.1 * softplus(x)), a Mamba2-style log-gate of the kind "Sparse Delta
+Memory: layer and kernels" uses in "What the layer computes".
+
+All draws are made on the CPU with ``torch.Generator().manual_seed(seed)`` in
+float32, in a fixed order (q, k, v, alpha logits, beta logits, then the initial
+state and the output gradient when requested); q, k, v are then rounded to the
+requested dtype, so every consumer sees identical values.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    K: int
+    V: int
+    chunk: int
+    dtype: torch.dtype
+    gate: str               # "sigmoid" or "decay"
+    s0_std: float | None = None
+    with_do: bool = False
+    split_at: int | None = None  # streaming seam for the long-context case
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+
+# The five workloads.  Seeds equal the workload number.
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 1, 64, 2, 16, 16, 16, torch.float32, "sigmoid", seed=1,
+                          note="tiny fp32, B1 T64 H2 K=V=16, chunk 16"),
+    "mid_bf16": Workload("mid_bf16", 2, 2048, 4, 128, 128, 64, torch.bfloat16, "decay", seed=2,
+                         note="mid bf16 forward, B2 T2048 H4 K=V=128, chunk 64"),
+    "train_bf16": Workload("train_bf16", 8, 4096, 6, 128, 128, 64, torch.bfloat16, "decay", seed=3,
+                           note="training-shape forward, B8 T4096 H6 K=V=128, chunk 64"),
+    "fwdbwd_bf16": Workload("fwdbwd_bf16", 4, 2048, 6, 128, 128, 64, torch.bfloat16, "decay",
+                            with_do=True, seed=4,
+                            note="forward+backward shape, B4 T2048 H6 K=V=128, chunk 64"),
+    "long_bf16": Workload("long_bf16", 1, 32768, 16, 128, 128, 64, torch.bfloat16, "decay",
+                          s0_std=0.02, split_at=16384, seed=5,
+                          note="long-context streaming prefill, B1 T32768 H16 K=V=128, "
+                               "chunk 64, S0 ~ 0.02 N(0,1), two 16384-token calls"),
+}
+
+
+def make_inputs(B: int, T: int, H: int, K: int, V: int, dtype=torch.bfloat16,
+                seed: int = 0, gate: str = "decay", s0_std: float | None = None,
+                with_do: bool = False) -> dict:
+    """Draw one seeded input set on the CPU.
+
+    Returns a dict with q, k, v (``dtype``), alpha, beta (float32 [B,T,H]),
+    initial_state (float32 [B,H,V,K] or None) and d_o (``dtype`` or None).
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    q = torch.randn(B, T, H, K, generator=g, dtype=torch.float32)
+    k = torch.randn(B, T, H, K, generator=g, dtype=torch.float32)
+    v = torch.randn(B, T, H, V, generator=g, dtype=torch.float32)
+    a_logit = torch.randn(B, T, H, generator=g, dtype=torch.float32)
+    b_logit = torch.randn(B, T, H, generator=g, dtype=torch.float32)
+    s0 = None
+    if s0_std is not None:
+        s0 = torch.randn(B, H, V, K, generator=g, dtype=torch.float32) * float(s0_std)
+    d_o = None
+    if with_do:
+        d_o = torch.randn(B, T, H, V, generator=g, dtype=torch.float32).to(dtype)
+    # unit-norm queries and keys along the key axis, normalised in float32
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    if gate == "sigmoid":
+        alpha = torch.sigmoid(a_logit)
+    elif gate == "decay":
+        alpha = torch.exp(-0.1 * torch.nn.functional.softplus(a_logit))
+    else:
+        raise ValueError("gate must be 'sigmoid' or 'decay'")
+    beta = torch.sigmoid(b_logit)
+    return {
+        "q": q.to(dtype).contiguous(), "k": k.to(dtype).contiguous(), "v": v.to(dtype).contiguous(),
+        "alpha": alpha.contiguous(), "beta": beta.contiguous(),
+        "initial_state": None if s0 is None else s0.contiguous(),
+        "d_o": d_o,
+    }
+
+
+def workload_inputs(w: Workload | str, **overrides) -> dict:
+    """Inputs of a named workload (overrides may shrink T or B for sampled checks)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    p = dict(B=w.B, T=w.T, H=w.H, K=w.K, V=w.V, dtype=w.dtype, seed=w.seed, gate=w.gate,
+             s0_std=w.s0_std, with_do=w.with_do)
+    p.update(overrides)
+    return make_inputs(**p)
