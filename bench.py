@@ -1,0 +1,168 @@
+"""Benchmark of the chunkwise gated-delta-rule forward on one MI355X.
+
+One step = one gdn_chunk_fwd call over the training-shape workload
+(B=8, T=4096, H=6, K=V=128, chunk 64, bf16 q/k/v/o, fp32 gates and state),
+inputs already resident in HBM.  Three input sets are rotated so that the
+256 MB Infinity Cache cannot serve a repeat of the previous step's inputs.
+
+Prints ONE JSON line (rank 0) with throughput in tokens/s, the roofline of the
+kernel, and the fp64 CPU oracle timed on the host as a reported baseline.
+The run is correctness-gated: the GPU output of input set 0 must match the
+oracle (relative L2 <= 2e-2) before any number is printed.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "GDN chunk fwd tokens/s + % bf16 MFMA peak at B8·T4096·H6·d128"
+
+
+def algorithmic_bytes(B, T, H, K, V, esz=2, with_s0=False):
+    """HBM bytes one forward must move: q, k, v read, o written, gates read, final state written."""
+    tok = B * T * H
+    by = tok * (2 * K + 2 * V) * esz + tok * 2 * 4 + B * H * V * K * 4
+    if with_s0:
+        by += B * H * V * K * 4
+    return by
+
+
+def algorithmic_flops(B, T, H, K, V, C):
+    """Structural FLOPs per token-head of the chunk algorithm (triangular products at
+    their structural size, the inverse as C^3/3 per chunk):
+    (3C-1)K + 2CV + 6KV + C^2/3."""
+    per = (3 * C - 1) * K + 2 * C * V + 6 * K * V + C * C / 3.0
+    return per * B * T * H
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gate", action="store_true", help="skip the oracle correctness gate")
+    ap.add_argument("--workload", default="train_bf16")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the (batch, head) streams are independent, so "
+              "a multi-GPU run is one of these per GPU with no communication; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_sequence_chunked_amd import chunk_fwd
+    from linear_attention_sequence_chunked_amd.workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, T, H, K, V, C = w.B, w.T, w.H, w.K, w.V, w.chunk
+    nsets = 3
+    cpu_sets = [workload_inputs(w, seed=w.seed + 1000 * i) for i in range(nsets)]
+    sets = [{n: (t.to(dev) if t is not None else None) for n, t in s.items()} for s in cpu_sets]
+    outs = [torch.empty(B, T, H, V, dtype=w.dtype, device=dev) for _ in range(nsets)]
+    states = [torch.empty(B, H, V, K, dtype=torch.float32, device=dev) for _ in range(nsets)]
+
+    def step(i):
+        s = sets[i % nsets]
+        chunk_fwd(s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["initial_state"], chunk=C,
+                  out=outs[i % nsets], final_state=states[i % nsets])
+
+    # correctness gate on input set 0
+    gate = None
+    if not args.no_gate:
+        import oracle
+        step(0)
+        torch.cuda.synchronize()
+        c = cpu_sets[0]
+        ro, rs = oracle.fwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["initial_state"])
+        eo = float(np.linalg.norm(outs[0].double().cpu().numpy() - ro) / np.linalg.norm(ro))
+        es = float(np.linalg.norm(states[0].double().cpu().numpy() - rs) / np.linalg.norm(rs))
+        gate = {"rel_l2_o": eo, "rel_l2_final_state": es, "tol": 2e-2}
+        if not (eo <= 2e-2 and es <= 2e-2):
+            print("correctness gate failed: %s" % json.dumps(gate), file=sys.stderr)
+            sys.exit(1)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)   # the stream the kernel is launched on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = total_ms / args.steps
+    kern_ms = float(per_launch.mean())
+
+    tokens = B * T
+    value = tokens / (ms_per_step / 1e3)
+    abytes = algorithmic_bytes(B, T, H, K, V, esz=2 if w.dtype == torch.bfloat16 else 4,
+                               with_s0=w.s0_std is not None)
+    aflops = algorithmic_flops(B, T, H, K, V, C)
+    achieved_gbs = abytes / (kern_ms / 1e3) / 1e9
+    tflops = aflops / (kern_ms / 1e3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        c = cpu_sets[0]
+        threads = oracle.default_threads()
+        used = min(threads, B * H)
+        # the whole workload: every (b, h) stream over all T tokens
+        t0 = time.perf_counter()
+        oracle.fwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["initial_state"], nthreads=used)
+        dt = time.perf_counter() - t0
+        cpu = {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+               "sample": "whole workload (all %d streams x %d tokens), fp64 token loop, %.2f s"
+                         % (B * H, T, dt)}
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s: B=%d T=%d H=%d K=%d V=%d chunk=%d, inputs resident in HBM, "
+                               "3 rotating input sets" % (w.name, B, T, H, K, V, C),
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": K,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel_ms": kern_ms, "algorithmic_bytes": abytes},
+        "mfma": {"tflops_algorithmic": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flops": aflops},
+        "cpu_baseline": cpu,
+        "gate": gate,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,113 @@
+/*
+ * gdn.h -- C ABI of the chunkwise gated-delta-rule forward for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation.  For every batch b and head h, with state S of shape [V, K]:
+ *
+ *     S <- initial_state[b,h]            (zeros when initial_state is NULL)
+ *     for t = 0 .. T-1:
+ *         S      <- alpha_t S (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *         o[b,t,h] = S q_t
+ *     final_state[b,h] <- S
+ *
+ * This is the gated delta rule of "Sparse Delta Memory: layer and kernels"
+ * (sparse-delta-memory 2.0.0), section "What the layer computes" -- decay the
+ * state, read it with k, write beta times the prediction error, read the output
+ * with q from the updated state -- in the dense limit its section "Product-key
+ * top-k" describes, with the operator contract (shapes, optional state,
+ * streaming continuation) of "OpenGDN 0.1.0", section "Core operator reference".
+ * It is computed by the extended-WY / UT chunk decomposition those pages name
+ * (cumulative log-gates, decay-weighted K K^T and Q K^T Gram matrices, the solve
+ * (I + tril(beta A, -1))^-1, the W/U build, then a sequential inter-chunk state
+ * update and readout); chunking changes results only by rounding.
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers are DEVICE pointers (memory from hipMalloc or a torch CUDA
+ *    tensor on the current device), except where stated.  The caller owns every
+ *    buffer; the library allocates no device memory for these calls.
+ *  - Tensors are dense, contiguous and row-major, each at least 16-byte aligned:
+ *        q, k            [B, T, H, K]   element type `dtype`
+ *        v, o            [B, T, H, V]   element type `dtype`
+ *        alpha, beta     [B, T, H]      float32
+ *        initial_state,
+ *        final_state     [B, H, V, K]   float32
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *    enqueued on it and the call returns without synchronising the host.
+ *  - All argument checks happen on the host BEFORE any device work; on an error
+ *    nothing is enqueued and no output is touched.  There is no fallback path:
+ *    an unsupported shape or dtype is an error, never a slower kernel.
+ *  - Domain (not checked on the device): 0 < alpha <= 1, beta finite.  NaN/Inf
+ *    inputs propagate; nothing is clipped.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define GDN_API __attribute__((visibility("default")))
+#else
+#define GDN_API
+#endif
+
+typedef enum gdn_status {
+    GDN_SUCCESS = 0,
+    GDN_ERROR_INVALID_VALUE = 1, /* NULL required pointer, non-positive size, misaligned pointer,
+                                    or overlapping input/output buffers */
+    GDN_ERROR_NOT_SUPPORTED = 2, /* valid, but outside the compiled kernel set (see below) */
+    GDN_ERROR_LAUNCH = 3         /* the HIP runtime refused the launch */
+} gdn_status_t;
+
+typedef enum gdn_dtype {
+    GDN_DTYPE_F32 = 0,  /* IEEE float32 q, k, v, o */
+    GDN_DTYPE_BF16 = 1  /* bfloat16 q, k, v, o; state arithmetic stays float32 */
+} gdn_dtype_t;
+
+/* ABI version of the loaded library (GDN_ABI_VERSION at build time). */
+GDN_API int gdn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (host memory, never freed). */
+GDN_API const char *gdn_status_string(gdn_status_t status);
+
+/*
+ * gdn_chunk_fwd -- forward of the gated delta rule over T tokens.
+ *
+ *   q, k           [B,T,H,K] dtype        queries and keys (read only)
+ *   v              [B,T,H,V] dtype        values (read only)
+ *   alpha, beta    [B,T,H]   float32      decay gate and write strength (read only)
+ *   initial_state  [B,H,V,K] float32      state before token 0, or NULL for zeros
+ *   o              [B,T,H,V] dtype        output, o[b,t,h] = S_t q_t (written)
+ *   final_state    [B,H,V,K] float32      state after token T-1, or NULL to skip
+ *   B, T, H        batch, tokens, heads   B >= 1, H >= 1, T >= 1
+ *   K, V           key and value widths   each one of 16, 32, 64, 128
+ *   chunk          tokens per chunk       16, 32 or 64; T need not be a multiple
+ *                                         (the last chunk is shorter)
+ *   dtype          element type of q, k, v, o
+ *   stream         hipStream_t as void*
+ *
+ * final_state may be the same pointer as initial_state (the state advances in
+ * place); any other overlap between an output and any other buffer is rejected
+ * when it is visible from the pointers and sizes.  Passing final_state back as
+ * the next call's initial_state continues the stream ("OpenGDN 0.1.0", section
+ * "Core operator reference").  The result is bitwise reproducible run to run:
+ * every output element has one writer and every sum runs in a fixed order.
+ * Sizes: B*T*H*max(K,V) must stay below 2^31 elements.
+ */
+GDN_API gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta,
+                           const float *initial_state,
+                           void *o, float *final_state,
+                           int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                           int64_t chunk, gdn_dtype_t dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

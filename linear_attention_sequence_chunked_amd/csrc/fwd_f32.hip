@@ -1,0 +1,209 @@
+// Chunkwise gated-delta-rule forward, float32 inputs: scalar fp32 kernel.
+//
+// One workgroup owns one (batch, head, value-slice) stream: the rows
+// [v0, v0 + VS) of the [V, K] state stay in LDS (fp32) for the whole sequence,
+// and the chunks are walked in order.  Per chunk of n <= C tokens (the steps of
+// the extended-WY / UT decomposition; "Sparse Delta Memory: layer and kernels",
+// "What the layer computes", and "OpenGDN 0.1.0", "Core operator reference"):
+//
+//   g_r  = sum_{i<=r} ln alpha_i,  gam = exp(g)                 (cumulative log-gates)
+//   A_ri = beta_r exp(g_r - g_i) k_r.k_i  for i < r              (decayed K K^T, strictly causal)
+//   Tm   = (I + A)^-1                                            (unit lower-triangular solve)
+//   R    = diag(beta) Vs - diag(beta gam) K S^T                  (right-hand side)
+//   U    = Tm R                                                  (corrected writes)
+//   P_ri = exp(g_r - g_i) q_r.k_i         for i <= r             (decayed Q K^T, causal)
+//   O    = diag(gam) Q S^T + P U                                 (readout)
+//   S   <- gam_n S + U^T diag(gam_n / gam) K                     (inter-chunk state update)
+//
+// where S is the chunk-start state slice.  Every exponent is g_r - g_i with
+// r >= i (or g_n - g_i), so it is <= 0 and never overflows; the masked upper
+// entries are never exponentiated.  All products and sums are fp32 in a fixed
+// order, so the result is bitwise reproducible.
+#include "launch.h"
+
+#include <hip/hip_bf16.h>
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(float x) {
+  return __float2bfloat16(x);  // round to nearest even
+}
+
+template <typename TIn>
+__global__ void __launch_bounds__(kThreads)
+fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+               const float* __restrict__ alpha, const float* __restrict__ beta,
+               const float* __restrict__ s0, TIn* __restrict__ o, float* __restrict__ s_final,
+               int T, int H, int K, int V, int C, int VS) {
+  extern __shared__ float lds[];
+  float* sq = lds;                 // [C][K]
+  float* sk = sq + C * K;          // [C][K]
+  float* sv = sk + C * K;          // [C][VS]
+  float* sA = sv + C * VS;         // [C][C]  A, later P
+  float* sT = sA + C * C;          // [C][C]
+  float* sR = sT + C * C;          // [C][VS] R, later Z = diag(gam) Q S^T
+  float* sU = sR + C * VS;         // [C][VS]
+  float* sS = sU + C * VS;         // [VS][K] state slice
+  float* sg = sS + VS * K;         // [C] cumulative log gate
+  float* sgam = sg + C;            // [C] exp(g)
+  float* sb = sgam + C;            // [C] beta
+
+  const int tid = threadIdx.x;
+  const int v0 = blockIdx.x * VS;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
+
+  for (int i = tid; i < VS * K; i += kThreads) sS[i] = s0 ? s0[state_base + i] : 0.0f;
+
+  for (int t0 = 0; t0 < T; t0 += C) {
+    const int n = min(C, T - t0);
+    __syncthreads();  // previous chunk finished with the tiles
+    for (int i = tid; i < n * K; i += kThreads) {
+      const int r = i / K, c = i - r * K;
+      const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + c;
+      sq[i] = to_f32(q[off]);
+      sk[i] = to_f32(k[off]);
+    }
+    for (int i = tid; i < n * VS; i += kThreads) {
+      const int r = i / VS, c = i - r * VS;
+      sv[i] = to_f32(v[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + c]);
+    }
+    if (tid < n) {
+      const size_t go = ((size_t)b * T + t0 + tid) * H + h;
+      sg[tid] = logf(alpha[go]);
+      sb[tid] = beta[go];
+    }
+    __syncthreads();
+    if (tid == 0) {  // cumulative log-gate, serial and in token order
+      float acc = 0.0f;
+      for (int r = 0; r < n; ++r) {
+        acc += sg[r];
+        sg[r] = acc;
+      }
+    }
+    __syncthreads();
+    if (tid < n) sgam[tid] = expf(sg[tid]);
+    // A (strictly lower), decay and beta applied; upper part zero.
+    for (int i = tid; i < n * n; i += kThreads) {
+      const int r = i / n, j = i - r * n;
+      float val = 0.0f;
+      if (j < r) {
+        float d = 0.0f;
+        for (int c = 0; c < K; ++c) d = fmaf(sk[r * K + c], sk[j * K + c], d);
+        val = sb[r] * expf(sg[r] - sg[j]) * d;
+      }
+      sA[r * C + j] = val;
+    }
+    // R = diag(beta) V - diag(beta gam) K S^T  and  Z = diag(gam) Q S^T (Z kept in sU for now)
+    __syncthreads();
+    for (int i = tid; i < n * VS; i += kThreads) {
+      const int r = i / VS, c = i - r * VS;
+      float dk = 0.0f, dq = 0.0f;
+      for (int e = 0; e < K; ++e) {
+        const float s = sS[c * K + e];
+        dk = fmaf(sk[r * K + e], s, dk);
+        dq = fmaf(sq[r * K + e], s, dq);
+      }
+      sR[r * VS + c] = sb[r] * sv[r * VS + c] - sb[r] * sgam[r] * dk;
+      sU[r * VS + c] = sgam[r] * dq;
+    }
+    // Tm = (I + A)^-1 by forward substitution, one column per thread.
+    if (tid < n) {
+      const int j = tid;
+      for (int r = 0; r < j; ++r) sT[r * C + j] = 0.0f;
+      sT[j * C + j] = 1.0f;
+      for (int r = j + 1; r < n; ++r) {
+        float s = 0.0f;
+        for (int i = j; i < r; ++i) s = fmaf(sA[r * C + i], sT[i * C + j], s);
+        sT[r * C + j] = -s;
+      }
+    }
+    __syncthreads();
+    // P (lower incl. diagonal) overwrites A; U = Tm R goes to sv (values no longer needed).
+    for (int i = tid; i < n * n; i += kThreads) {
+      const int r = i / n, j = i - r * n;
+      float val = 0.0f;
+      if (j <= r) {
+        float d = 0.0f;
+        for (int c = 0; c < K; ++c) d = fmaf(sq[r * K + c], sk[j * K + c], d);
+        val = expf(sg[r] - sg[j]) * d;
+      }
+      sA[r * C + j] = val;
+    }
+    for (int i = tid; i < n * VS; i += kThreads) {
+      const int r = i / VS, c = i - r * VS;
+      float u = 0.0f;
+      for (int j = 0; j <= r; ++j) u = fmaf(sT[r * C + j], sR[j * VS + c], u);
+      sv[r * VS + c] = u;
+    }
+    __syncthreads();
+    // O = Z + P U, stored.
+    for (int i = tid; i < n * VS; i += kThreads) {
+      const int r = i / VS, c = i - r * VS;
+      float acc = sU[r * VS + c];
+      for (int j = 0; j <= r; ++j) acc = fmaf(sA[r * C + j], sv[j * VS + c], acc);
+      o[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + c] = from_f32<TIn>(acc);
+    }
+    // S <- gam_n S + U^T diag(gam_n / gam) K
+    const float gn = sg[n - 1];
+    const float gam_n = sgam[n - 1];
+    for (int i = tid; i < VS * K; i += kThreads) {
+      const int c = i / K, e = i - c * K;
+      float acc = gam_n * sS[i];
+      for (int j = 0; j < n; ++j) acc = fmaf(sv[j * VS + c] * expf(gn - sg[j]), sk[j * K + e], acc);
+      sS[i] = acc;
+    }
+  }
+  __syncthreads();
+  if (s_final)
+    for (int i = tid; i < VS * K; i += kThreads) s_final[state_base + i] = sS[i];
+}
+
+template <typename TIn>
+hipError_t launch_scalar(const FwdArgs& a, hipStream_t stream) {
+  const int VS = a.V < 16 ? a.V : 16;
+  const int C = a.chunk;
+  const size_t lds = sizeof(float) * (size_t)(2 * C * a.K + C * VS + 2 * C * C + 2 * C * VS +
+                                              VS * a.K + 3 * C);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)fwd_f32_kernel<TIn>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid(a.V / VS, a.H, a.B);
+  hipLaunchKernelGGL(fwd_f32_kernel<TIn>, grid, dim3(kThreads), lds, stream,
+                     static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                     static_cast<const TIn*>(a.v), a.alpha, a.beta, a.s0,
+                     static_cast<TIn*>(a.o), a.s_final, a.T, a.H, a.K, a.V, C, VS);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  return launch_scalar<float>(a, stream);
+}
+
+hipError_t launch_fwd_bf16_scalar(const FwdArgs& a, hipStream_t stream) {
+  return launch_scalar<__hip_bfloat16>(a, stream);
+}
+
+}  // namespace gdn
+
+namespace gdn {
+// Bfloat16 entry until the MFMA kernel replaces it.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+  return launch_fwd_bf16_scalar(a, stream);
+}
+bool fwd_bf16_supported(int, int, int) { return true; }
+}  // namespace gdn

@@ -1,0 +1,106 @@
+// C-ABI layer of libgdn: host-side argument checks, then one kernel launch on
+// the caller's stream.  Every check runs before any device work, so a failing
+// call enqueues nothing and touches no output.  There is exactly one kernel per
+// dtype and no fallback: a shape outside the compiled set is an error.
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "launch.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool width_supported(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status_t status) {
+  switch (status) {
+    case GDN_SUCCESS:
+      return "success";
+    case GDN_ERROR_INVALID_VALUE:
+      return "invalid value: a required pointer is NULL, a size is not positive, a pointer is "
+             "not 16-byte aligned, or an output overlaps another buffer";
+    case GDN_ERROR_NOT_SUPPORTED:
+      return "not supported: K and V must be 16, 32, 64 or 128, chunk 16, 32 or 64, dtype F32 "
+             "or BF16, and B*T*H*max(K,V) below 2^31";
+    case GDN_ERROR_LAUNCH:
+      return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* initial_state, void* o,
+                           float* final_state, int64_t B, int64_t T, int64_t H, int64_t K,
+                           int64_t V, int64_t chunk, gdn_dtype_t dtype, void* stream) {
+  if (!q || !k || !v || !alpha || !beta || !o) return GDN_ERROR_INVALID_VALUE;
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {q, k, v, alpha, beta, initial_state, o, final_state};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERROR_NOT_SUPPORTED;
+  if (!width_supported(K) || !width_supported(V)) return GDN_ERROR_NOT_SUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
+  const int64_t maxd = K > V ? K : V;
+  if (B > (INT64_C(1) << 31) || T > (INT64_C(1) << 31) || H > (INT64_C(1) << 31) ||
+      B * T > (INT64_C(1) << 31) || B * T * H * maxd >= (INT64_C(1) << 31))
+    return GDN_ERROR_NOT_SUPPORTED;
+
+  const int64_t esz = dtype == GDN_DTYPE_F32 ? 4 : 2;
+  const Range rq = range_of(q, B * T * H * K * esz), rk = range_of(k, B * T * H * K * esz),
+              rv = range_of(v, B * T * H * V * esz), ra = range_of(alpha, B * T * H * 4),
+              rb = range_of(beta, B * T * H * 4), ro = range_of(o, B * T * H * V * esz);
+  const int64_t state_bytes = B * H * V * K * 4;
+  const Range inputs[] = {rq, rk, rv, ra, rb};
+  for (const Range& r : inputs)
+    if (overlaps(ro, r)) return GDN_ERROR_INVALID_VALUE;
+  if (initial_state && overlaps(ro, range_of(initial_state, state_bytes)))
+    return GDN_ERROR_INVALID_VALUE;
+  if (final_state) {
+    const Range rf = range_of(final_state, state_bytes);
+    for (const Range& r : inputs)
+      if (overlaps(rf, r)) return GDN_ERROR_INVALID_VALUE;
+    if (overlaps(rf, ro)) return GDN_ERROR_INVALID_VALUE;
+    if (initial_state && initial_state != final_state &&
+        overlaps(rf, range_of(initial_state, state_bytes)))
+      return GDN_ERROR_INVALID_VALUE;
+  }
+
+  gdn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.s0 = initial_state;
+  a.o = o;
+  a.s_final = final_state;
+  a.B = static_cast<int>(B);
+  a.T = static_cast<int>(T);
+  a.H = static_cast<int>(H);
+  a.K = static_cast<int>(K);
+  a.V = static_cast<int>(V);
+  a.chunk = static_cast<int>(chunk);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = dtype == GDN_DTYPE_F32 ? gdn::launch_fwd_f32(a, s) : gdn::launch_fwd_bf16(a, s);
+  return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
+}
+
+}  // extern "C"

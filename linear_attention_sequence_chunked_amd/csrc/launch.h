@@ -1,0 +1,31 @@
+// Internal launch interface between the C-ABI layer (gdn_api.hip) and the
+// kernel translation units.  Not installed; the public interface is include/gdn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// One forward problem, already validated by the C-ABI layer.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* s0;  // may be null (zeros)
+  void* o;
+  float* s_final;   // may be null (skip)
+  int B, T, H, K, V, chunk;
+};
+
+// Float32 q/k/v/o: scalar fp32 kernel (exact fp32 products and sums).
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+// Bfloat16 q/k/v/o: bf16 MFMA kernel with fp32 accumulation and fp32 state.
+// Returns hipErrorInvalidValue for a shape outside its compiled set.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+bool fwd_bf16_supported(int K, int V, int chunk);
+
+}  // namespace gdn

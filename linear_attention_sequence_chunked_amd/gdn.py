@@ -1,0 +1,140 @@
+"""Python binding of libgdn (ctypes).  Argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI declared
+in ``include/gdn.h``; this module checks tensors, allocates outputs with torch
+(device memory and streams are all torch is used for), and forwards raw device
+pointers plus the current HIP stream.  If the built library is missing it raises
+at load time: there is no CPU or PyTorch fallback.
+
+Operator contract ("OpenGDN 0.1.0", section "Core operator reference"): q, k
+[B,T,H,K], v [B,T,H,V], alpha, beta [B,T,H], state [B,H,V,K]; feeding the
+returned final state back as ``initial_state`` continues the stream exactly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_SUCCESS = 0
+GDN_ERROR_INVALID_VALUE = 1
+GDN_ERROR_NOT_SUPPORTED = 2
+GDN_ERROR_LAUNCH = 3
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+
+_DTYPES = {torch.float32: GDN_DTYPE_F32, torch.bfloat16: GDN_DTYPE_BF16}
+
+# every symbol the header declares, with its ctypes signature
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+SIGNATURES = {
+    "gdn_abi_version": (ctypes.c_int, []),
+    "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gdn_chunk_fwd": (ctypes.c_int, [_VP] * 8 + [_I64] * 6 + [ctypes.c_int, _VP]),
+}
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgdn.so (built ahead of time by ``build.build()``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(
+                "libgdn.so is not built (%s); run __graft_entry__.build() or "
+                "python -m linear_attention_sequence_chunked_amd.build" % path)
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return load_library().gdn_status_string(int(code)).decode()
+
+
+def _raise_for(code: int, what: str):
+    if code == GDN_SUCCESS:
+        return
+    msg = "%s: %s" % (what, status_string(code))
+    if code == GDN_ERROR_INVALID_VALUE:
+        raise ValueError(msg)
+    if code == GDN_ERROR_NOT_SUPPORTED:
+        raise NotImplementedError(msg)
+    raise GdnError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, *,
+              out=None, final_state=None, want_final_state: bool = True, stream=None):
+    """Gated-delta-rule forward through ``gdn_chunk_fwd``.
+
+    Returns ``(o, final_state)``; ``final_state`` is None when
+    ``want_final_state`` is False.  ``final_state`` may be passed as the same
+    tensor as ``initial_state`` to advance the state in place.  The call is
+    asynchronous on ``stream`` (default: torch's current stream of q's device).
+    """
+    lib = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B,T,H,K]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    if q.dtype not in _DTYPES:
+        raise NotImplementedError("dtype %s is not supported (float32 or bfloat16)" % q.dtype)
+    B, T, H, K = q.shape
+    if v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B,T,H,V]")
+    V = v.shape[-1]
+    _check(k, "k", (B, T, H, K), q.dtype, dev)
+    _check(v, "v", (B, T, H, V), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check(q, "q", (B, T, H, K), q.dtype, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, V, K), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", (B, T, H, V), q.dtype, dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, H, V, K), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (B, H, V, K), torch.float32, dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(initial_state), _ptr(out), _ptr(final_state),
+                               B, T, H, K, V, int(chunk), _DTYPES[q.dtype],
+                               ctypes.c_void_p(s.cuda_stream))
+    _raise_for(rc, "gdn_chunk_fwd")
+    return out, final_state
