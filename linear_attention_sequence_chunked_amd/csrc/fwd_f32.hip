@@ -194,16 +194,6 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
   return launch_scalar<float>(a, stream);
 }
 
-hipError_t launch_fwd_bf16_scalar(const FwdArgs& a, hipStream_t stream) {
-  return launch_scalar<__hip_bfloat16>(a, stream);
-}
 
 }  // namespace gdn
 
-namespace gdn {
-// Bfloat16 entry until the MFMA kernel replaces it.
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  return launch_fwd_bf16_scalar(a, stream);
-}
-bool fwd_bf16_supported(int, int, int) { return true; }
-}  // namespace gdn
