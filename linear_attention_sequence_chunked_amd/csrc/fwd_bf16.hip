@@ -1,33 +1,51 @@
-// Chunkwise gated-delta-rule forward, bfloat16 inputs: MFMA kernel for gfx950.
+// Chunkwise gated-delta-rule forward, bfloat16 inputs: warp-specialised MFMA
+// kernel for gfx950 (MI355X).
 //
-// One workgroup (4 wavefronts) owns one (batch, head, value-slice) stream: rows
-// [v0, v0 + VS) of the [V, K] state.  The fp32 state lives in MFMA accumulator
-// registers for the whole sequence; the chunks are walked in order.  Per chunk of
-// n <= C tokens, padded to a CP-token tile (padding tokens carry alpha = 1,
-// beta = 0, q = k = v = 0, which leaves every product and the state unchanged),
-// the steps of the extended-WY / UT decomposition are ("Sparse Delta Memory:
-// layer and kernels", section "What the layer computes"; "OpenGDN 0.1.0",
-// section "Core operator reference"):
+// What is computed.  For each (batch, head) stream the state S [V, K] follows
+// S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t
+// ("Sparse Delta Memory: layer and kernels", section "What the layer computes",
+// in its dense limit; shapes and streaming as in "OpenGDN 0.1.0", section "Core
+// operator reference").  It is evaluated chunk by chunk with the extended-WY /
+// UT decomposition.  For a chunk of n <= C tokens (padded to CP rows with
+// alpha = 1, beta = 0, q = k = v = 0, which changes nothing) and chunk-start
+// state S:
 //
-//   gates   g_r = sum_{i<=r} log2 alpha_i  (wavefront scan), gam = 2^g
-//   Gram    A_ri = beta_r 2^(g_r-g_i) k_r.k_i  (i < r),  P_ri = 2^(g_r-g_i) q_r.k_i  (i <= r)
-//   solve   Tm = (I + A)^-1: 16x16 diagonal blocks by fp32 substitution, the
-//           off-diagonal blocks by two levels of block products on MFMA
-//   chain   Y = K S^T, Z = Q S^T           (one bf16 MFMA pass over the state)
+//   gates   g_r  = sum_{i<=r} log2 alpha_i,  gam = 2^g           (wave scan)
+//   Gram    A_ri = beta_r 2^(g_r-g_i) k_r.k_i  (i < r)            (MFMA)
+//           P_ri =        2^(g_r-g_i) q_r.k_i  (i <= r)
+//   solve   Tm = (I + A)^-1: 16x16 diagonal blocks by fp32 substitution,
+//           off-diagonal blocks by two levels of block products (MFMA)
+//   chain   Y = K S^T, Z = Q S^T                                  (MFMA)
 //           U = Tm (diag(beta) Vs - diag(beta gam) Y)
-//           O = diag(gam) Z + P U           (stored as bf16)
-//           S <- gam_n S + (diag(gam_n/gam) U)^T K   (MFMA into the fp32 state)
+//           O = diag(gam) Z + P U          -> o (bf16)
+//           S <- gam_n S + (diag(gam_n/gam) U)^T K                 (MFMA into fp32 S)
 //
-// Every exponent is g_r - g_i with r >= i, or g_n - g_i: never positive.  The
-// Gram matrices accumulate exact bf16 products in fp32; the solve's diagonal
-// blocks are fp32; all other MFMA operands are bf16 with fp32 accumulation.
-// Every output element has one writer and every sum a fixed order, so the result
-// is bitwise reproducible.
+// Every exponent is g_r - g_i with r >= i (or g_n - g_i) and so never positive.
+// Gram products are exact bf16 products summed in fp32; the diagonal solve is
+// fp32; every other operand is bf16 with fp32 accumulation.  Each output element
+// has one writer and each sum a fixed order: results are bitwise reproducible.
 //
-// LDS layouts.  An MFMA operand fragment (16 rows x 32 k) is read either from a
-// row-major [row][k] array with one 16-byte read per lane, or from a [k][row]
-// array with two gfx950 transpose reads (ds_read_b64_tr_b16).  Accumulator tiles
-// are always written transposed ([col][row], 8 bytes per lane).
+// Organisation.  One workgroup of 8 wavefronts owns one (stream, value slice of
+// VS rows) pair and walks the chunks in order.  The state-independent work of a
+// chunk does not wait for the previous chunk, so it is done ahead by other
+// waves while the chain waves run the sequential part:
+//
+//   chain waves (one per 16 value rows): Y, Z, R of chunk x      | U, O, S of chunk x
+//   levels wave:                         off-diagonal Tm of x     |
+//   diag wave:                                                    | diagonal Tm of x+1
+//   Gram waves:                          A, P of chunk x+1        | stage chunk x+2 in LDS,
+//                                                                 | load chunk x+3
+//
+// Two workgroup barriers per chunk separate the phases.  Rings of LDS slots
+// carry each chunk's tiles from stage to use: keys 3 deep (read from staging
+// until the state update two iterations later), queries, values, P, Tm 2 deep.
+//
+// LDS layouts.  An MFMA operand (16 rows x 32 k) is read either from a [row][k]
+// array (one 16-byte read per lane) or from a [k][row] array with two gfx950
+// transpose reads (ds_read_b64_tr_b16).  Accumulator tiles are written
+// transposed ([col][row], 8 bytes per lane).  Key and query tiles are row-major
+// [token][channel] with the 16-byte chunks of each row XOR-swizzled by the row
+// index, so both access patterns spread over all banks without padding.
 #include "launch.h"
 
 namespace gdn {
@@ -39,48 +57,46 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef bf16x4 __attribute__((address_space(3))) lds_bf16x4;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Fragment of rows r0..r0+15, k0..k0+31 from a row-major [row][k] array:
-// lane (g = l/16, s = l%16) receives row r0 + s, k = k0 + 8g .. k0 + 8g + 7.
-__device__ __forceinline__ bf16x8 frag_rows(const bf16* base, int ld, int r0, int k0, int lane) {
-  return *reinterpret_cast<const bf16x8*>(base + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
-}
-
-// Same fragment from a [k][row] array by transpose reads: within each 16-lane
-// group the hardware hands lane 4a+c the c-th 16-bit element of the lanes a,
-// a+4, a+8, a+12.  Source lane s therefore points at row k0 + 8g + s/4 and
-// column r0 + 4(s%4); the second read covers k + 4.
-__device__ __forceinline__ bf16x8 frag_cols(const bf16* base, int ld, int r0, int k0, int lane) {
-  const int s = lane & 15, g = lane >> 4;
-  const bf16* p = base + (k0 + 8 * g + (s >> 2)) * ld + r0 + 4 * (s & 3);
-  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * ld));
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// Accumulator tile (lane holds rows 4g..4g+3 of column s) written transposed:
-// dst[c0 + s][r0 + 4g .. r0 + 4g + 3].
-__device__ __forceinline__ void store_tile_t(bf16* base, int ld, int c0, int r0, f32x4 d, int lane) {
-  const int s = lane & 15, g = lane >> 4;
-  *reinterpret_cast<bf16x4*>(base + (c0 + s) * ld + r0 + 4 * g) =
-      bf16x4{(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]};
-}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
+#pragma unroll
   for (int j = 0; j < 8; ++j) z[j] = (bf16)0.0f;
   return z;
 }
 
-// 16-deep variants for products over one 16-wide block: the lanes that would hold
-// k in [16, 32) read the same (valid) rows as their k in [0, 16) partners and are
-// then zeroed, so the 32-deep MFMA adds exact zeros.
+__device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// Operand fragment of rows r0..r0+15, k0..k0+31 from a row-major [row][k] array
+// (leading dimension ld): lane (g = lane/16, s = lane%16) receives row r0 + s,
+// k = k0 + 8g .. k0 + 8g + 7.
+__device__ __forceinline__ bf16x8 frag_rows(const bf16* base, int ld, int r0, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(base + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+
+// The same fragment from a [k][row] array by transpose reads.  Within each
+// 16-lane group the hardware gives lane 4a+c the c-th 16-bit element read by
+// lanes a, a+4, a+8, a+12; so source lane s points at row k0 + 8g + s/4,
+// column r0 + 4(s%4), and a second read covers k + 4.
+__device__ __forceinline__ bf16x8 frag_cols(const bf16* base, int ld, int r0, int k0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const bf16* p = base + (k0 + 8 * g + (s >> 2)) * ld + r0 + 4 * (s & 3);
+  const bf16x4 lo = tr_read(p), hi = tr_read(p + 4 * ld);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// 16-deep products: lanes that would hold k in [16, 32) read their partner's
+// (valid) rows and are zeroed, so the 32-deep MFMA adds exact zeros.
 __device__ __forceinline__ bf16x8 frag_rows16(const bf16* base, int ld, int r0, int k0, int lane) {
   const bf16x8 f = frag_rows(base, ld, r0, k0 - 16 * ((lane >> 5) & 1), lane);
   return (lane >> 5) ? zero8() : f;
@@ -90,380 +106,587 @@ __device__ __forceinline__ bf16x8 frag_cols16(const bf16* base, int ld, int r0, 
   return (lane >> 5) ? zero8() : f;
 }
 
+// Swizzled [token][channel] tiles (row length KD, 16-byte chunk c stored at c ^ (row & SW)).
+template <int KD>
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int SW = (KD / 8 < 16 ? KD / 8 : 16) - 1;
+  return row * KD + ((((col >> 3) ^ (row & SW))) << 3) + (col & 7);
+}
+template <int KD>
+__device__ __forceinline__ bf16x8 frag_rows_sw(const bf16* base, int r0, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(base + swz<KD>(r0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+template <int KD>
+__device__ __forceinline__ bf16x8 frag_cols_sw(const bf16* base, int c0, int k0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const int row = k0 + 8 * g + (s >> 2), col = c0 + 4 * (s & 3);
+  const bf16x4 lo = tr_read(base + swz<KD>(row, col)), hi = tr_read(base + swz<KD>(row + 4, col));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Accumulator tile (lane holds rows 4g..4g+3 of column s) stored transposed:
+// dst[(c0 + s) * ld + r0 + 4g + e] = d[e], as bf16.
+__device__ __forceinline__ void store_tile_t(bf16* base, int ld, int c0, int r0, f32x4 d, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  *reinterpret_cast<bf16x4*>(base + (c0 + s) * ld + r0 + 4 * g) =
+      bf16x4{(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]};
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load and store (a workgroup-scope fence on all memory),
+// which would stall the prefetch of the next chunks at every barrier; no data
+// passes between the waves of a workgroup through global memory here.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ float bits_f(int x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ int f_bits(float x) { return __builtin_bit_cast(int, x); }
+
+// Inclusive prefix sum over the 64 lanes of a wavefront, in a fixed order:
+// shifts 1, 2, 4, 8 inside each 16-lane row (DPP), then the row totals.
+__device__ __forceinline__ float wave_scan(float x, int lane) {
+  x += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(x), 0x111, 0xf, 0xf, false));
+  x += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(x), 0x112, 0xf, 0xf, false));
+  x += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(x), 0x114, 0xf, 0xf, false));
+  x += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(x), 0x118, 0xf, 0xf, false));
+  const float t0 = bits_f(__builtin_amdgcn_readlane(f_bits(x), 15));
+  const float t1 = bits_f(__builtin_amdgcn_readlane(f_bits(x), 31));
+  const float t2 = bits_f(__builtin_amdgcn_readlane(f_bits(x), 47));
+  const int row = lane >> 4;
+  const float add = row == 0 ? 0.0f : (row == 1 ? t0 : (row == 2 ? t0 + t1 : (t0 + t1) + t2));
+  return x + add;
+}
+
 template <int KD, int VS, int CP>
 struct alignas(16) Smem {
-  static constexpr int LDK = KD + 8;   // q, k tiles [CP][LDK]
-  static constexpr int LDC = CP + 8;   // CP-wide square tiles [CP][LDC]
-  static constexpr int LDV = VS + 8;   // state [KD][LDV]
-  bf16 k[CP * LDK];
-  bf16 q[CP * LDK];
-  bf16 v[CP * VS];
-  bf16 st[KD * LDV];                   // state^T in bf16: st[c][v]
-  bf16 at[CP * LDC];                   // A^T: at[i][r]
-  bf16 pt[CP * LDC];                   // P^T: pt[i][r]
-  bf16 tt[CP * LDC];                   // Tm^T: tt[j][i]
-  bf16 xt[CP * LDC];                   // block-product scratch (transposed)
-  bf16 rt[VS * LDC];                   // R^T: rt[v][j]
-  bf16 ut[VS * LDC];                   // U^T
+  static constexpr int NTB = CP / 16;
+  static constexpr int LDC = CP + 8;   // CP x CP tiles
+  static constexpr int LDV = VS + 8;   // state^T [KD][LDV]
+  static constexpr int LDA = 24;       // packed 16-wide A^T blocks
+  static constexpr int APK = (NTB == 4 ? 96 : 16) * LDA;
+  bf16 k[3][CP * KD];                  // keys, swizzled [token][channel]
+  bf16 q[2][CP * KD];                  // queries, swizzled
+  bf16 v[2][CP * VS];                  // value slice [token][v]
+  float gl[3][CP];                     // cumulative log2 gate
+  float gam[3][CP];                    // 2^g
+  float beta[3][CP];
+  float bg[3][CP];                     // beta * gam
+  float dn[3][CP];                     // gam_n / gam
+  bf16 pt[2][CP * LDC];                // P^T: pt[i][r]
+  bf16 tt[2][CP * LDC];                // Tm^T: tt[j][i]; upper blocks zero (level scratch)
+  bf16 ap[2][APK];                     // off-diagonal A^T blocks used by the levels
+  float ad[NTB * 256];                 // diagonal A blocks, fp32, transposed [c][r]
+  bf16 st[KD * LDV];                   // bf16 state^T: st[c][v]
+  bf16 rt[VS * LDC];                   // R^T, then U^T: [v][token]
   bf16 upt[VS * LDC];                  // (diag(gam_n/gam) U)^T
-  float ad[(CP / 16) * 256];           // fp32 diagonal 16x16 blocks of A, row-major
-  float g[CP];                         // cumulative log2 gate
-  float gam[CP];                       // 2^g
-  float beta[CP];
-  float bg[CP];                        // beta * gam
-  float dn[CP];                        // gam_n / gam
 };
 
-template <int KD, int VS, int CP>
-__global__ void __launch_bounds__(kThreads, 1)
-fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-                const float* __restrict__ alpha, const float* __restrict__ beta,
-                const float* __restrict__ s0, bf16* __restrict__ o, float* __restrict__ s_final,
-                int T, int H, int K, int V, int C) {
-  using SM = Smem<KD, VS, CP>;
-  constexpr int LDK = SM::LDK, LDC = SM::LDC, LDV = SM::LDV;
-  constexpr int NTB = CP / 16;    // token blocks
-  constexpr int NVB = VS / 16;    // value blocks
-  constexpr int NCB = KD / 16;    // key-channel blocks
-  constexpr int NST = NVB * NCB;  // state tiles
-  constexpr int ST_PER_WAVE = (NST + kWaves - 1) / kWaves;
-  __shared__ SM sm;
+// Off-diagonal blocks of Tm = (I + A)^-1 from its diagonal blocks (already in
+// tt) and the packed off-diagonal A^T blocks, in two levels of block products:
+//   level 1: Tm_10 = -Tm_11 (A_10 Tm_00),  Tm_32 = -Tm_33 (A_32 Tm_22)
+//   level 2: Tm_[23][01] = -Tm_[23] (A_[23][01] Tm_[01])
+// Two waves share the work: both compute level 1 (identical values, written
+// twice), then each computes one 16-column block bj = part of level 2.  Scratch
+// tiles live in Tm's upper (zero) blocks and are zeroed again afterwards.
+template <int CP>
+__device__ __forceinline__ void levels_part(bf16* tt, const bf16* ap, int lane, int part) {
+  constexpr int NTB = CP / 16;
+  constexpr int LDC = CP + 8, LDA = 24;
+  if constexpr (NTB == 4) {
+    bf16* scr = tt + (48 - 16 * part) * LDC;  // Tm^T rows [48,64) or [32,48), columns [0,32)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int bi = 2 * pr + 1, bj = 2 * pr;
+      const f32x4 X = mma(frag_cols16(ap + 16 * pr * LDA, LDA, 0, 0, lane),
+                          frag_rows16(tt, LDC, 16 * bj, 16 * bj, lane), zero4());
+      store_tile_t(scr, LDC, 0, 16 * pr, X, lane);
+      const f32x4 Tij = mma(frag_cols16(tt, LDC, 16 * bi, 16 * bi, lane), frag_rows16(scr, LDC, 0, 16 * pr, lane),
+                            zero4());
+      store_tile_t(tt, LDC, 16 * bj, 16 * bi, -Tij, lane);
+    }
+    const int bj = part;
+#pragma unroll
+    for (int bi = 2; bi < 4; ++bi) {
+      const f32x4 X2 = mma(frag_cols(ap + (bi == 2 ? 32 : 64) * LDA, LDA, 0, 0, lane),
+                           frag_rows(tt, LDC, 16 * bj, 0, lane), zero4());
+      store_tile_t(scr, LDC, 0, 16 * (bi - 2), X2, lane);
+    }
+#pragma unroll
+    for (int bi = 2; bi < 4; ++bi) {
+      const f32x4 Tij = mma(frag_cols(tt, LDC, 16 * bi, 32, lane), frag_rows(scr, LDC, 0, 0, lane), zero4());
+      store_tile_t(tt, LDC, 16 * bj, 16 * bi, -Tij, lane);
+    }
+    {
+      const int r = lane >> 2, c8 = (lane & 3) * 8;  // 16 rows x 32 columns
+      *reinterpret_cast<bf16x8*>(&scr[r * LDC + c8]) = zero8();
+    }
+  } else {
+    if (part != 0) return;
+    bf16* scr = tt + 16 * LDC;  // Tm's upper block (0, 1)
+    const f32x4 X = mma(frag_cols16(ap, LDA, 0, 0, lane), frag_rows16(tt, LDC, 0, 0, lane), zero4());
+    store_tile_t(scr, LDC, 0, 0, X, lane);
+    const f32x4 Tij = mma(frag_cols16(tt, LDC, 16, 16, lane), frag_rows16(scr, LDC, 0, 0, lane), zero4());
+    store_tile_t(tt, LDC, 0, 16, -Tij, lane);
+    if (lane < 32) {
+      const int r = lane >> 1, c8 = (lane & 1) * 8;
+      *reinterpret_cast<bf16x8*>(&scr[r * LDC + c8]) = zero8();
+    }
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// Gram tiles of one chunk for token-block rows R0 and R1 (compile-time, so all
+// fragments stay in registers): TYPE 0 builds A (strictly lower, beta and decay
+// applied; diagonal blocks to `ad` in fp32, the off-diagonal blocks the solve
+// needs to `ap`), TYPE 1 builds P (lower, decay applied) into the P ring.  The
+// key fragments of rows 0..R1 are read once and reused across tiles.
+template <int KD, int CP, int TYPE, int R0, int R1, typename SM>
+__device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
+  constexpr int NTB = CP / 16;
+  constexpr int KS = KD / 32;
+  constexpr int LDC = SM::LDC, LDA = SM::LDA;
   const int ls = lane & 15, lg = lane >> 4;
-  const int v0 = blockIdx.x * VS;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const size_t tok_stride_k = (size_t)H * K;   // elements between tokens in q, k
-  const size_t tok_stride_v = (size_t)H * V;
-  const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
-
-  // ---- the upper (never written) blocks of A^T, P^T, Tm^T must read as zeros
-  for (int i = tid; i < CP * LDC; i += kThreads) {
-    sm.tt[i] = (bf16)0.0f;
-    sm.pt[i] = (bf16)0.0f;
-    sm.at[i] = (bf16)0.0f;
-    sm.xt[i] = (bf16)0.0f;
+  const int gs = c % 3;
+  const bf16* kk = sm.k[c % 3];
+  const bf16* qq = sm.q[c % 2];
+  bf16* ptw = sm.pt[c % 2];
+  bf16* apw = sm.ap[c % 2];
+  const float* gl = sm.gl[gs];
+  const float* bta = sm.beta[gs];
+  // every operand and gate value is requested before the first MFMA
+  bf16x8 kf[R1 + 1][KS], af[2][KS];
+  f32x4 gr[2], br[2];
+  float gi[R1 + 1];
+#pragma unroll
+  for (int tb = 0; tb <= R1; ++tb) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = frag_rows_sw<KD>(kk, 16 * tb, 32 * ks, lane);
+    gi[tb] = gl[16 * tb + ls];
   }
-
-  // ---- initial state into accumulators (tile t = wave + 4j: vb = t / NCB, cb = t % NCB)
-  f32x4 S[ST_PER_WAVE];
 #pragma unroll
-  for (int j = 0; j < ST_PER_WAVE; ++j) {
-    const int t = wave + kWaves * j;
-    S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < NST && s0) {
-      const int vb = t / NCB, cb = t % NCB;
-      const int c = 16 * cb + ls;
-      if (c < K)
-        for (int e = 0; e < 4; ++e) S[j][e] = s0[state_base + (size_t)(16 * vb + 4 * lg + e) * K + c];
+  for (int ri = 0; ri < 2; ++ri) {
+    const int tr = ri == 0 ? R0 : R1;
+    if (TYPE == 1) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[ri][ks] = frag_rows_sw<KD>(qq, 16 * tr, 32 * ks, lane);
     }
+    gr[ri] = *reinterpret_cast<const f32x4*>(&gl[16 * tr + 4 * lg]);
+    br[ri] = *reinterpret_cast<const f32x4*>(&bta[16 * tr + 4 * lg]);
   }
-
-  // ---- register prefetch of one chunk: q, k rows (8 bf16 per slot), v slice, gates
-  constexpr int KCH = KD / 8;                       // 16-byte pieces per q/k row
-  constexpr int QK_SLOTS = (CP * KCH + kThreads - 1) / kThreads;
-  constexpr int VCH = VS / 8;
-  constexpr int V_SLOTS = (CP * VCH + kThreads - 1) / kThreads;
-  bf16x8 pq[QK_SLOTS], pk[QK_SLOTS], pv[V_SLOTS];
-  float pa = 1.0f, pb = 0.0f;
-
-  auto prefetch = [&](int t0) {
-    const int n = min(C, T - t0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < QK_SLOTS; ++j) {
-      const int idx = tid + kThreads * j;
-      const int r = idx / KCH, c = (idx % KCH) * 8;
-      pq[j] = zero8();
-      pk[j] = zero8();
-      if (r < n && c < K) {
-        const size_t off = ((size_t)b * T + t0 + r) * tok_stride_k + (size_t)h * K + c;
-        pq[j] = *reinterpret_cast<const bf16x8*>(q + off);
-        pk[j] = *reinterpret_cast<const bf16x8*>(k + off);
-      }
-    }
+  for (int ri = 0; ri < 2; ++ri) {
+    const int tr = ri == 0 ? R0 : R1;
 #pragma unroll
-    for (int j = 0; j < V_SLOTS; ++j) {
-      const int idx = tid + kThreads * j;
-      const int r = idx / VCH, c = (idx % VCH) * 8;
-      pv[j] = zero8();
-      if (r < n)
-        pv[j] = *reinterpret_cast<const bf16x8*>(
-            v + ((size_t)b * T + t0 + r) * tok_stride_v + (size_t)h * V + v0 + c);
-    }
-    pa = 1.0f;
-    pb = 0.0f;
-    if (tid < n) {
-      const size_t go = ((size_t)b * T + t0 + tid) * H + h;
-      pa = alpha[go];
-      pb = beta[go];
-    }
-  };
-
-  prefetch(0);
-
-  for (int t0 = 0; t0 < T; t0 += C) {
-    const int n = min(C, T - t0);
-    __syncthreads();  // every wave is done with the previous chunk's tiles
-    // ---- stage the prefetched chunk in LDS
+    for (int tc = 0; tc <= tr; ++tc) {
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int j = 0; j < QK_SLOTS; ++j) {
-      const int idx = tid + kThreads * j;
-      const int r = idx / KCH, c = (idx % KCH) * 8;
-      if (r < CP) {
-        *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c]) = pq[j];
-        *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c]) = pk[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < V_SLOTS; ++j) {
-      const int idx = tid + kThreads * j;
-      const int r = idx / VCH, c = (idx % VCH) * 8;
-      if (r < CP) *reinterpret_cast<bf16x8*>(&sm.v[r * VS + c]) = pv[j];
-    }
-    const float my_a = pa, my_b = pb;
-    // state (bf16, transposed) for this chunk's Y = K S^T, Z = Q S^T
-#pragma unroll
-    for (int j = 0; j < ST_PER_WAVE; ++j) {
-      const int t = wave + kWaves * j;
-      if (t < NST) store_tile_t(sm.st, LDV, 16 * (t % NCB), 16 * (t / NCB), S[j], lane);
-    }
-    __syncthreads();
-    if (t0 + C < T) prefetch(t0 + C);  // overlaps with the compute below
-
-    // ---- gates (wave 0): inclusive scan of log2 alpha over the tile
-    if (wave == 0) {
-      float la = (lane < CP) ? log2f(my_a) : 0.0f;
-      float bt = (lane < CP) ? my_b : 0.0f;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        float y = __shfl_up(la, d, 64);
-        if (lane >= d) la += y;
-      }
-      const float glast = __shfl(la, CP - 1, 64);
-      if (lane < CP) {
-        const float gm = exp2f(la);
-        sm.g[lane] = la;
-        sm.gam[lane] = gm;
-        sm.beta[lane] = bt;
-        sm.bg[lane] = bt * gm;
-        sm.dn[lane] = exp2f(glast - la);
-      }
-    }
-    // ---- Y = K S^T and Z = Q S^T for token block tb = wave (all value blocks)
-    f32x4 Y[NVB], Z[NVB];
-    const int tb = wave;
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      Y[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      Z[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (tb < NTB) {
-#pragma unroll
-      for (int ks = 0; ks < KD / 32; ++ks) {
-        const bf16x8 ka = frag_rows(sm.k, LDK, 16 * tb, 32 * ks, lane);
-        const bf16x8 qa = frag_rows(sm.q, LDK, 16 * tb, 32 * ks, lane);
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-          const bf16x8 sb = frag_cols(sm.st, LDV, 16 * vb, 32 * ks, lane);
-          Y[vb] = mma(ka, sb, Y[vb]);
-          Z[vb] = mma(qa, sb, Z[vb]);
-        }
-      }
-    }
-    __syncthreads();  // gates visible
-
-    // ---- Gram tiles: A (strictly lower) and P (lower), tile list round-robin over waves
-    constexpr int NTRI = NTB * (NTB + 1) / 2;
-    for (int t = wave; t < 2 * NTRI; t += kWaves) {
-      const bool isP = t >= NTRI;
-      int u = isP ? t - NTRI : t;
-      int tr = 0;
-      while (u > tr) { u -= tr + 1; ++tr; }
-      const int tc = u;  // tc <= tr
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KD / 32; ++ks) {
-        const bf16x8 a = frag_rows(isP ? sm.q : sm.k, LDK, 16 * tr, 32 * ks, lane);
-        const bf16x8 bb = frag_rows(sm.k, LDK, 16 * tc, 32 * ks, lane);
-        acc = mma(a, bb, acc);
-      }
+      for (int ks = 0; ks < KS; ++ks) acc = mma(TYPE == 0 ? kf[tr][ks] : af[ri][ks], kf[tc][ks], acc);
       const int i = 16 * tc + ls;
-      const float gi = sm.g[i];
       f32x4 val;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * tr + 4 * lg + e;
-        const bool keep = isP ? (i <= r) : (i < r);
-        const float dec = keep ? exp2f(sm.g[r] - gi) : 0.0f;
-        val[e] = isP ? dec * acc[e] : sm.beta[r] * dec * acc[e];
+        const bool keep = TYPE == 0 ? (i < r) : (i <= r);
+        const float dec = __builtin_amdgcn_exp2f(keep ? gr[ri][e] - gi[tc] : -INFINITY);
+        val[e] = (TYPE == 0 ? br[ri][e] : 1.0f) * dec * acc[e];
       }
-      if (isP) {
-        store_tile_t(sm.pt, LDC, 16 * tc, 16 * tr, val, lane);
+      if (TYPE == 1) {
+        store_tile_t(ptw, LDC, 16 * tc, 16 * tr, val, lane);
+      } else if (tc == tr) {
+        *reinterpret_cast<f32x4*>(&sm.ad[tr * 256 + ls * 16 + 4 * lg]) = val;  // [c][r]
       } else {
-        store_tile_t(sm.at, LDC, 16 * tc, 16 * tr, val, lane);
-        if (tr == tc) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sm.ad[tr * 256 + (4 * lg + e) * 16 + ls] = val[e];
-        }
+        // packed A^T blocks: (1,0) -> 0, (3,2) -> 16, (2,0..1) -> 32.., (3,0..1) -> 64..
+        const int off = tr == 1 ? 0 : (tr == 3 && tc == 2 ? 16 : (tr == 2 ? 32 : 64) + 16 * tc);
+        store_tile_t(apw, LDA, off, 0, val, lane);
       }
     }
-    // ---- R = diag(beta) V - diag(beta gam) Y  ->  R^T (bf16); Z scaled by gam
-    if (tb < NTB) {
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 rr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + 4 * lg + e;
-          const float vv = (float)sm.v[r * VS + 16 * vb + ls];
-          rr[e] = sm.beta[r] * vv - sm.bg[r] * Y[vb][e];
-          Z[vb][e] *= sm.gam[r];
-        }
-        store_tile_t(sm.rt, LDC, 16 * vb, 16 * tb, rr, lane);
-      }
-    }
-    __syncthreads();
+  }
+  (void)NTB;
+}
 
-    // ---- diagonal blocks of Tm by forward substitution in fp32 (wave 0):
-    // lane (block bb = lane/16, column j = lane%16) builds column j of (I + L_bb)^-1.
-    if (wave == 0 && lg < NTB) {
-      const int bb = lg, j = ls;
-      const float* L = &sm.ad[bb * 256];
-      float x[16], acc[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // x_r = delta_rj - sum_{i<r} L[r][i] x_i ; acc[r] holds the running sum
-        x[r] = (r == j) ? 1.0f : ((r < j) ? 0.0f : -acc[r]);
-#pragma unroll
-        for (int rr = r + 1; rr < 16; ++rr) acc[rr] = fmaf(L[rr * 16 + r], x[r], acc[rr]);
-      }
-      bf16x8 lo, hi;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        lo[r] = (bf16)x[r];
-        hi[r] = (bf16)x[8 + r];
-      }
-      bf16* dst = &sm.tt[(16 * bb + j) * LDC + 16 * bb];
-      *reinterpret_cast<bf16x8*>(dst) = lo;
-      *reinterpret_cast<bf16x8*>(dst + 8) = hi;
-    }
-    __syncthreads();
+template <int KD, int VS, int CP>
+__global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                const float* __restrict__ alpha, const float* __restrict__ beta,
+                const float* __restrict__ s0, bf16* __restrict__ o, float* __restrict__ s_final,
+                int T, int H, int K, int V, int C, int nslice) {
+  using SM = Smem<KD, VS, CP>;
+  constexpr int LDC = SM::LDC, LDV = SM::LDV, LDA = SM::LDA;
+  constexpr int NTB = CP / 16;          // token blocks per chunk tile
+  constexpr int NCB = KD / 16;          // key-channel blocks
+  constexpr int KS = KD / 32;           // k-steps over key channels
+  constexpr int CS = CP / 32;           // k-steps over tokens
+  constexpr int NCH = VS / 16;          // chain waves (one per 16 value rows)
+  constexpr int W_LEV = NCH;            // levels wave
+  constexpr int W_DIAG = NCH + 1;       // diagonal-solve wave
+  constexpr int W_G0 = NCH + 2;         // first Gram / staging wave
+  constexpr int NG = kWaves - W_G0;     // Gram / staging waves
+  static_assert(NG >= 2, "need at least two Gram waves");
+  __shared__ SM sm;
 
-    // ---- level 1: Tm_ij = -Tm_ii (A_ij Tm_jj) for (i, j) = (1, 0) [and (3, 2)]
-    if (wave < NTB / 2) {
-      const int bi = 2 * wave + 1, bj = 2 * wave;
-      // X = A_ij Tm_jj  (k = the 16 columns of block j)
-      const bf16x8 a = frag_cols16(sm.at, LDC, 16 * bi, 16 * bj, lane);
-      const bf16x8 bb = frag_rows16(sm.tt, LDC, 16 * bj, 16 * bj, lane);
-      f32x4 X = mma(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
-      store_tile_t(sm.xt, LDC, 16 * bj, 16 * bi, X, lane);  // xt[col][row]
-      __builtin_amdgcn_s_waitcnt(0xc07f);                   // lgkmcnt(0): same-wave LDS order
-      // Tm_ij = -Tm_ii X   (k = the 16 rows of block i)
-      const bf16x8 t2 = frag_cols16(sm.tt, LDC, 16 * bi, 16 * bi, lane);
-      const bf16x8 x2 = frag_rows16(sm.xt, LDC, 16 * bj, 16 * bi, lane);
-      f32x4 Tij = mma(t2, x2, f32x4{0.f, 0.f, 0.f, 0.f});
-      store_tile_t(sm.tt, LDC, 16 * bj, 16 * bi, -Tij, lane);
-    }
-    if constexpr (NTB == 4) {
-      __syncthreads();
-      // ---- level 2a: X2 = A_[23][01] Tm_[01]  (tile (2 + wave/2, wave%2), k = 32)
-      {
-        const int bi = 2 + wave / 2, bj = wave % 2;
-        bf16x8 a = frag_cols(sm.at, LDC, 16 * bi, 0, lane);
-        bf16x8 bb = frag_rows(sm.tt, LDC, 16 * bj, 0, lane);
-        f32x4 X = mma(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
-        store_tile_t(sm.xt, LDC, 16 * bj, 16 * bi, X, lane);
-      }
-      __syncthreads();
-      // ---- level 2b: Tm_[23][01] = -Tm_[23] X2
-      {
-        const int bi = 2 + wave / 2, bj = wave % 2;
-        bf16x8 a = frag_cols(sm.tt, LDC, 16 * bi, 32, lane);
-        bf16x8 bb = frag_rows(sm.xt, LDC, 16 * bj, 32, lane);
-        f32x4 Tij = mma(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
-        store_tile_t(sm.tt, LDC, 16 * bj, 16 * bi, -Tij, lane);
-      }
-    }
-    __syncthreads();
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ls = lane & 15, lg = lane >> 4;
 
-    // ---- U = Tm R for token block tb (value blocks vb); write U^T and (dn U)^T
-    if (tb < NTB) {
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < CP / 32; ++ks) {
-          if (32 * ks > 16 * tb + 15) break;  // Tm is lower triangular
-          const bf16x8 a = frag_cols(sm.tt, LDC, 16 * tb, 32 * ks, lane);
-          const bf16x8 bb = frag_rows(sm.rt, LDC, 16 * vb, 32 * ks, lane);
-          U = mma(a, bb, U);
-        }
-        store_tile_t(sm.ut, LDC, 16 * vb, 16 * tb, U, lane);
-        f32x4 Up;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Up[e] = sm.dn[16 * tb + 4 * lg + e] * U[e];
-        store_tile_t(sm.upt, LDC, 16 * vb, 16 * tb, Up, lane);
-      }
-    }
-    __syncthreads();
+  // XCD-aware mapping: consecutive workgroup ids go to different XCDs, so give
+  // the slices of one stream ids that are equal modulo 8 (same XCD, shared L2).
+  int item = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int slice = item % nslice;
+  const int bh = item / nslice;
+  const int h = bh % H, b = bh / H;
+  const int v0 = slice * VS;
+  const size_t tok_k = (size_t)H * K;
+  const size_t tok_v = (size_t)H * V;
+  const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
+  const int NT = (T + C - 1) / C;
 
-    // ---- O = diag(gam) Z + P U for token block tb, stored as bf16
-    if (tb < NTB) {
+  // ---- zero the P and Tm rings: their upper blocks are read as zeros
+  for (int i = tid; i < 2 * CP * LDC; i += kThreads) {
+    (&sm.pt[0][0])[i] = (bf16)0.0f;
+    (&sm.tt[0][0])[i] = (bf16)0.0f;
+  }
+
+  // ---- chain waves: initial state into accumulators and the bf16 state^T
+  f32x4 S[NCB];
+  const int vb = wave;  // value block of a chain wave
+  if (wave < NCH) {
 #pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 O = Z[vb];
+    for (int cb = 0; cb < NCB; ++cb) {
+      S[cb] = zero4();
+      const int c = 16 * cb + ls;
+      if (s0 && c < K) {
 #pragma unroll
-        for (int ks = 0; ks < CP / 32; ++ks) {
-          if (32 * ks > 16 * tb + 15) break;  // P is lower triangular
-          const bf16x8 a = frag_cols(sm.pt, LDC, 16 * tb, 32 * ks, lane);
-          const bf16x8 bb = frag_rows(sm.ut, LDC, 16 * vb, 32 * ks, lane);
-          O = mma(a, bb, O);
-        }
+        for (int e = 0; e < 4; ++e) S[cb][e] = s0[state_base + (size_t)(16 * vb + 4 * lg + e) * K + c];
+      }
+      store_tile_t(sm.st, LDV, 16 * cb, 16 * vb, S[cb], lane);
+    }
+  }
+
+  // ---- staging registers of the Gram waves (one chunk in flight)
+  constexpr int NSL = 64 * NG;                       // staging lanes
+  constexpr int KPIECES = CP * KD / 8;               // 16-byte pieces per key/query tile
+  constexpr int VPIECES = CP * VS / 8;
+  constexpr int KPL = (KPIECES + NSL - 1) / NSL;
+  constexpr int VPL = (VPIECES + NSL - 1) / NSL;
+  const int sl = tid - 64 * W_G0;                    // staging lane (valid on Gram waves)
+  bf16x8 rk[KPL], rq[KPL], rv[VPL];
+  float ra = 1.0f, rb = 0.0f;
+
+  auto load_chunk = [&](int c) {
+    const int t0 = c * C;
+    const int n = min(C, T - t0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + 4 * lg + e;
-          if (r < n)
-            o[((size_t)b * T + t0 + r) * tok_stride_v + (size_t)h * V + v0 + 16 * vb + ls] = (bf16)O[e];
-        }
+    for (int j = 0; j < KPL; ++j) {
+      const int p = sl + NSL * j;
+      const int r = p / (KD / 8), ch = (p % (KD / 8)) * 8;
+      rk[j] = zero8();
+      rq[j] = zero8();
+      if (p < KPIECES && r < n && ch < K) {
+        const size_t off = ((size_t)b * T + t0 + r) * tok_k + (size_t)h * K + ch;
+        rk[j] = *reinterpret_cast<const bf16x8*>(k + off);
+        rq[j] = *reinterpret_cast<const bf16x8*>(q + off);
       }
     }
-    // ---- state: S <- gam_n S + Up^T K
-    {
-      const float gam_n = sm.gam[CP - 1];
 #pragma unroll
-      for (int j = 0; j < ST_PER_WAVE; ++j) {
-        const int t = wave + kWaves * j;
-        if (t < NST) {
-          const int vb = t / NCB, cb = t % NCB;
-          f32x4 acc = S[j] * gam_n;
+    for (int j = 0; j < VPL; ++j) {
+      const int p = sl + NSL * j;
+      const int r = p / (VS / 8), ch = (p % (VS / 8)) * 8;
+      rv[j] = zero8();
+      if (p < VPIECES && r < n)
+        rv[j] = *reinterpret_cast<const bf16x8*>(v + ((size_t)b * T + t0 + r) * tok_v + (size_t)h * V +
+                                                   v0 + ch);
+    }
+    ra = 1.0f;
+    rb = 0.0f;
+    if (sl < n) {  // the first Gram wave holds the gates
+      const size_t go = ((size_t)b * T + t0 + sl) * H + h;
+      ra = alpha[go];
+      rb = beta[go];
+    }
+  };
+
+  auto stage_chunk = [&](int c) {
+    const int ks = c % 3, qs = c % 2;
 #pragma unroll
-          for (int ks = 0; ks < CP / 32; ++ks) {
-            const bf16x8 a = frag_rows(sm.upt, LDC, 16 * vb, 32 * ks, lane);
-            const bf16x8 bb = frag_cols(sm.k, LDK, 16 * cb, 32 * ks, lane);
-            acc = mma(a, bb, acc);
+    for (int j = 0; j < KPL; ++j) {
+      const int p = sl + NSL * j;
+      if (p < KPIECES) {
+        const int r = p / (KD / 8), ch = (p % (KD / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&sm.k[ks][swz<KD>(r, ch)]) = rk[j];
+        *reinterpret_cast<bf16x8*>(&sm.q[qs][swz<KD>(r, ch)]) = rq[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int p = sl + NSL * j;
+      if (p < VPIECES) {
+        const int r = p / (VS / 8), ch = (p % (VS / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&sm.v[qs][r * VS + ch]) = rv[j];
+      }
+    }
+    if (wave == W_G0) {
+      const float la = (lane < CP) ? __builtin_amdgcn_logf(ra) : 0.0f;  // log2; padding: alpha = 1
+      const float bt = (lane < CP) ? rb : 0.0f;
+      const float g = wave_scan(la, lane);
+      const float glast = bits_f(__builtin_amdgcn_readlane(f_bits(g), CP - 1));
+      if (lane < CP) {
+        const float gm = __builtin_amdgcn_exp2f(g);
+        sm.gl[ks][lane] = g;
+        sm.gam[ks][lane] = gm;
+        sm.beta[ks][lane] = bt;
+        sm.bg[ks][lane] = bt * gm;
+        sm.dn[ks][lane] = __builtin_amdgcn_exp2f(glast - g);
+      }
+    }
+  };
+
+  // Each role runs its own copy of the chunk loop (so the register allocator
+  // sees one role's live values at a time); every copy executes exactly two
+  // workgroup barriers per iteration, x = -2 .. NT-1.
+  if (wave < NCH) {
+    // ============================ chain waves ============================
+    for (int x = -2; x < NT; ++x) {
+      lds_barrier();
+      if (x < 0) {
+        lds_barrier();
+        continue;
+      }
+      // ---- phase A: Y = K S^T, Z = Q S^T for all token blocks of this value block.
+      // Fragments of token block tb + 1 are requested before the MFMAs of tb
+      // (scheduling barriers keep that order) so LDS latency overlaps the math.
+      const bf16* kk = sm.k[x % 3];
+      const bf16* qq = sm.q[x % 2];
+      const bf16* vv = sm.v[x % 2];
+      const int gs = x % 3;
+      bf16x8 sbf[KS], ka[2][KS], qa[2][KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sbf[ks] = frag_cols(sm.st, LDV, 16 * vb, 32 * ks, lane);
+        ka[0][ks] = frag_rows_sw<KD>(kk, 0, 32 * ks, lane);
+        qa[0][ks] = frag_rows_sw<KD>(qq, 0, 32 * ks, lane);
+      }
+      f32x4 Y[NTB], Z[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        if (tb + 1 < NTB) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            ka[(tb + 1) & 1][ks] = frag_rows_sw<KD>(kk, 16 * (tb + 1), 32 * ks, lane);
+            qa[(tb + 1) & 1][ks] = frag_rows_sw<KD>(qq, 16 * (tb + 1), 32 * ks, lane);
           }
-          S[j] = acc;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        Y[tb] = zero4();
+        Z[tb] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          Y[tb] = mma(ka[tb & 1][ks], sbf[ks], Y[tb]);
+          Z[tb] = mma(qa[tb & 1][ks], sbf[ks], Z[tb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // ---- R = diag(beta) V - diag(beta gam) Y  ->  R^T; keep diag(gam) Z.
+      // One transpose read gives each lane V[16 tb + 4g + e][16 vb + s], e = 0..3.
+      bf16x4 vt[NTB];
+      f32x4 bt[NTB], bgv[NTB], gm[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        const int r0 = 16 * tb + 4 * lg;
+        vt[tb] = tr_read(vv + (r0 + (ls >> 2)) * VS + 16 * vb + 4 * (ls & 3));
+        bt[tb] = *reinterpret_cast<const f32x4*>(&sm.beta[gs][r0]);
+        bgv[tb] = *reinterpret_cast<const f32x4*>(&sm.bg[gs][r0]);
+        gm[tb] = *reinterpret_cast<const f32x4*>(&sm.gam[gs][r0]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        f32x4 R;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[e] = bt[tb][e] * (float)vt[tb][e] - bgv[tb][e] * Y[tb][e];
+        store_tile_t(sm.rt, LDC, 16 * vb, 16 * tb, R, lane);
+        Z[tb] = Z[tb] * gm[tb];
+      }
+      lds_barrier();  // Tm_x is complete after this barrier
+      // ---- phase B.  Operands that do not depend on this phase's results are
+      // read first so their LDS latency overlaps.
+      const bf16* tt = sm.tt[x % 2];
+      const bf16* pt = sm.pt[x % 2];
+      bf16x8 rf[CS], kt[NCB][CS], tf[NTB][CS], pf[NTB][CS];
+      f32x4 dnv[NTB];
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) rf[cs] = frag_rows(sm.rt, LDC, 16 * vb, 32 * cs, lane);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        dnv[tb] = *reinterpret_cast<const f32x4*>(&sm.dn[gs][16 * tb + 4 * lg]);
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs)
+          if (32 * cs <= 16 * tb + 15) {  // Tm and P are lower triangular
+            tf[tb][cs] = frag_cols(tt, LDC, 16 * tb, 32 * cs, lane);
+            pf[tb][cs] = frag_cols(pt, LDC, 16 * tb, 32 * cs, lane);
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // U = Tm R
+      f32x4 U[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        U[tb] = zero4();
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs)
+          if (32 * cs <= 16 * tb + 15) U[tb] = mma(tf[tb][cs], rf[cs], U[tb]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        store_tile_t(sm.rt, LDC, 16 * vb, 16 * tb, U[tb], lane);  // U^T replaces R^T
+        store_tile_t(sm.upt, LDC, 16 * vb, 16 * tb, U[tb] * dnv[tb], lane);
+      }
+      bf16x8 uf[CS], upf[CS];
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) {
+        uf[cs] = frag_rows(sm.rt, LDC, 16 * vb, 32 * cs, lane);
+        upf[cs] = frag_rows(sm.upt, LDC, 16 * vb, 32 * cs, lane);
+      }
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) kt[cb][cs] = frag_cols_sw<KD>(kk, 16 * cb, 32 * cs, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      // O = diag(gam) Z + P U
+      f32x4 O[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        O[tb] = Z[tb];
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs)
+          if (32 * cs <= 16 * tb + 15) O[tb] = mma(pf[tb][cs], uf[cs], O[tb]);
+      }
+      // S <- gam_n S + Up^T K
+      const float gam_n = sm.gam[gs][CP - 1];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        f32x4 acc = S[cb] * gam_n;
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) acc = mma(upf[cs], kt[cb][cs], acc);
+        S[cb] = acc;
+        store_tile_t(sm.st, LDV, 16 * cb, 16 * vb, acc, lane);
+      }
+      // O leaves through this wave's rows of rt, re-read as [token][16] so each
+      // lane stores 16 contiguous bytes of one token row.
+      bf16* ost = sm.rt + 16 * vb * LDC;
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ost[(16 * tb + 4 * lg + e) * 16 + ls] = (bf16)O[tb][e];
+      const int t0 = x * C;
+      const int n = min(C, T - t0);
+      bf16* obase = o + ((size_t)b * T + t0) * tok_v + (size_t)h * V + v0 + 16 * vb;
+#pragma unroll
+      for (int j = 0; j < CP / 32; ++j) {
+        const int p = lane + 64 * j;
+        const int r = p >> 1, half = p & 1;
+        const bf16x8 val = *reinterpret_cast<const bf16x8*>(&ost[r * 16 + 8 * half]);
+        if (r < n) *reinterpret_cast<bf16x8*>(obase + (size_t)r * tok_v + 8 * half) = val;
+      }
+    }
+  } else if (wave == W_LEV) {
+    // ============================ levels wave ============================
+    for (int x = -2; x < NT; ++x) {
+      lds_barrier();
+      if (x >= 0) levels_part<CP>(sm.tt[x % 2], sm.ap[x % 2], lane, 0);
+      lds_barrier();
+    }
+  } else if (wave == W_DIAG) {
+    // ============================= diag wave =============================
+    for (int x = -2; x < NT; ++x) {
+      lds_barrier();
+      // phase A: the second half of the off-diagonal solve of chunk x
+      if (NTB == 4 && x >= 0) levels_part<CP>(sm.tt[x % 2], sm.ap[x % 2], lane, 1);
+      lds_barrier();
+      // phase B: diagonal blocks of chunk x + 1
+      const int c = x + 1;
+      if (c >= 0 && c < NT && lg < NTB) {
+        // column j of (I + L_bb)^-1 by forward substitution in fp32;
+        // acc[r] carries sum_{i<r} L[r][i] x_i.
+        bf16* tt = sm.tt[c % 2];
+        const int bb = lg, j = ls;
+        const float* Lt = &sm.ad[bb * 256];  // Lt[c][r] = L[r][c]
+        float xv[16], acc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          xv[r] = (r == j) ? 1.0f : ((r < j) ? 0.0f : -acc[r]);
+          if (r < 15) {
+            f32x4 col[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) col[u] = *reinterpret_cast<const f32x4*>(&Lt[r * 16 + 4 * u]);
+#pragma unroll
+            for (int rr = r + 1; rr < 16; ++rr) acc[rr] = fmaf(col[rr >> 2][rr & 3], xv[r], acc[rr]);
+          }
+        }
+        bf16x8 lo, hi;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          lo[r] = (bf16)xv[r];
+          hi[r] = (bf16)xv[8 + r];
+        }
+        bf16* dst = &tt[(16 * bb + j) * LDC + 16 * bb];
+        *reinterpret_cast<bf16x8*>(dst) = lo;
+        *reinterpret_cast<bf16x8*>(dst + 8) = hi;
+      }
+    }
+  } else {
+    // ========================== Gram / staging waves ==========================
+    load_chunk(0);
+    const int gw = wave - W_G0;
+    for (int x = -2; x < NT; ++x) {
+      lds_barrier();
+      {
+        const int c = x + 1;  // chunk whose Gram is built now
+        // plan: (type, rows) per Gram wave.  type 0: A = K K^T, type 1: P = Q K^T.
+        // Four token blocks are split as rows {0, 3} and {1, 2} for balance.
+        if (c >= 0 && c < NT) {
+          if constexpr (NTB == 4) {
+            switch (gw) {
+              case 0: gram_rows<KD, CP, 0, 0, 3>(sm, c, lane); break;
+              case 1: gram_rows<KD, CP, 0, 1, 2>(sm, c, lane); break;
+              case 2: gram_rows<KD, CP, 1, 0, 3>(sm, c, lane); break;
+              case 3: gram_rows<KD, CP, 1, 1, 2>(sm, c, lane); break;
+              default: break;
+            }
+          } else {
+            switch (gw) {
+              case 0: gram_rows<KD, CP, 0, 0, 1>(sm, c, lane); break;
+              case 1: gram_rows<KD, CP, 1, 0, 1>(sm, c, lane); break;
+              default: break;
+            }
+          }
+        }
+      }
+      lds_barrier();
+      {
+        const int c = x + 2;
+        if (c >= 0 && c < NT) {
+          stage_chunk(c);
+          if (c + 1 < NT) load_chunk(c + 1);
         }
       }
     }
   }
 
   // ---- final state
-  if (s_final) {
+  if (wave < NCH && s_final) {
 #pragma unroll
-    for (int j = 0; j < ST_PER_WAVE; ++j) {
-      const int t = wave + kWaves * j;
-      if (t < NST) {
-        const int vb = t / NCB, cb = t % NCB;
-        const int c = 16 * cb + ls;
-        if (c < K)
-          for (int e = 0; e < 4; ++e)
-            s_final[state_base + (size_t)(16 * vb + 4 * lg + e) * K + c] = S[j][e];
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int c = 16 * cb + ls;
+      if (c < K) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_final[state_base + (size_t)(16 * vb + 4 * lg + e) * K + c] = S[cb][e];
       }
     }
   }
@@ -471,11 +694,12 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
 template <int KD, int VS, int CP>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  dim3 grid(a.V / VS, a.H, a.B);
-  hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP>), grid, dim3(kThreads), 0, stream,
+  const int nslice = a.V / VS;
+  const int nblk = a.B * a.H * nslice;
+  hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP>), dim3(nblk), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                      static_cast<const bf16*>(a.v), a.alpha, a.beta, a.s0,
-                     static_cast<bf16*>(a.o), a.s_final, a.T, a.H, a.K, a.V, a.chunk);
+                     static_cast<bf16*>(a.o), a.s_final, a.T, a.H, a.K, a.V, a.chunk, nslice);
   return hipGetLastError();
 }
 
@@ -486,20 +710,15 @@ hipError_t launch_cp(const FwdArgs& a, hipStream_t stream) {
 
 template <int KD>
 hipError_t launch_vs(const FwdArgs& a, int vs, hipStream_t stream) {
-  switch (vs) {
-    case 16: return launch_cp<KD, 16>(a, stream);
-    case 32: return launch_cp<KD, 32>(a, stream);
-    default: return launch_cp<KD, 64>(a, stream);
-  }
+  return vs == 16 ? launch_cp<KD, 16>(a, stream) : launch_cp<KD, 32>(a, stream);
 }
 
-// Value-slice width: as wide as possible while the (batch, head, slice) grid
-// still covers the 256 compute units; each slice repeats the K-side work
-// (gates, Gram, solve), so wider slices mean less repeated work.
+// Value-slice width: 32 rows (two chain waves) while the (batch, head, slice)
+// grid still has at least 192 workgroups, else 16 for more parallelism.  Each
+// slice repeats the state-independent work, so wider slices do less of it.
 int pick_vs(int B, int H, int V) {
-  int vs = V < 64 ? V : 64;
-  while (vs > 16 && (long)B * H * (V / vs) < 192) vs /= 2;
-  return vs;
+  if (V < 32) return 16;
+  return (long)B * H * (V / 32) >= 192 ? 32 : 16;
 }
 
 }  // namespace
