@@ -44,8 +44,7 @@
 // array (one 16-byte read per lane) or from a [k][row] array with two gfx950
 // transpose reads (ds_read_b64_tr_b16).  Accumulator tiles are written
 // transposed ([col][row], 8 bytes per lane).  Key and query tiles are row-major
-// [token][channel] with the 16-byte chunks of each row XOR-swizzled by the row
-// index, so both access patterns spread over all banks without padding.
+// [token][channel] with padded rows.
 #include "launch.h"
 
 namespace gdn {
@@ -106,11 +105,13 @@ __device__ __forceinline__ bf16x8 frag_cols16(const bf16* base, int ld, int r0, 
   return (lane >> 5) ? zero8() : f;
 }
 
-// Swizzled [token][channel] tiles (row length KD, 16-byte chunk c stored at c ^ (row & SW)).
+// Key and query tiles: row-major [token][channel] with 8 elements of padding
+// per row (row stride KD + 8).  A 16-byte fragment read by 16 lanes of
+// consecutive rows then covers all 64 banks, and every fragment of a tile is a
+// constant offset from one per-lane base address (no per-read address math).
 template <int KD>
 __device__ __forceinline__ int swz(int row, int col) {
-  constexpr int SW = (KD / 8 < 16 ? KD / 8 : 16) - 1;
-  return row * KD + ((((col >> 3) ^ (row & SW))) << 3) + (col & 7);
+  return row * (KD + 8) + col;
 }
 template <int KD>
 __device__ __forceinline__ bf16x8 frag_rows_sw(const bf16* base, int r0, int k0, int lane) {
@@ -142,6 +143,27 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Two accumulator tiles a (rows 0..15) and b (rows 16..31) of the same 16
+// columns -> the MFMA operand whose k index is their row (k = 8g + j for lane
+// group g), without LDS.  Each lane packs its 4 rows (4g..4g+3) of a tile into
+// two bf16-pair dwords; viewing a wave as four 16-lane rows [x0 x1 x2 x3],
+// permlane32_swap(a, b) gives ([a0 a1 b0 b1], [a2 a3 b2 b3]) and permlane16_swap
+// of that pair gives ([a0 a2 b0 b2], [a1 a3 b1 b3]): group g then holds rows
+// 8g..8g+3 and 8g+4..8g+7, the operand layout.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int pack2(float x, float y) {
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(int, bf16x2{(bf16)x, (bf16)y});
+}
+__device__ __forceinline__ bf16x8 acc_pair_to_frag(f32x4 a, f32x4 b) {
+  const i32x2 s_lo = __builtin_amdgcn_permlane32_swap(pack2(a[0], a[1]), pack2(b[0], b[1]), false, false);
+  const i32x2 s_hi = __builtin_amdgcn_permlane32_swap(pack2(a[2], a[3]), pack2(b[2], b[3]), false, false);
+  const i32x2 t_lo = __builtin_amdgcn_permlane16_swap(s_lo[0], s_lo[1], false, false);
+  const i32x2 t_hi = __builtin_amdgcn_permlane16_swap(s_hi[0], s_hi[1], false, false);
+  return __builtin_bit_cast(bf16x8, i32x4{t_lo[0], t_hi[0], t_lo[1], t_hi[1]});
+}
+
 __device__ __forceinline__ float bits_f(int x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ int f_bits(float x) { return __builtin_bit_cast(int, x); }
 
@@ -164,11 +186,10 @@ template <int KD, int VS, int CP>
 struct alignas(16) Smem {
   static constexpr int NTB = CP / 16;
   static constexpr int LDC = CP + 8;   // CP x CP tiles
-  static constexpr int LDV = VS + 8;   // state^T [KD][LDV]
   static constexpr int LDA = 24;       // packed 16-wide A^T blocks
   static constexpr int APK = (NTB == 4 ? 96 : 16) * LDA;
-  bf16 k[3][CP * KD];                  // keys, swizzled [token][channel]
-  bf16 q[2][CP * KD];                  // queries, swizzled
+  bf16 k[3][CP * (KD + 8)];            // keys [token][channel], padded rows
+  bf16 q[2][CP * (KD + 8)];            // queries, padded rows
   bf16 v[2][CP * VS];                  // value slice [token][v]
   float gl[3][CP];                     // cumulative log2 gate
   float gam[3][CP];                    // 2^g
@@ -179,9 +200,6 @@ struct alignas(16) Smem {
   bf16 tt[2][CP * LDC];                // Tm^T: tt[j][i]; upper blocks zero (level scratch)
   bf16 ap[2][APK];                     // off-diagonal A^T blocks used by the levels
   float ad[NTB * 256];                 // diagonal A blocks, fp32, transposed [c][r]
-  bf16 st[KD * LDV];                   // bf16 state^T: st[c][v]
-  bf16 rt[VS * LDC];                   // R^T, then U^T: [v][token]
-  bf16 upt[VS * LDC];                  // (diag(gam_n/gam) U)^T
 };
 
 // Off-diagonal blocks of Tm = (I + A)^-1 from its diagonal blocks (already in
@@ -276,32 +294,61 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
     br[ri] = *reinterpret_cast<const f32x4*>(&bta[16 * tr + 4 * lg]);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // all tiles advance together over the k-steps: independent accumulators
+  constexpr int NT0 = R0 + 1, NTILE = R0 + 1 + R1 + 1;
+  f32x4 acc[NTILE];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) acc[t] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const int ri = t < NT0 ? 0 : 1;
+      const int tr = ri == 0 ? R0 : R1;
+      const int tc = ri == 0 ? t : t - NT0;
+      acc[t] = mma(TYPE == 0 ? kf[tr][ks] : af[ri][ks], kf[tc][ks], acc[t]);
+    }
+  // Decay 2^(g_r - g_i).  Diagonal tiles: per element, masked before the
+  // exponential.  Off-diagonal tiles (every i < r): 2^(g_r - g_ref) 2^(g_ref - g_i)
+  // with g_ref the gate of the row block's first token, both factors <= 1; the
+  // row factor (times beta for A) is shared by the row block's tiles.
+  f32x4 rowf[2];
 #pragma unroll
   for (int ri = 0; ri < 2; ++ri) {
     const int tr = ri == 0 ? R0 : R1;
+    const float gref = gl[16 * tr];
 #pragma unroll
-    for (int tc = 0; tc <= tr; ++tc) {
-      f32x4 acc = zero4();
+    for (int e = 0; e < 4; ++e)
+      rowf[ri][e] = (TYPE == 0 ? br[ri][e] : 1.0f) * __builtin_amdgcn_exp2f(gr[ri][e] - gref);
+  }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mma(TYPE == 0 ? kf[tr][ks] : af[ri][ks], kf[tc][ks], acc);
-      const int i = 16 * tc + ls;
-      f32x4 val;
+  for (int t = 0; t < NTILE; ++t) {
+    const int ri = t < NT0 ? 0 : 1;
+    const int tr = ri == 0 ? R0 : R1;
+    const int tc = ri == 0 ? t : t - NT0;
+    const int i = 16 * tc + ls;
+    f32x4 val;
+    if (tc == tr) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * tr + 4 * lg + e;
         const bool keep = TYPE == 0 ? (i < r) : (i <= r);
         const float dec = __builtin_amdgcn_exp2f(keep ? gr[ri][e] - gi[tc] : -INFINITY);
-        val[e] = (TYPE == 0 ? br[ri][e] : 1.0f) * dec * acc[e];
+        val[e] = (TYPE == 0 ? br[ri][e] : 1.0f) * dec * acc[t][e];
       }
-      if (TYPE == 1) {
-        store_tile_t(ptw, LDC, 16 * tc, 16 * tr, val, lane);
-      } else if (tc == tr) {
-        *reinterpret_cast<f32x4*>(&sm.ad[tr * 256 + ls * 16 + 4 * lg]) = val;  // [c][r]
-      } else {
-        // packed A^T blocks: (1,0) -> 0, (3,2) -> 16, (2,0..1) -> 32.., (3,0..1) -> 64..
-        const int off = tr == 1 ? 0 : (tr == 3 && tc == 2 ? 16 : (tr == 2 ? 32 : 64) + 16 * tc);
-        store_tile_t(apw, LDA, off, 0, val, lane);
-      }
+    } else {
+      const float colf = __builtin_amdgcn_exp2f(gl[16 * tr] - gi[tc]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = rowf[ri][e] * (colf * acc[t][e]);
+    }
+    if (TYPE == 1) {
+      store_tile_t(ptw, LDC, 16 * tc, 16 * tr, val, lane);
+    } else if (tc == tr) {
+      *reinterpret_cast<f32x4*>(&sm.ad[tr * 256 + ls * 16 + 4 * lg]) = val;  // [c][r]
+    } else {
+      // packed A^T blocks: (1,0) -> 0, (3,2) -> 16, (2,0..1) -> 32.., (3,0..1) -> 64..
+      const int off = tr == 1 ? 0 : (tr == 3 && tc == 2 ? 16 : (tr == 2 ? 32 : 64) + 16 * tc);
+      store_tile_t(apw, LDA, off, 0, val, lane);
     }
   }
   (void)NTB;
@@ -314,7 +361,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
                 const float* __restrict__ s0, bf16* __restrict__ o, float* __restrict__ s_final,
                 int T, int H, int K, int V, int C, int nslice) {
   using SM = Smem<KD, VS, CP>;
-  constexpr int LDC = SM::LDC, LDV = SM::LDV, LDA = SM::LDA;
+  constexpr int LDC = SM::LDC, LDA = SM::LDA;
   constexpr int NTB = CP / 16;          // token blocks per chunk tile
   constexpr int NCB = KD / 16;          // key-channel blocks
   constexpr int KS = KD / 32;           // k-steps over key channels
@@ -352,19 +399,16 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     (&sm.tt[0][0])[i] = (bf16)0.0f;
   }
 
-  // ---- chain waves: initial state into accumulators and the bf16 state^T
+  // ---- chain waves: the state slice as S^T accumulator tiles: tile cb holds
+  // S^T[16 cb + 4g + e][16 vb + s] = S[16 vb + s][16 cb + 4g + e] in lane (g, s)
   f32x4 S[NCB];
   const int vb = wave;  // value block of a chain wave
   if (wave < NCH) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       S[cb] = zero4();
-      const int c = 16 * cb + ls;
-      if (s0 && c < K) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[cb][e] = s0[state_base + (size_t)(16 * vb + 4 * lg + e) * K + c];
-      }
-      store_tile_t(sm.st, LDV, 16 * cb, 16 * vb, S[cb], lane);
+      if (s0 && 16 * cb < K)
+        S[cb] = *reinterpret_cast<const f32x4*>(&s0[state_base + (size_t)(16 * vb + ls) * K + 16 * cb + 4 * lg]);
     }
   }
 
@@ -375,64 +419,75 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   constexpr int KPL = (KPIECES + NSL - 1) / NSL;
   constexpr int VPL = (VPIECES + NSL - 1) / NSL;
   const int sl = tid - 64 * W_G0;                    // staging lane (valid on Gram waves)
-  bf16x8 rk[KPL], rq[KPL], rv[VPL];
-  float ra = 1.0f, rb = 0.0f;
+  struct StageRegs {
+    bf16x8 k[KPL], q[KPL], v[VPL];
+    float a, b;
+  };
 
-  auto load_chunk = [&](int c) {
+  // Per-piece token row, global offset within a chunk and LDS offset: fixed
+  // for a staging lane, so computed once.
+  int krow[KPL], kgo[KPL], klo[KPL], vrow[VPL], vgo[VPL], vlo[VPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int p = sl + NSL * j;
+    const int r = p / (KD / 8), ch = (p % (KD / 8)) * 8;
+    krow[j] = (p < KPIECES && ch < K) ? r : CP;  // CP: never loaded or stored
+    kgo[j] = r * (int)tok_k + ch;
+    klo[j] = swz<KD>(r, ch);
+  }
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int p = sl + NSL * j;
+    const int r = p / (VS / 8), ch = (p % (VS / 8)) * 8;
+    vrow[j] = p < VPIECES ? r : CP;
+    vgo[j] = r * (int)tok_v + ch;
+    vlo[j] = r * VS + ch;
+  }
+
+  auto load_chunk = [&](int c, StageRegs& R) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
+    const bf16* kb = k + ((size_t)b * T + t0) * tok_k + (size_t)h * K;
+    const bf16* qb = q + ((size_t)b * T + t0) * tok_k + (size_t)h * K;
+    const bf16* vbp = v + ((size_t)b * T + t0) * tok_v + (size_t)h * V + v0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      const int p = sl + NSL * j;
-      const int r = p / (KD / 8), ch = (p % (KD / 8)) * 8;
-      rk[j] = zero8();
-      rq[j] = zero8();
-      if (p < KPIECES && r < n && ch < K) {
-        const size_t off = ((size_t)b * T + t0 + r) * tok_k + (size_t)h * K + ch;
-        rk[j] = *reinterpret_cast<const bf16x8*>(k + off);
-        rq[j] = *reinterpret_cast<const bf16x8*>(q + off);
+      R.k[j] = zero8();
+      R.q[j] = zero8();
+      if (krow[j] < n) {
+        R.k[j] = *reinterpret_cast<const bf16x8*>(kb + kgo[j]);
+        R.q[j] = *reinterpret_cast<const bf16x8*>(qb + kgo[j]);
       }
     }
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      const int p = sl + NSL * j;
-      const int r = p / (VS / 8), ch = (p % (VS / 8)) * 8;
-      rv[j] = zero8();
-      if (p < VPIECES && r < n)
-        rv[j] = *reinterpret_cast<const bf16x8*>(v + ((size_t)b * T + t0 + r) * tok_v + (size_t)h * V +
-                                                   v0 + ch);
+      R.v[j] = zero8();
+      if (vrow[j] < n) R.v[j] = *reinterpret_cast<const bf16x8*>(vbp + vgo[j]);
     }
-    ra = 1.0f;
-    rb = 0.0f;
+    R.a = 1.0f;
+    R.b = 0.0f;
     if (sl < n) {  // the first Gram wave holds the gates
       const size_t go = ((size_t)b * T + t0 + sl) * H + h;
-      ra = alpha[go];
-      rb = beta[go];
+      R.a = alpha[go];
+      R.b = beta[go];
     }
   };
 
-  auto stage_chunk = [&](int c) {
+  auto stage_chunk = [&](int c, const StageRegs& R) {
     const int ks = c % 3, qs = c % 2;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      const int p = sl + NSL * j;
-      if (p < KPIECES) {
-        const int r = p / (KD / 8), ch = (p % (KD / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(&sm.k[ks][swz<KD>(r, ch)]) = rk[j];
-        *reinterpret_cast<bf16x8*>(&sm.q[qs][swz<KD>(r, ch)]) = rq[j];
+      if (sl + NSL * j < KPIECES) {  // pieces past K are stored as zeros
+        *reinterpret_cast<bf16x8*>(&sm.k[ks][klo[j]]) = R.k[j];
+        *reinterpret_cast<bf16x8*>(&sm.q[qs][klo[j]]) = R.q[j];
       }
     }
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int p = sl + NSL * j;
-      if (p < VPIECES) {
-        const int r = p / (VS / 8), ch = (p % (VS / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(&sm.v[qs][r * VS + ch]) = rv[j];
-      }
-    }
+    for (int j = 0; j < VPL; ++j)
+      if (vrow[j] < CP) *reinterpret_cast<bf16x8*>(&sm.v[qs][vlo[j]]) = R.v[j];
     if (wave == W_G0) {
-      const float la = (lane < CP) ? __builtin_amdgcn_logf(ra) : 0.0f;  // log2; padding: alpha = 1
-      const float bt = (lane < CP) ? rb : 0.0f;
+      const float la = (lane < CP) ? __builtin_amdgcn_logf(R.a) : 0.0f;  // log2; padding: alpha = 1
+      const float bt = (lane < CP) ? R.b : 0.0f;
       const float g = wave_scan(la, lane);
       const float glast = bits_f(__builtin_amdgcn_readlane(f_bits(g), CP - 1));
       if (lane < CP) {
@@ -451,75 +506,84 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // workgroup barriers per iteration, x = -2 .. NT-1.
   if (wave < NCH) {
     // ============================ chain waves ============================
+    // Everything that depends on the state stays in registers: the state (as
+    // S^T tiles), R and U become MFMA operands through permlane swaps.  Only
+    // the chunk's K, Q, V, gates, Tm and P come from LDS.
     for (int x = -2; x < NT; ++x) {
       lds_barrier();
       if (x < 0) {
         lds_barrier();
         continue;
       }
-      // ---- phase A: Y = K S^T, Z = Q S^T for all token blocks of this value block.
-      // Fragments of token block tb + 1 are requested before the MFMAs of tb
-      // (scheduling barriers keep that order) so LDS latency overlaps the math.
       const bf16* kk = sm.k[x % 3];
       const bf16* qq = sm.q[x % 2];
       const bf16* vv = sm.v[x % 2];
       const int gs = x % 3;
-      bf16x8 sbf[KS], ka[2][KS], qa[2][KS];
+      // ---- phase A: Y = K S^T and Z^T = S Q^T (the state operand has k = key
+      // channel; as the B operand of Y and the A operand of Z^T it is the same
+      // registers).
+      // The k-step is the outer loop so the 2 NTB accumulators are independent;
+      // fragments of k-step ks + 1 are requested before the MFMAs of ks.
+      bf16x8 sbf[KS], ka[2][NTB], qa[2][NTB];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sbf[ks] = frag_cols(sm.st, LDV, 16 * vb, 32 * ks, lane);
-        ka[0][ks] = frag_rows_sw<KD>(kk, 0, 32 * ks, lane);
-        qa[0][ks] = frag_rows_sw<KD>(qq, 0, 32 * ks, lane);
+      for (int tb = 0; tb < NTB; ++tb) {
+        ka[0][tb] = frag_rows_sw<KD>(kk, 16 * tb, 0, lane);
+        qa[0][tb] = frag_rows_sw<KD>(qq, 16 * tb, 0, lane);
       }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sbf[ks] = acc_pair_to_frag(S[2 * ks], S[2 * ks + 1]);
       f32x4 Y[NTB], Z[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        if (tb + 1 < NTB) {
+        Y[tb] = zero4();
+        Z[tb] = zero4();
+      }
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            ka[(tb + 1) & 1][ks] = frag_rows_sw<KD>(kk, 16 * (tb + 1), 32 * ks, lane);
-            qa[(tb + 1) & 1][ks] = frag_rows_sw<KD>(qq, 16 * (tb + 1), 32 * ks, lane);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb) {
+            ka[(ks + 1) & 1][tb] = frag_rows_sw<KD>(kk, 16 * tb, 32 * (ks + 1), lane);
+            qa[(ks + 1) & 1][tb] = frag_rows_sw<KD>(qq, 16 * tb, 32 * (ks + 1), lane);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        Y[tb] = zero4();
-        Z[tb] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          Y[tb] = mma(ka[tb & 1][ks], sbf[ks], Y[tb]);
-          Z[tb] = mma(qa[tb & 1][ks], sbf[ks], Z[tb]);
+        for (int tb = 0; tb < NTB; ++tb) {
+          Y[tb] = mma(ka[ks & 1][tb], sbf[ks], Y[tb]);   // Y   [token][v]
+          Z[tb] = mma(sbf[ks], qa[ks & 1][tb], Z[tb]);   // Z^T [v][token]
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // ---- R = diag(beta) V - diag(beta gam) Y  ->  R^T; keep diag(gam) Z.
+      // ---- R = diag(beta) V - diag(beta gam) Y, kept as the U = Tm R operand
       // One transpose read gives each lane V[16 tb + 4g + e][16 vb + s], e = 0..3.
       bf16x4 vt[NTB];
-      f32x4 bt[NTB], bgv[NTB], gm[NTB];
+      f32x4 bt[NTB], bgv[NTB];
+      float gmt[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         const int r0 = 16 * tb + 4 * lg;
         vt[tb] = tr_read(vv + (r0 + (ls >> 2)) * VS + 16 * vb + 4 * (ls & 3));
         bt[tb] = *reinterpret_cast<const f32x4*>(&sm.beta[gs][r0]);
         bgv[tb] = *reinterpret_cast<const f32x4*>(&sm.bg[gs][r0]);
-        gm[tb] = *reinterpret_cast<const f32x4*>(&sm.gam[gs][r0]);
+        gmt[tb] = sm.gam[gs][16 * tb + ls];  // Z^T columns are tokens
       }
+      f32x4 R[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        f32x4 R;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) R[e] = bt[tb][e] * (float)vt[tb][e] - bgv[tb][e] * Y[tb][e];
-        store_tile_t(sm.rt, LDC, 16 * vb, 16 * tb, R, lane);
-        Z[tb] = Z[tb] * gm[tb];
+        for (int e = 0; e < 4; ++e) R[tb][e] = bt[tb][e] * (float)vt[tb][e] - bgv[tb][e] * Y[tb][e];
+        Z[tb] = Z[tb] * gmt[tb];
       }
+      bf16x8 rb[CS];
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) rb[cs] = acc_pair_to_frag(R[2 * cs], R[2 * cs + 1]);
       lds_barrier();  // Tm_x is complete after this barrier
-      // ---- phase B.  Operands that do not depend on this phase's results are
-      // read first so their LDS latency overlaps.
+      // ---- phase B: U = Tm R, O = diag(gam) Z + P U, S^T <- gam_n S^T + K^T Up
       const bf16* tt = sm.tt[x % 2];
       const bf16* pt = sm.pt[x % 2];
-      bf16x8 rf[CS], kt[NCB][CS], tf[NTB][CS], pf[NTB][CS];
+      bf16x8 tf[NTB][CS], pf[NTB][CS];
       f32x4 dnv[NTB];
-#pragma unroll
-      for (int cs = 0; cs < CS; ++cs) rf[cs] = frag_rows(sm.rt, LDC, 16 * vb, 32 * cs, lane);
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         dnv[tb] = *reinterpret_cast<const f32x4*>(&sm.dn[gs][16 * tb + 4 * lg]);
@@ -530,67 +594,45 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
             pf[tb][cs] = frag_cols(pt, LDC, 16 * tb, 32 * cs, lane);
           }
       }
+      const float gam_n = sm.gam[gs][CP - 1];
       __builtin_amdgcn_sched_barrier(0);
-      // U = Tm R
-      f32x4 U[NTB];
+      f32x4 U[NTB], Up[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         U[tb] = zero4();
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs)
-          if (32 * cs <= 16 * tb + 15) U[tb] = mma(tf[tb][cs], rf[cs], U[tb]);
+          if (32 * cs <= 16 * tb + 15) U[tb] = mma(tf[tb][cs], rb[cs], U[tb]);
+        Up[tb] = U[tb] * dnv[tb];
       }
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        store_tile_t(sm.rt, LDC, 16 * vb, 16 * tb, U[tb], lane);  // U^T replaces R^T
-        store_tile_t(sm.upt, LDC, 16 * vb, 16 * tb, U[tb] * dnv[tb], lane);
-      }
-      bf16x8 uf[CS], upf[CS];
+      bf16x8 ub[CS], upb[CS];
 #pragma unroll
       for (int cs = 0; cs < CS; ++cs) {
-        uf[cs] = frag_rows(sm.rt, LDC, 16 * vb, 32 * cs, lane);
-        upf[cs] = frag_rows(sm.upt, LDC, 16 * vb, 32 * cs, lane);
+        ub[cs] = acc_pair_to_frag(U[2 * cs], U[2 * cs + 1]);
+        upb[cs] = acc_pair_to_frag(Up[2 * cs], Up[2 * cs + 1]);
       }
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int cs = 0; cs < CS; ++cs) kt[cb][cs] = frag_cols_sw<KD>(kk, 16 * cb, 32 * cs, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      // O = diag(gam) Z + P U
-      f32x4 O[NTB];
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        O[tb] = Z[tb];
-#pragma unroll
-        for (int cs = 0; cs < CS; ++cs)
-          if (32 * cs <= 16 * tb + 15) O[tb] = mma(pf[tb][cs], uf[cs], O[tb]);
-      }
-      // S <- gam_n S + Up^T K
-      const float gam_n = sm.gam[gs][CP - 1];
+      // S^T <- gam_n S^T + K^T Up  (A operand: K^T by transpose reads, k = token)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = S[cb] * gam_n;
 #pragma unroll
-        for (int cs = 0; cs < CS; ++cs) acc = mma(upf[cs], kt[cb][cs], acc);
+        for (int cs = 0; cs < CS; ++cs) acc = mma(frag_cols_sw<KD>(kk, 16 * cb, 32 * cs, lane), upb[cs], acc);
         S[cb] = acc;
-        store_tile_t(sm.st, LDV, 16 * cb, 16 * vb, acc, lane);
       }
-      // O leaves through this wave's rows of rt, re-read as [token][16] so each
-      // lane stores 16 contiguous bytes of one token row.
-      bf16* ost = sm.rt + 16 * vb * LDC;
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ost[(16 * tb + 4 * lg + e) * 16 + ls] = (bf16)O[tb][e];
+      // O^T = Z^T diag(gam) + U^T P^T: lane (g, s) ends with O[token 16 tb + s]
+      // [v 16 vb + 4g .. 4g + 3], stored as one 8-byte write.
       const int t0 = x * C;
       const int n = min(C, T - t0);
-      bf16* obase = o + ((size_t)b * T + t0) * tok_v + (size_t)h * V + v0 + 16 * vb;
+      bf16* obase = o + ((size_t)b * T + t0) * tok_v + (size_t)h * V + v0 + 16 * vb + 4 * lg;
 #pragma unroll
-      for (int j = 0; j < CP / 32; ++j) {
-        const int p = lane + 64 * j;
-        const int r = p >> 1, half = p & 1;
-        const bf16x8 val = *reinterpret_cast<const bf16x8*>(&ost[r * 16 + 8 * half]);
-        if (r < n) *reinterpret_cast<bf16x8*>(obase + (size_t)r * tok_v + 8 * half) = val;
+      for (int tb = 0; tb < NTB; ++tb) {
+        f32x4 O = Z[tb];
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs)
+          if (32 * cs <= 16 * tb + 15) O = mma(ub[cs], pf[tb][cs], O);
+        const int r = 16 * tb + ls;
+        if (r < n)
+          *reinterpret_cast<bf16x4*>(obase + (size_t)r * tok_v) = bf16x4{(bf16)O[0], (bf16)O[1], (bf16)O[2], (bf16)O[3]};
       }
     }
   } else if (wave == W_LEV) {
@@ -642,7 +684,9 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     }
   } else {
     // ========================== Gram / staging waves ==========================
-    load_chunk(0);
+    // Chunk c is loaded into registers one iteration before it is staged in LDS.
+    StageRegs R;
+    load_chunk(0, R);
     const int gw = wave - W_G0;
     for (int x = -2; x < NT; ++x) {
       lds_barrier();
@@ -670,10 +714,10 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
       lds_barrier();
       {
-        const int c = x + 2;
+        const int c = x + 2;  // chunk staged now; the registers are reloaded with c + 1
         if (c >= 0 && c < NT) {
-          stage_chunk(c);
-          if (c + 1 < NT) load_chunk(c + 1);
+          stage_chunk(c, R);
+          if (c + 1 < NT) load_chunk(c + 1, R);
         }
       }
     }
@@ -682,13 +726,9 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // ---- final state
   if (wave < NCH && s_final) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int c = 16 * cb + ls;
-      if (c < K) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s_final[state_base + (size_t)(16 * vb + 4 * lg + e) * K + c] = S[cb][e];
-      }
-    }
+    for (int cb = 0; cb < NCB; ++cb)
+      if (16 * cb < K)
+        *reinterpret_cast<f32x4*>(&s_final[state_base + (size_t)(16 * vb + ls) * K + 16 * cb + 4 * lg]) = S[cb];
   }
 }
 
