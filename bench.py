@@ -11,6 +11,7 @@ The run is correctness-gated: the GPU output of input set 0 must match the
 oracle (relative L2 <= 2e-2) before any number is printed.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,6 +23,56 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 METRIC = "GDN chunk fwd tokens/s + % bf16 MFMA peak at B8·T4096·H6·d128"
+
+# Sources of the timed kernel: a traffic record measured on other sources is stale.
+KERNEL_SOURCES = ["linear_attention_sequence_chunked_amd/csrc/fwd_bf16.hip",
+                  "linear_attention_sequence_chunked_amd/csrc/gdn_api.hip",
+                  "linear_attention_sequence_chunked_amd/csrc/launch.h"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "fwd_bf16_train_B8T4096H6_hbm_traffic.md")
+COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter record, or None
+    when there is none or it was taken on different kernel sources.
+
+    The record holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the forward
+    kernel and of a calibration copy of COPY_BYTES; each kernel counter is divided
+    by the copy's reading per byte copied."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    rec = None
+    for line in open(TRAFFIC_RECORD):
+        if line.startswith("TRAFFIC_JSON "):
+            rec = json.loads(line[len("TRAFFIC_JSON "):])
+    if rec is None or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    f_fetch = rec["copy_fetch_kib"] * 1024.0 / COPY_BYTES
+    f_write = rec["copy_write_kib"] * 1024.0 / COPY_BYTES
+    return rec["fwd_fetch_kib"] * 1024.0 / f_fetch + rec["fwd_write_kib"] * 1024.0 / f_write
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size, for counter calibration:
+    rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) on this run gives the counter's
+    reading for COPY_BYTES read and COPY_BYTES written."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "kernel_source_sha256": kernel_source_hash()}),
+          flush=True)
 
 
 def algorithmic_bytes(B, T, H, K, V, esz=2, with_s0=False):
@@ -49,7 +100,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gate", action="store_true", help="skip the oracle correctness gate")
     ap.add_argument("--workload", default="train_bf16")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the known-size copy used to calibrate HBM counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the (batch, head) streams are independent, so "
               "a multi-GPU run is one of these per GPU with no communication; "
@@ -120,6 +176,7 @@ def main():
                                with_s0=w.s0_std is not None)
     aflops = algorithmic_flops(B, T, H, K, V, C)
     achieved_gbs = abytes / (kern_ms / 1e3) / 1e9
+    traffic = measured_traffic() if args.workload == "train_bf16" else None
     tflops = aflops / (kern_ms / 1e3) / 1e12
 
     cpu = None
@@ -154,7 +211,7 @@ def main():
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": K,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel_ms": kern_ms, "algorithmic_bytes": abytes},
         "mfma": {"tflops_algorithmic": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flops": aflops},
