@@ -55,6 +55,38 @@ typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef bf16x4 __attribute__((address_space(3))) lds_bf16x4;
+typedef bf16x8 __attribute__((address_space(3))) lds_bf16x8;
+typedef bf16 __attribute__((address_space(3))) lbf16;
+typedef float __attribute__((address_space(3))) lf32;
+typedef f32x4 __attribute__((address_space(3))) lf32x4;
+
+// LDS pointer with a per-lane part, made opaque to the optimiser: every access
+// of a tile is then this register plus a constant in the instruction's offset
+// field, instead of one precomputed address register (and one add per chunk)
+// per access.
+template <typename T>
+__device__ __forceinline__ T* pin(T* p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds(T* p) {
+  return (__attribute__((address_space(3))) T*)p;
+}
+__device__ __forceinline__ bf16x8 ld8(const lbf16* p) { return *reinterpret_cast<const lds_bf16x8*>(p); }
+__device__ __forceinline__ bf16x4 tr4(const lbf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+// MFMA operand from a [k][row] array through a base that already holds the
+// lane part (row k0 + 8g + s/4, column 4(s%4)): two transpose reads.
+__device__ __forceinline__ bf16x8 frag_cols_at(const lbf16* cb, int ld, int r0, int k0) {
+  const bf16x4 lo = tr4(cb + k0 * ld + r0), hi = tr4(cb + (k0 + 4) * ld + r0);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ int cols_lane(int ld, int lane) {
+  return (8 * (lane >> 4) + ((lane & 15) >> 2)) * ld + 4 * (lane & 3);
+}
+__device__ __forceinline__ int rows_lane(int ld, int lane) { return (lane & 15) * ld + 8 * (lane >> 4); }
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -190,16 +222,26 @@ struct alignas(16) Smem {
   static constexpr int APK = (NTB == 4 ? 96 : 16) * LDA;
   bf16 k[3][CP * (KD + 8)];            // keys [token][channel], padded rows
   bf16 q[2][CP * (KD + 8)];            // queries, padded rows
-  bf16 v[2][CP * VS];                  // value slice [token][v]
-  float gl[3][CP];                     // cumulative log2 gate
-  float gam[3][CP];                    // 2^g
-  float beta[3][CP];
-  float bg[3][CP];                     // beta * gam
-  float dn[3][CP];                     // gam_n / gam
+  // value slice [token][v]; rows of 96 bytes keep the transpose reads of 8
+  // consecutive token rows on distinct banks
+  static constexpr int LDV = (VS == 16 || VS == 32) ? 48 : VS + 16;
+  bf16 v[2][CP * LDV];
+  struct Gates {
+    float gl[CP];                      // cumulative log2 gate
+    float gam[CP];                     // 2^g
+    float beta[CP];
+    float bg[CP];                      // beta * gam
+    float dn[CP];                      // gam_n / gam
+  } gt[3];
+  // offsets (in floats) of the gate vectors from gl within one slot
+  static constexpr int GAM = CP, BETA = 2 * CP, BG = 3 * CP, DN = 4 * CP;
   bf16 pt[2][CP * LDC];                // P^T: pt[i][r]
   bf16 tt[2][CP * LDC];                // Tm^T: tt[j][i]; upper blocks zero (level scratch)
   bf16 ap[2][APK];                     // off-diagonal A^T blocks used by the levels
-  float ad[NTB * 256];                 // diagonal A blocks, fp32, transposed [c][r]
+  // diagonal A blocks, fp32, transposed [c][r]; blocks ADS floats apart so the
+  // four blocks read at once by the diagonal solve fall on different banks
+  static constexpr int ADS = 256 + 4;
+  float ad[NTB * ADS];
 };
 
 // Off-diagonal blocks of Tm = (I + A)^-1 from its diagonal blocks (already in
@@ -267,12 +309,13 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
   constexpr int LDC = SM::LDC, LDA = SM::LDA;
   const int ls = lane & 15, lg = lane >> 4;
   const int gs = c % 3;
-  const bf16* kk = sm.k[c % 3];
-  const bf16* qq = sm.q[c % 2];
-  bf16* ptw = sm.pt[c % 2];
-  bf16* apw = sm.ap[c % 2];
-  const float* gl = sm.gl[gs];
-  const float* bta = sm.beta[gs];
+  constexpr int LDK = KD + 8;
+  const lbf16* kr = pin(lds(sm.k[gs]) + rows_lane(LDK, lane));
+  const lbf16* qr = pin(lds(sm.q[c % 2]) + rows_lane(LDK, lane));
+  const lf32* gl = lds(sm.gt[gs].gl);
+  const lf32* g1 = pin(gl + ls);
+  const lf32* g4 = pin(gl + 4 * lg);
+  constexpr int BOFF = SM::BETA;
   // every operand and gate value is requested before the first MFMA
   bf16x8 kf[R1 + 1][KS], af[2][KS];
   f32x4 gr[2], br[2];
@@ -280,18 +323,18 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
 #pragma unroll
   for (int tb = 0; tb <= R1; ++tb) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = frag_rows_sw<KD>(kk, 16 * tb, 32 * ks, lane);
-    gi[tb] = gl[16 * tb + ls];
+    for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = ld8(kr + 16 * tb * LDK + 32 * ks);
+    gi[tb] = g1[16 * tb];
   }
 #pragma unroll
   for (int ri = 0; ri < 2; ++ri) {
     const int tr = ri == 0 ? R0 : R1;
     if (TYPE == 1) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) af[ri][ks] = frag_rows_sw<KD>(qq, 16 * tr, 32 * ks, lane);
+      for (int ks = 0; ks < KS; ++ks) af[ri][ks] = ld8(qr + 16 * tr * LDK + 32 * ks);
     }
-    gr[ri] = *reinterpret_cast<const f32x4*>(&gl[16 * tr + 4 * lg]);
-    br[ri] = *reinterpret_cast<const f32x4*>(&bta[16 * tr + 4 * lg]);
+    gr[ri] = *reinterpret_cast<const lf32x4*>(g4 + 16 * tr);
+    br[ri] = *reinterpret_cast<const lf32x4*>(g4 + BOFF + 16 * tr);
   }
   __builtin_amdgcn_sched_barrier(0);
   // all tiles advance together over the k-steps: independent accumulators
@@ -312,6 +355,14 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
   // exponential.  Off-diagonal tiles (every i < r): 2^(g_r - g_ref) 2^(g_ref - g_i)
   // with g_ref the gate of the row block's first token, both factors <= 1; the
   // row factor (times beta for A) is shared by the row block's tiles.
+  lbf16* pw = nullptr;
+  lbf16* aw = nullptr;
+  lf32* adw = nullptr;
+  if (TYPE == 1) pw = pin(lds(sm.pt[c % 2]) + ls * LDC + 4 * lg);
+  if (TYPE == 0) {
+    aw = pin(lds(sm.ap[c % 2]) + ls * LDA + 4 * lg);
+    adw = pin(lds(sm.ad) + ls * 16 + 4 * lg);
+  }
   f32x4 rowf[2];
 #pragma unroll
   for (int ri = 0; ri < 2; ++ri) {
@@ -341,14 +392,17 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) val[e] = rowf[ri][e] * (colf * acc[t][e]);
     }
+    // accumulator tiles are stored transposed: lane (g, s) writes row s of the
+    // transposed tile, 4 consecutive bf16 (or fp32) at column 4g
+    const bf16x4 vb4 = bf16x4{(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
     if (TYPE == 1) {
-      store_tile_t(ptw, LDC, 16 * tc, 16 * tr, val, lane);
+      *reinterpret_cast<lds_bf16x4*>(pw + 16 * tc * LDC + 16 * tr) = vb4;
     } else if (tc == tr) {
-      *reinterpret_cast<f32x4*>(&sm.ad[tr * 256 + ls * 16 + 4 * lg]) = val;  // [c][r]
+      *reinterpret_cast<lf32x4*>(adw + tr * SM::ADS) = val;  // [c][r]
     } else {
       // packed A^T blocks: (1,0) -> 0, (3,2) -> 16, (2,0..1) -> 32.., (3,0..1) -> 64..
       const int off = tr == 1 ? 0 : (tr == 3 && tc == 2 ? 16 : (tr == 2 ? 32 : 64) + 16 * tc);
-      store_tile_t(apw, LDA, off, 0, val, lane);
+      *reinterpret_cast<lds_bf16x4*>(aw + off * LDA) = vb4;
     }
   }
   (void)NTB;
@@ -371,6 +425,9 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   constexpr int W_DIAG = NCH + 1;       // diagonal-solve wave
   constexpr int W_G0 = NCH + 2;         // first Gram / staging wave
   constexpr int NG = kWaves - W_G0;     // Gram / staging waves
+  // the gates go to the Gram wave whose SIMD partner (the levels wave) is idle
+  // while chunks are staged
+  constexpr int W_GATE = W_G0 + (NG >= 3 ? 2 : 0);
   static_assert(NG >= 2, "need at least two Gram waves");
   __shared__ SM sm;
 
@@ -441,7 +498,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     const int r = p / (VS / 8), ch = (p % (VS / 8)) * 8;
     vrow[j] = p < VPIECES ? r : CP;
     vgo[j] = r * (int)tok_v + ch;
-    vlo[j] = r * VS + ch;
+    vlo[j] = r * SM::LDV + ch;
   }
 
   auto load_chunk = [&](int c, StageRegs& R) {
@@ -466,8 +523,8 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     }
     R.a = 1.0f;
     R.b = 0.0f;
-    if (sl < n) {  // the first Gram wave holds the gates
-      const size_t go = ((size_t)b * T + t0 + sl) * H + h;
+    if (wave == W_GATE && lane < n) {  // one Gram wave holds the gates
+      const size_t go = ((size_t)b * T + t0 + lane) * H + h;
       R.a = alpha[go];
       R.b = beta[go];
     }
@@ -475,28 +532,33 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
   auto stage_chunk = [&](int c, const StageRegs& R) {
     const int ks = c % 3, qs = c % 2;
+    // piece j of a staging lane sits NSL / (KD / 8) token rows below piece 0
+    static_assert(NSL % (KD / 8) == 0 && NSL % (VS / 8) == 0, "staging pieces must tile rows");
+    lbf16* kst = pin(lds(sm.k[ks]) + klo[0]);
+    lbf16* qst = pin(lds(sm.q[qs]) + klo[0]);
+    lbf16* vst = pin(lds(sm.v[qs]) + vlo[0]);
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       if (sl + NSL * j < KPIECES) {  // pieces past K are stored as zeros
-        *reinterpret_cast<bf16x8*>(&sm.k[ks][klo[j]]) = R.k[j];
-        *reinterpret_cast<bf16x8*>(&sm.q[qs][klo[j]]) = R.q[j];
+        *reinterpret_cast<lds_bf16x8*>(kst + j * (NSL / (KD / 8)) * (KD + 8)) = R.k[j];
+        *reinterpret_cast<lds_bf16x8*>(qst + j * (NSL / (KD / 8)) * (KD + 8)) = R.q[j];
       }
     }
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
-      if (vrow[j] < CP) *reinterpret_cast<bf16x8*>(&sm.v[qs][vlo[j]]) = R.v[j];
-    if (wave == W_G0) {
+      if (vrow[j] < CP) *reinterpret_cast<lds_bf16x8*>(vst + j * (NSL / (VS / 8)) * SM::LDV) = R.v[j];
+    if (wave == W_GATE) {
       const float la = (lane < CP) ? __builtin_amdgcn_logf(R.a) : 0.0f;  // log2; padding: alpha = 1
       const float bt = (lane < CP) ? R.b : 0.0f;
       const float g = wave_scan(la, lane);
       const float glast = bits_f(__builtin_amdgcn_readlane(f_bits(g), CP - 1));
       if (lane < CP) {
         const float gm = __builtin_amdgcn_exp2f(g);
-        sm.gl[ks][lane] = g;
-        sm.gam[ks][lane] = gm;
-        sm.beta[ks][lane] = bt;
-        sm.bg[ks][lane] = bt * gm;
-        sm.dn[ks][lane] = __builtin_amdgcn_exp2f(glast - g);
+        sm.gt[ks].gl[lane] = g;
+        sm.gt[ks].gam[lane] = gm;
+        sm.gt[ks].beta[lane] = bt;
+        sm.gt[ks].bg[lane] = bt * gm;
+        sm.gt[ks].dn[lane] = __builtin_amdgcn_exp2f(glast - g);
       }
     }
   };
@@ -509,16 +571,18 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     // Everything that depends on the state stays in registers: the state (as
     // S^T tiles), R and U become MFMA operands through permlane swaps.  Only
     // the chunk's K, Q, V, gates, Tm and P come from LDS.
-    for (int x = -2; x < NT; ++x) {
+    // the two pipeline-fill iterations (x = -2, -1) have no chain work
+    for (int i = 0; i < 4; ++i) lds_barrier();
+    for (int x = 0; x < NT; ++x) {
       lds_barrier();
-      if (x < 0) {
-        lds_barrier();
-        continue;
-      }
-      const bf16* kk = sm.k[x % 3];
-      const bf16* qq = sm.q[x % 2];
-      const bf16* vv = sm.v[x % 2];
       const int gs = x % 3;
+      constexpr int LDK = KD + 8;
+      const lbf16* kr = pin(lds(sm.k[gs]) + rows_lane(LDK, lane));      // K rows
+      const lbf16* qr = pin(lds(sm.q[x % 2]) + rows_lane(LDK, lane));   // Q rows
+      const lbf16* kc = pin(lds(sm.k[gs]) + cols_lane(LDK, lane));      // K^T by transpose reads
+      const lbf16* vc = pin(lds(sm.v[x % 2]) + (4 * lg + (ls >> 2)) * SM::LDV + 16 * vb + 4 * (ls & 3));
+      const lf32* g4 = pin(lds(&sm.gt[gs].beta[0]) + 4 * lg);             // per-row gate vectors
+      const lf32* g1 = pin(lds(&sm.gt[gs].gam[0]) + ls);                  // per-column gates
       // ---- phase A: Y = K S^T and Z^T = S Q^T (the state operand has k = key
       // channel; as the B operand of Y and the A operand of Z^T it is the same
       // registers).
@@ -527,8 +591,8 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       bf16x8 sbf[KS], ka[2][NTB], qa[2][NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        ka[0][tb] = frag_rows_sw<KD>(kk, 16 * tb, 0, lane);
-        qa[0][tb] = frag_rows_sw<KD>(qq, 16 * tb, 0, lane);
+        ka[0][tb] = ld8(kr + 16 * tb * LDK);
+        qa[0][tb] = ld8(qr + 16 * tb * LDK);
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) sbf[ks] = acc_pair_to_frag(S[2 * ks], S[2 * ks + 1]);
@@ -543,8 +607,8 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         if (ks + 1 < KS) {
 #pragma unroll
           for (int tb = 0; tb < NTB; ++tb) {
-            ka[(ks + 1) & 1][tb] = frag_rows_sw<KD>(kk, 16 * tb, 32 * (ks + 1), lane);
-            qa[(ks + 1) & 1][tb] = frag_rows_sw<KD>(qq, 16 * tb, 32 * (ks + 1), lane);
+            ka[(ks + 1) & 1][tb] = ld8(kr + 16 * tb * LDK + 32 * (ks + 1));
+            qa[(ks + 1) & 1][tb] = ld8(qr + 16 * tb * LDK + 32 * (ks + 1));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -562,11 +626,10 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       float gmt[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        const int r0 = 16 * tb + 4 * lg;
-        vt[tb] = tr_read(vv + (r0 + (ls >> 2)) * VS + 16 * vb + 4 * (ls & 3));
-        bt[tb] = *reinterpret_cast<const f32x4*>(&sm.beta[gs][r0]);
-        bgv[tb] = *reinterpret_cast<const f32x4*>(&sm.bg[gs][r0]);
-        gmt[tb] = sm.gam[gs][16 * tb + ls];  // Z^T columns are tokens
+        vt[tb] = tr4(vc + 16 * tb * SM::LDV);
+        bt[tb] = *reinterpret_cast<const lf32x4*>(g4 + 16 * tb);
+        bgv[tb] = *reinterpret_cast<const lf32x4*>(g4 + (SM::BG - SM::BETA) + 16 * tb);
+        gmt[tb] = g1[16 * tb];  // Z^T columns are tokens
       }
       f32x4 R[NTB];
 #pragma unroll
@@ -580,21 +643,21 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       for (int cs = 0; cs < CS; ++cs) rb[cs] = acc_pair_to_frag(R[2 * cs], R[2 * cs + 1]);
       lds_barrier();  // Tm_x is complete after this barrier
       // ---- phase B: U = Tm R, O = diag(gam) Z + P U, S^T <- gam_n S^T + K^T Up
-      const bf16* tt = sm.tt[x % 2];
-      const bf16* pt = sm.pt[x % 2];
+      const lbf16* tc = pin(lds(sm.tt[x % 2]) + cols_lane(LDC, lane));
+      const lbf16* pc = tc + (&sm.pt[0][0] - &sm.tt[0][0]);
       bf16x8 tf[NTB][CS], pf[NTB][CS];
       f32x4 dnv[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        dnv[tb] = *reinterpret_cast<const f32x4*>(&sm.dn[gs][16 * tb + 4 * lg]);
+        dnv[tb] = *reinterpret_cast<const lf32x4*>(g4 + (SM::DN - SM::BETA) + 16 * tb);
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs)
           if (32 * cs <= 16 * tb + 15) {  // Tm and P are lower triangular
-            tf[tb][cs] = frag_cols(tt, LDC, 16 * tb, 32 * cs, lane);
-            pf[tb][cs] = frag_cols(pt, LDC, 16 * tb, 32 * cs, lane);
+            tf[tb][cs] = frag_cols_at(tc, LDC, 16 * tb, 32 * cs);
+            pf[tb][cs] = frag_cols_at(pc, LDC, 16 * tb, 32 * cs);
           }
       }
-      const float gam_n = sm.gam[gs][CP - 1];
+      const float gam_n = sm.gt[gs].gam[CP - 1];
       __builtin_amdgcn_sched_barrier(0);
       f32x4 U[NTB], Up[NTB];
 #pragma unroll
@@ -616,7 +679,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = S[cb] * gam_n;
 #pragma unroll
-        for (int cs = 0; cs < CS; ++cs) acc = mma(frag_cols_sw<KD>(kk, 16 * cb, 32 * cs, lane), upb[cs], acc);
+        for (int cs = 0; cs < CS; ++cs) acc = mma(frag_cols_at(kc, LDK, 16 * cb, 32 * cs), upb[cs], acc);
         S[cb] = acc;
       }
       // O^T = Z^T diag(gam) + U^T P^T: lane (g, s) ends with O[token 16 tb + s]
@@ -637,9 +700,10 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     }
   } else if (wave == W_LEV) {
     // ============================ levels wave ============================
-    for (int x = -2; x < NT; ++x) {
+    for (int i = 0; i < 4; ++i) lds_barrier();
+    for (int x = 0; x < NT; ++x) {
       lds_barrier();
-      if (x >= 0) levels_part<CP>(sm.tt[x % 2], sm.ap[x % 2], lane, 0);
+      levels_part<CP>(sm.tt[x % 2], sm.ap[x % 2], lane, 0);
       lds_barrier();
     }
   } else if (wave == W_DIAG) {
@@ -656,7 +720,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         // acc[r] carries sum_{i<r} L[r][i] x_i.
         bf16* tt = sm.tt[c % 2];
         const int bb = lg, j = ls;
-        const float* Lt = &sm.ad[bb * 256];  // Lt[c][r] = L[r][c]
+        const float* Lt = &sm.ad[bb * SM::ADS];  // Lt[c][r] = L[r][c]
         float xv[16], acc[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
