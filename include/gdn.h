@@ -1,6 +1,6 @@
 /*
- * gdn.h -- C ABI of the chunkwise gated-delta-rule forward for AMD Instinct
- * MI355X (gfx950).
+ * gdn.h -- C ABI of the chunkwise gated-delta-rule forward and backward for
+ * AMD Instinct MI355X (gfx950).
  *
  * The operation.  For every batch b and head h, with state S of shape [V, K]:
  *
@@ -42,13 +42,14 @@
 #ifndef GDN_H_
 #define GDN_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -103,6 +104,53 @@ GDN_API gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *alpha, const float *beta,
                            const float *initial_state,
                            void *o, float *final_state,
+                           int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                           int64_t chunk, gdn_dtype_t dtype, void *stream);
+
+/*
+ * gdn_chunk_bwd_workspace_size -- bytes of device workspace gdn_chunk_bwd needs
+ * for these sizes: two float32 [V, K] states per (batch, head, backward chunk),
+ * the backward chunk being min(chunk, 32) tokens, i.e.
+ * 2 * B * H * ceil(T / min(chunk, 32)) * V * K * 4 bytes.  Returns 0 when a size
+ * is not positive.
+ */
+GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K,
+                                            int64_t V, int64_t chunk);
+
+/*
+ * gdn_chunk_bwd -- reverse mode of gdn_chunk_fwd for the loss
+ *     L = sum(o * d_o) + sum(final_state * d_final_state).
+ *
+ *   q, k, v, alpha, beta, initial_state   as for gdn_chunk_fwd (read only)
+ *   d_o            [B,T,H,V] dtype        gradient of o (read only)
+ *   d_final_state  [B,H,V,K] float32      gradient of final_state, or NULL for zeros
+ *   dq, dk         [B,T,H,K] dtype        dL/dq, dL/dk (written)
+ *   dv             [B,T,H,V] dtype        dL/dv (written)
+ *   dalpha, dbeta  [B,T,H]   float32      dL/dalpha, dL/dbeta with respect to the
+ *                                         gates themselves (written)
+ *   d_initial_state [B,H,V,K] float32     dL/dinitial_state, or NULL to skip
+ *   workspace      device scratch of workspace_bytes >= gdn_chunk_bwd_workspace_size(...);
+ *                  owned by the caller, contents undefined after the call
+ *   B .. dtype, stream                    as for gdn_chunk_fwd
+ *
+ * The chunk-start states are recomputed from the inputs (nothing is kept from a
+ * forward call), the chunks are walked in reverse to carry the state gradient,
+ * and every chunk then forms its token gradients from its two boundary states:
+ * "OpenGDN 0.1.0", section "Core operator reference" (backward from recomputed
+ * fp32 chunk-boundary states) and "Sparse Delta Memory: layer and kernels",
+ * sections "What the layer computes" and "Execution" (the backward walks the
+ * chunks in reverse).  All arithmetic is float32 in a fixed order, so results
+ * are bitwise reproducible; dq, dk, dv are rounded to dtype once.  No output may
+ * overlap any other buffer (inputs, other outputs, workspace).  Errors as for
+ * gdn_chunk_fwd; a workspace smaller than required is GDN_ERROR_INVALID_VALUE.
+ */
+GDN_API gdn_status_t gdn_chunk_bwd(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta,
+                           const float *initial_state,
+                           const void *d_o, const float *d_final_state,
+                           void *dq, void *dk, void *dv,
+                           float *dalpha, float *dbeta, float *d_initial_state,
+                           void *workspace, size_t workspace_bytes,
                            int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                            int64_t chunk, gdn_dtype_t dtype, void *stream);
 

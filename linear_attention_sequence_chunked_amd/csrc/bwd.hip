@@ -1,0 +1,509 @@
+// Chunkwise gated-delta-rule backward: reverse mode of the forward in
+// fwd_f32.hip / fwd_bf16.hip for the loss <o, dO> + <S_final, dS_final>.
+//
+// The chunk form of the forward ("Sparse Delta Memory: layer and kernels",
+// section "What the layer computes"; operator contract of "OpenGDN 0.1.0",
+// section "Core operator reference"), for a chunk of n tokens with start state S:
+//
+//   g = cumsum(ln alpha), gam = e^g, D = e^(g_last - g)
+//   M_ri = e^(g_r - g_i) k_r.k_i (i < r),  A = diag(beta) M,  Tm = (I + A)^-1
+//   P_ri = e^(g_r - g_i) q_r.k_i (i <= r)
+//   Y = K S^T, Z = Q S^T, R = diag(beta) V - diag(beta gam) Y, U = Tm R
+//   O = diag(gam) Z + P U,  S' = gam_last S + U^T diag(D) K
+//
+// differentiated by hand.  With dS' the gradient of the chunk-end state:
+//
+//   W  = K dS'^T,  dU = diag(D) W + P^T dO,  dR = Tm^T dU
+//   dS (chunk start) = gam_last dS' + dO^T diag(gam) Q - dR^T diag(beta gam) K
+//   dP = tril(dO U^T),  dA = strict_tril(-dR U^T)
+//   dQ = diag(gam) dO S + (dP o E) K                       (E_ri = e^(g_r - g_i))
+//   dK = diag(D) U dS' - diag(beta gam) dR S + (dP o E)^T Q + (dA o bE) K + (dA o bE)^T K
+//   dV = diag(beta) dR
+//   dbeta_r = dR_r.(v_r - gam_r Y_r) + sum_i dA_ri M_ri
+//   dg_r = gam_r dO_r.Z_r - beta_r gam_r dR_r.Y_r - D_r U_r.W_r
+//          + sum_i (dP o P)_ri - sum_i (dP o P)_ir + sum_i (dA o A)_ri - sum_i (dA o A)_ir
+//   dg_last += gam_last <dS', S> + sum_r D_r U_r.W_r
+//   d ln alpha_t = sum_{r >= t} dg_r,   dalpha_t = d ln alpha_t / alpha_t
+//
+// Three launches: (1) the scalar forward recomputes the chunk-start states into
+// the workspace; (2) a reverse walk over the chunks carries dS and stores each
+// chunk's dS'; (3) every chunk computes its token gradients independently.
+// All arithmetic is fp32 in a fixed order (bitwise reproducible); inputs and the
+// dq, dk, dv outputs have the dtype of q.  The backward chunk is at most 32
+// tokens (chunk size changes results only by rounding).
+#include "launch.h"
+
+#include <hip/hip_bf16.h>
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(float x) {
+  return __float2bfloat16(x);  // round to nearest even
+}
+
+// Gates of one chunk into LDS: g (cumulative natural-log gate, summed in token
+// order), gam = e^g, beta.  Leaves a barrier behind.
+__device__ __forceinline__ void load_gates(const float* alpha, const float* beta, float* sg,
+                                           float* sgam, float* sb, int b, int h, int T, int H,
+                                           int t0, int n, int tid) {
+  if (tid < n) {
+    const size_t go = ((size_t)b * T + t0 + tid) * H + h;
+    sg[tid] = logf(alpha[go]);
+    sb[tid] = beta[go];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.0f;
+    for (int r = 0; r < n; ++r) {
+      acc += sg[r];
+      sg[r] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < n) sgam[tid] = expf(sg[tid]);
+  __syncthreads();
+}
+
+// M (strictly lower, decayed K K^T, no beta), P (lower, decayed Q K^T) and
+// Tm = (I + diag(beta) M)^-1 by forward substitution (one column per thread).
+// Leading dimension C.  Leaves a barrier behind.
+__device__ __forceinline__ void chunk_mats(const float* sq, const float* sk, const float* sg,
+                                           const float* sb, float* sM, float* sP, float* sT,
+                                           int n, int C, int K, int tid) {
+  for (int i = tid; i < C * C; i += kThreads) {
+    const int r = i / C, j = i - r * C;
+    float m = 0.0f, p = 0.0f;
+    if (r < n && j <= r) {
+      float dk = 0.0f, dq = 0.0f;
+      for (int c = 0; c < K; ++c) {
+        dk = fmaf(sk[r * K + c], sk[j * K + c], dk);
+        dq = fmaf(sq[r * K + c], sk[j * K + c], dq);
+      }
+      const float e = expf(sg[r] - sg[j]);
+      if (j < r) m = e * dk;
+      p = e * dq;
+    }
+    sM[i] = m;
+    sP[i] = p;
+  }
+  __syncthreads();
+  if (tid < n) {
+    const int j = tid;
+    for (int r = 0; r < j; ++r) sT[r * C + j] = 0.0f;
+    sT[j * C + j] = 1.0f;
+    for (int r = j + 1; r < n; ++r) {
+      float s = 0.0f;
+      for (int i = j; i < r; ++i) s = fmaf(sb[r] * sM[r * C + i], sT[i * C + j], s);
+      sT[r * C + j] = -s;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// (2) Reverse walk: one workgroup per (batch, head, value slice of VS rows).
+// Stores dS' of every chunk to ws_dS [B, H, NT, V, K] and the gradient of the
+// initial state.
+template <typename TIn>
+__global__ void __launch_bounds__(kThreads)
+bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ d_o,
+                  const float* __restrict__ alpha, const float* __restrict__ beta,
+                  const float* __restrict__ d_sfinal, float* __restrict__ d_s0,
+                  float* __restrict__ ws_dS, int T, int H, int K, int V, int C, int VS) {
+  extern __shared__ float lds[];
+  float* sq = lds;                 // [C][K]
+  float* sk = sq + C * K;          // [C][K]
+  float* sdo = sk + C * K;         // [C][VS]
+  float* sM = sdo + C * VS;        // [C][C]
+  float* sP = sM + C * C;          // [C][C]
+  float* sT = sP + C * C;          // [C][C]
+  float* sdU = sT + C * C;         // [C][VS]
+  float* sdR = sdU + C * VS;       // [C][VS]
+  float* sdS = sdR + C * VS;       // [VS][K]
+  float* sg = sdS + VS * K;        // [C]
+  float* sgam = sg + C;
+  float* sb = sgam + C;
+
+  const int tid = threadIdx.x;
+  const int v0 = blockIdx.x * VS;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int NT = (T + C - 1) / C;
+  const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
+
+  for (int i = tid; i < VS * K; i += kThreads) sdS[i] = d_sfinal ? d_sfinal[state_base + i] : 0.0f;
+
+  for (int c = NT - 1; c >= 0; --c) {
+    const int t0 = c * C;
+    const int n = min(C, T - t0);
+    __syncthreads();
+    float* dst = ws_dS + ((((size_t)b * H + h) * NT + c) * V + v0) * (size_t)K;
+    for (int i = tid; i < VS * K; i += kThreads) dst[i] = sdS[i];
+    for (int i = tid; i < n * K; i += kThreads) {
+      const int r = i / K, e = i - r * K;
+      const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + e;
+      sq[i] = to_f32(q[off]);
+      sk[i] = to_f32(k[off]);
+    }
+    for (int i = tid; i < n * VS; i += kThreads) {
+      const int r = i / VS, e = i - r * VS;
+      sdo[i] = to_f32(d_o[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e]);
+    }
+    load_gates(alpha, beta, sg, sgam, sb, b, h, T, H, t0, n, tid);
+    chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, tid);
+    const float glast = sg[n - 1];
+    // dU = diag(D) K dS'^T + P^T dO
+    for (int i = tid; i < n * VS; i += kThreads) {
+      const int r = i / VS, e = i - r * VS;
+      float w = 0.0f;
+      for (int j = 0; j < K; ++j) w = fmaf(sk[r * K + j], sdS[e * K + j], w);
+      float acc = expf(glast - sg[r]) * w;
+      for (int rr = r; rr < n; ++rr) acc = fmaf(sP[rr * C + r], sdo[rr * VS + e], acc);
+      sdU[i] = acc;
+    }
+    __syncthreads();
+    // dR = Tm^T dU
+    for (int i = tid; i < n * VS; i += kThreads) {
+      const int r = i / VS, e = i - r * VS;
+      float acc = 0.0f;
+      for (int rr = r; rr < n; ++rr) acc = fmaf(sT[rr * C + r], sdU[rr * VS + e], acc);
+      sdR[i] = acc;
+    }
+    __syncthreads();
+    // dS <- gam_last dS + dO^T diag(gam) Q - dR^T diag(beta gam) K
+    const float gam_last = sgam[n - 1];
+    for (int i = tid; i < VS * K; i += kThreads) {
+      const int e = i / K, j = i - e * K;
+      float acc = gam_last * sdS[i];
+      for (int r = 0; r < n; ++r) {
+        acc = fmaf(sgam[r] * sdo[r * VS + e], sq[r * K + j], acc);
+        acc = fmaf(-sb[r] * sgam[r] * sdR[r * VS + e], sk[r * K + j], acc);
+      }
+      sdS[i] = acc;
+    }
+  }
+  __syncthreads();
+  if (d_s0)
+    for (int i = tid; i < VS * K; i += kThreads) d_s0[state_base + i] = sdS[i];
+}
+
+// ---------------------------------------------------------------------------
+// (3) Token gradients of one chunk: one workgroup per (chunk, head, batch).
+// dQ and dK accumulate in registers (QPT elements per thread), dP and dA in
+// LDS; the value axis is walked in slices of VS.
+constexpr int kBwdC = 32;   // backward chunk (tokens)
+constexpr int kBwdVS = 32;  // value slice of the local kernel
+constexpr int kQPT = kBwdC * 128 / kThreads;
+
+template <typename TIn>
+__global__ void __launch_bounds__(kThreads)
+bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+                 const TIn* __restrict__ d_o, const float* __restrict__ alpha,
+                 const float* __restrict__ beta, const float* __restrict__ ws_S,
+                 const float* __restrict__ ws_dS, TIn* __restrict__ dq, TIn* __restrict__ dk,
+                 TIn* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta,
+                 int T, int H, int K, int V, int C) {
+  constexpr int VS = kBwdVS;
+  extern __shared__ float lds[];
+  float* sq = lds;                 // [C][K]
+  float* sk = sq + C * K;          // [C][K]
+  float* sM = sk + C * K;          // [C][C]
+  float* sP = sM + C * C;
+  float* sT = sP + C * C;
+  float* sdP = sT + C * C;
+  float* sdA = sdP + C * C;
+  float* sv = sdA + C * C;         // [C][VS] slices
+  float* sdo = sv + C * VS;
+  float* sY = sdo + C * VS;
+  float* sZ = sY + C * VS;
+  float* sW = sZ + C * VS;
+  float* sU = sW + C * VS;         // R, then U
+  float* sdU = sU + C * VS;
+  float* sdR = sdU + C * VS;
+  float* sS = sdR + C * VS;        // [VS][K]
+  float* sdS = sS + VS * K;        // [VS][K]
+  float* sg = sdS + VS * K;        // [C]
+  float* sgam = sg + C;
+  float* sb = sgam + C;
+  float* sdb = sb + C;             // dbeta accumulator
+  float* sdg = sdb + C;            // dg accumulator
+  float* sred = sdg + C;           // [kThreads] reduction scratch
+
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int NT = (T + C - 1) / C;
+  const int t0 = c * C;
+  const int n = min(C, T - t0);
+  const size_t ck = (((size_t)b * H + h) * NT + c) * (size_t)V * K;
+
+  for (int i = tid; i < n * K; i += kThreads) {
+    const int r = i / K, e = i - r * K;
+    const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + e;
+    sq[i] = to_f32(q[off]);
+    sk[i] = to_f32(k[off]);
+  }
+  if (tid < C) {
+    sdb[tid] = 0.0f;
+    sdg[tid] = 0.0f;
+  }
+  for (int i = tid; i < C * C; i += kThreads) {
+    sdP[i] = 0.0f;
+    sdA[i] = 0.0f;
+  }
+  load_gates(alpha, beta, sg, sgam, sb, b, h, T, H, t0, n, tid);
+  chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, tid);
+  const float glast = sg[n - 1];
+  const float gam_last = sgam[n - 1];
+
+  float aq[kQPT], ak[kQPT];
+#pragma unroll
+  for (int j = 0; j < kQPT; ++j) aq[j] = ak[j] = 0.0f;
+  float sdot = 0.0f, esum = 0.0f;  // <dS', S> and sum_r D_r U_r.W_r, per-thread partials
+
+  for (int v0 = 0; v0 < V; v0 += VS) {
+    const int vs = min(VS, V - v0);
+    __syncthreads();
+    for (int i = tid; i < n * vs; i += kThreads) {
+      const int r = i / vs, e = i - r * vs;
+      const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e;
+      sv[r * VS + e] = to_f32(v[off]);
+      sdo[r * VS + e] = to_f32(d_o[off]);
+    }
+    for (int i = tid; i < vs * K; i += kThreads) {
+      sS[i] = ws_S[ck + (size_t)v0 * K + i];
+      sdS[i] = ws_dS[ck + (size_t)v0 * K + i];
+    }
+    __syncthreads();
+    // Y = K S^T, Z = Q S^T, W = K dS'^T;  R = diag(beta) V - diag(beta gam) Y
+    for (int i = tid; i < n * vs; i += kThreads) {
+      const int r = i / vs, e = i - r * vs;
+      float y = 0.0f, z = 0.0f, w = 0.0f;
+      for (int j = 0; j < K; ++j) {
+        const float kk = sk[r * K + j];
+        y = fmaf(kk, sS[e * K + j], y);
+        z = fmaf(sq[r * K + j], sS[e * K + j], z);
+        w = fmaf(kk, sdS[e * K + j], w);
+      }
+      sY[r * VS + e] = y;
+      sZ[r * VS + e] = z;
+      sW[r * VS + e] = w;
+      sdR[r * VS + e] = sb[r] * sv[r * VS + e] - sb[r] * sgam[r] * y;  // R (temporary)
+    }
+    __syncthreads();
+    // U = Tm R;  <dS', S> partials
+    for (int i = tid; i < n * vs; i += kThreads) {
+      const int r = i / vs, e = i - r * vs;
+      float u = 0.0f;
+      for (int j = 0; j <= r; ++j) u = fmaf(sT[r * C + j], sdR[j * VS + e], u);
+      sU[r * VS + e] = u;
+    }
+    for (int i = tid; i < vs * K; i += kThreads) sdot = fmaf(sdS[i], sS[i], sdot);
+    __syncthreads();
+    // dU = diag(D) W + P^T dO
+    for (int i = tid; i < n * vs; i += kThreads) {
+      const int r = i / vs, e = i - r * vs;
+      float acc = expf(glast - sg[r]) * sW[r * VS + e];
+      for (int rr = r; rr < n; ++rr) acc = fmaf(sP[rr * C + r], sdo[rr * VS + e], acc);
+      sdU[r * VS + e] = acc;
+    }
+    __syncthreads();
+    // dR = Tm^T dU
+    for (int i = tid; i < n * vs; i += kThreads) {
+      const int r = i / vs, e = i - r * vs;
+      float acc = 0.0f;
+      for (int rr = r; rr < n; ++rr) acc = fmaf(sT[rr * C + r], sdU[rr * VS + e], acc);
+      sdR[r * VS + e] = acc;
+    }
+    __syncthreads();
+    // dP += dO U^T (lower), dA -= dR U^T (strictly lower): each element has one owner
+    for (int i = tid; i < C * C; i += kThreads) {
+      const int r = i / C, j = i - r * C;
+      if (r < n && j <= r) {
+        float p = 0.0f, a = 0.0f;
+        for (int e = 0; e < vs; ++e) {
+          p = fmaf(sdo[r * VS + e], sU[j * VS + e], p);
+          a = fmaf(sdR[r * VS + e], sU[j * VS + e], a);
+        }
+        sdP[i] += p;
+        if (j < r) sdA[i] -= a;
+      }
+    }
+    // dQ += diag(gam) dO S;  dK += diag(D) U dS' - diag(beta gam) dR S
+#pragma unroll
+    for (int jj = 0; jj < kQPT; ++jj) {
+      const int i = tid + jj * kThreads;
+      const int r = i / K, j = i - r * K;
+      if (r < n) {
+        float zq = 0.0f, zu = 0.0f, zr = 0.0f;
+        for (int e = 0; e < vs; ++e) {
+          const float s = sS[e * K + j];
+          zq = fmaf(sdo[r * VS + e], s, zq);
+          zu = fmaf(sU[r * VS + e], sdS[e * K + j], zu);
+          zr = fmaf(sdR[r * VS + e], s, zr);
+        }
+        aq[jj] = fmaf(sgam[r], zq, aq[jj]);
+        ak[jj] = fmaf(expf(glast - sg[r]), zu, ak[jj]);
+        ak[jj] = fmaf(-sb[r] * sgam[r], zr, ak[jj]);
+      }
+    }
+    // dV = diag(beta) dR
+    for (int i = tid; i < n * vs; i += kThreads) {
+      const int r = i / vs, e = i - r * vs;
+      dv[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e] = from_f32<TIn>(sb[r] * sdR[r * VS + e]);
+    }
+    // per-token sums over this slice
+    if (tid < n) {
+      const int r = tid;
+      float db = 0.0f, oz = 0.0f, ry = 0.0f, uw = 0.0f;
+      for (int e = 0; e < vs; ++e) {
+        const float y = sY[r * VS + e], dr = sdR[r * VS + e];
+        db = fmaf(dr, sv[r * VS + e] - sgam[r] * y, db);
+        oz = fmaf(sdo[r * VS + e], sZ[r * VS + e], oz);
+        ry = fmaf(dr, y, ry);
+        uw = fmaf(sU[r * VS + e], sW[r * VS + e], uw);
+      }
+      const float du = expf(glast - sg[r]) * uw;
+      sdb[r] += db;
+      sdg[r] += sgam[r] * oz - sb[r] * sgam[r] * ry - du;
+      esum += du;
+    }
+  }
+  __syncthreads();
+  // (dP o E) and beta (dA o E) in place, dg and dbeta terms of P and A
+  if (tid < n) {
+    const int r = tid;
+    float s = 0.0f, db = 0.0f;
+    for (int i = 0; i <= r; ++i) s = fmaf(sdP[r * C + i], sP[r * C + i], s);
+    for (int rr = r; rr < n; ++rr) s = fmaf(-sdP[rr * C + r], sP[rr * C + r], s);
+    for (int i = 0; i < r; ++i) {
+      s = fmaf(sdA[r * C + i], sb[r] * sM[r * C + i], s);
+      db = fmaf(sdA[r * C + i], sM[r * C + i], db);
+    }
+    for (int rr = r + 1; rr < n; ++rr) s = fmaf(-sdA[rr * C + r], sb[rr] * sM[rr * C + r], s);
+    sdg[r] += s;
+    sdb[r] += db;
+  }
+  // reduction of the <dS', S> and esum partials (fixed order)
+  sred[tid] = fmaf(gam_last, sdot, esum);
+  __syncthreads();
+  for (int i = tid; i < C * C; i += kThreads) {
+    const int r = i / C, j = i - r * C;
+    if (r < n && j <= r) {
+      const float e = expf(sg[r] - sg[j]);
+      sdP[i] *= e;
+      sdA[i] *= sb[r] * e;
+    }
+  }
+  for (int st = kThreads / 2; st > 0; st >>= 1) {
+    if (tid < st) sred[tid] += sred[tid + st];
+    __syncthreads();
+  }
+  // dQ += (dP o E) K;  dK += (dP o E)^T Q + (dA o bE) K + (dA o bE)^T K
+#pragma unroll
+  for (int jj = 0; jj < kQPT; ++jj) {
+    const int i = tid + jj * kThreads;
+    const int r = i / K, j = i - r * K;
+    if (r < n) {
+      float zq = 0.0f, zk = 0.0f;
+      for (int ii = 0; ii <= r; ++ii) zq = fmaf(sdP[r * C + ii], sk[ii * K + j], zq);
+      for (int rr = r; rr < n; ++rr) zk = fmaf(sdP[rr * C + r], sq[rr * K + j], zk);
+      for (int ii = 0; ii < r; ++ii) zk = fmaf(sdA[r * C + ii], sk[ii * K + j], zk);
+      for (int rr = r + 1; rr < n; ++rr) zk = fmaf(sdA[rr * C + r], sk[rr * K + j], zk);
+      const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + j;
+      dq[off] = from_f32<TIn>(aq[jj] + zq);
+      dk[off] = from_f32<TIn>(ak[jj] + zk);
+    }
+  }
+  if (tid == 0) {
+    sdg[n - 1] += sred[0];
+    float acc = 0.0f;  // d ln alpha_t = sum_{r >= t} dg_r
+    for (int r = n - 1; r >= 0; --r) {
+      acc += sdg[r];
+      const size_t go = ((size_t)b * T + t0 + r) * H + h;
+      dalpha[go] = acc / alpha[go];
+      dbeta[go] = sdb[r];
+    }
+  }
+}
+
+template <typename TIn>
+hipError_t set_lds_limit(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+}
+
+template <typename TIn>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  const int C = a.chunk < kBwdC ? a.chunk : kBwdC;
+  const int NT = (a.T + C - 1) / C;
+  float* ws_S = a.workspace;
+  float* ws_dS = ws_S + (size_t)a.B * a.H * NT * a.V * a.K;
+  hipError_t e;
+
+  // (1) chunk-start states
+  FwdArgs f;
+  f.q = a.q;
+  f.k = a.k;
+  f.v = a.v;
+  f.alpha = a.alpha;
+  f.beta = a.beta;
+  f.s0 = a.s0;
+  f.o = nullptr;
+  f.s_final = nullptr;
+  f.B = a.B;
+  f.T = a.T;
+  f.H = a.H;
+  f.K = a.K;
+  f.V = a.V;
+  f.chunk = C;
+  e = launch_fwd_states(f, sizeof(TIn) == 2, ws_S, stream);
+  if (e != hipSuccess) return e;
+
+  // (2) reverse walk
+  {
+    const int VS = a.V < 32 ? a.V : 32;
+    const size_t lds = sizeof(float) * (size_t)(2 * C * a.K + C * VS + 3 * C * C + 2 * C * VS +
+                                                VS * a.K + 3 * C);
+    if ((e = set_lds_limit<TIn>((const void*)bwd_dstate_kernel<TIn>)) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dstate_kernel<TIn>, dim3(a.V / VS, a.H, a.B), dim3(kThreads), lds, stream,
+                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                       static_cast<const TIn*>(a.d_o), a.alpha, a.beta, a.d_sfinal, a.d_s0, ws_dS,
+                       a.T, a.H, a.K, a.V, C, VS);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // (3) token gradients
+  {
+    const size_t lds = sizeof(float) * (size_t)(2 * C * a.K + 5 * C * C + 8 * C * kBwdVS +
+                                                2 * kBwdVS * a.K + 5 * C + kThreads);
+    if ((e = set_lds_limit<TIn>((const void*)bwd_local_kernel<TIn>)) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_local_kernel<TIn>, dim3(NT, a.H, a.B), dim3(kThreads), lds, stream,
+                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                       static_cast<const TIn*>(a.v), static_cast<const TIn*>(a.d_o), a.alpha,
+                       a.beta, ws_S, ws_dS, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),
+                       static_cast<TIn*>(a.dv), a.dalpha, a.dbeta, a.T, a.H, a.K, a.V, C);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk) {
+  const int64_t C = chunk < kBwdC ? chunk : kBwdC;
+  const int64_t NT = (T + C - 1) / C;
+  return (size_t)(2 * B * H * NT * V * K) * sizeof(float);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_bwd_t<__hip_bfloat16>(a, stream) : launch_bwd_t<float>(a, stream);
+}
+
+}  // namespace gdn

@@ -415,7 +415,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
                 const float* __restrict__ s0, bf16* __restrict__ o, float* __restrict__ s_final,
                 int T, int H, int K, int V, int C, int nslice) {
   using SM = Smem<KD, VS, CP>;
-  constexpr int LDC = SM::LDC, LDA = SM::LDA;
+  constexpr int LDC = SM::LDC;
   constexpr int NTB = CP / 16;          // token blocks per chunk tile
   constexpr int NCB = KD / 16;          // key-channel blocks
   constexpr int KS = KD / 32;           // k-steps over key channels

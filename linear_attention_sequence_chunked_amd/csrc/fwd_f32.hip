@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(kThreads)
 fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                const float* __restrict__ alpha, const float* __restrict__ beta,
                const float* __restrict__ s0, TIn* __restrict__ o, float* __restrict__ s_final,
-               int T, int H, int K, int V, int C, int VS) {
+               float* __restrict__ s_ckpt, int T, int H, int K, int V, int C, int VS) {
   extern __shared__ float lds[];
   float* sq = lds;                 // [C][K]
   float* sk = sq + C * K;          // [C][K]
@@ -66,6 +66,11 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
   for (int t0 = 0; t0 < T; t0 += C) {
     const int n = min(C, T - t0);
     __syncthreads();  // previous chunk finished with the tiles
+    if (s_ckpt) {  // chunk-start state, [B, H, NT, V, K]
+      const int NT = (T + C - 1) / C;
+      float* dst = s_ckpt + ((((size_t)b * H + h) * NT + t0 / C) * V + v0) * (size_t)K;
+      for (int i = tid; i < VS * K; i += kThreads) dst[i] = sS[i];
+    }
     for (int i = tid; i < n * K; i += kThreads) {
       const int r = i / K, c = i - r * K;
       const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + c;
@@ -128,7 +133,7 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
     }
     __syncthreads();
     // P (lower incl. diagonal) overwrites A; U = Tm R goes to sv (values no longer needed).
-    for (int i = tid; i < n * n; i += kThreads) {
+    for (int i = tid; o && i < n * n; i += kThreads) {
       const int r = i / n, j = i - r * n;
       float val = 0.0f;
       if (j <= r) {
@@ -145,8 +150,8 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
       sv[r * VS + c] = u;
     }
     __syncthreads();
-    // O = Z + P U, stored.
-    for (int i = tid; i < n * VS; i += kThreads) {
+    // O = Z + P U, stored (skipped when only the states are wanted).
+    for (int i = tid; o && i < n * VS; i += kThreads) {
       const int r = i / VS, c = i - r * VS;
       float acc = sU[r * VS + c];
       for (int j = 0; j <= r; ++j) acc = fmaf(sA[r * C + j], sv[j * VS + c], acc);
@@ -168,7 +173,7 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
 }
 
 template <typename TIn>
-hipError_t launch_scalar(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_scalar(const FwdArgs& a, float* s_ckpt, hipStream_t stream) {
   const int VS = a.V < 16 ? a.V : 16;
   const int C = a.chunk;
   const size_t lds = sizeof(float) * (size_t)(2 * C * a.K + C * VS + 2 * C * C + 2 * C * VS +
@@ -184,14 +189,18 @@ hipError_t launch_scalar(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(fwd_f32_kernel<TIn>, grid, dim3(kThreads), lds, stream,
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                      static_cast<const TIn*>(a.v), a.alpha, a.beta, a.s0,
-                     static_cast<TIn*>(a.o), a.s_final, a.T, a.H, a.K, a.V, C, VS);
+                     static_cast<TIn*>(a.o), a.s_final, s_ckpt, a.T, a.H, a.K, a.V, C, VS);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
-  return launch_scalar<float>(a, stream);
+  return launch_scalar<float>(a, nullptr, stream);
+}
+
+hipError_t launch_fwd_states(const FwdArgs& a, bool bf16, float* s_ckpt, hipStream_t stream) {
+  return bf16 ? launch_scalar<__hip_bfloat16>(a, s_ckpt, stream) : launch_scalar<float>(a, s_ckpt, stream);
 }
 
 

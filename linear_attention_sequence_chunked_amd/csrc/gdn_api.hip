@@ -24,6 +24,21 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool width_supported(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// Shape checks shared by the entry points: INVALID_VALUE for non-positive sizes,
+// NOT_SUPPORTED outside the compiled set, SUCCESS otherwise.
+gdn_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk,
+                         gdn_dtype_t dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_ERROR_INVALID_VALUE;
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERROR_NOT_SUPPORTED;
+  if (!width_supported(K) || !width_supported(V)) return GDN_ERROR_NOT_SUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
+  const int64_t maxd = K > V ? K : V;
+  if (B > (INT64_C(1) << 31) || T > (INT64_C(1) << 31) || H > (INT64_C(1) << 31) ||
+      B * T > (INT64_C(1) << 31) || B * T * H * maxd >= (INT64_C(1) << 31))
+    return GDN_ERROR_NOT_SUPPORTED;
+  return GDN_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -100,6 +115,75 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
   a.chunk = static_cast<int>(chunk);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = dtype == GDN_DTYPE_F32 ? gdn::launch_fwd_f32(a, s) : gdn::launch_fwd_bf16(a, s);
+  return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
+}
+
+size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                    int64_t chunk) {
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0) return 0;
+  return gdn::bwd_workspace_bytes(B, T, H, K, V, chunk);
+}
+
+gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* initial_state, const void* d_o,
+                           const float* d_final_state, void* dq, void* dk, void* dv,
+                           float* dalpha, float* dbeta, float* d_initial_state, void* workspace,
+                           size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t K,
+                           int64_t V, int64_t chunk, gdn_dtype_t dtype, void* stream) {
+  if (!q || !k || !v || !alpha || !beta || !d_o || !dq || !dk || !dv || !dalpha || !dbeta ||
+      !workspace)
+    return GDN_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {q, k, v, alpha, beta, initial_state, d_o, d_final_state, dq, dk, dv,
+                        dalpha, dbeta, d_initial_state, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
+  const gdn_status_t st = check_shape(B, T, H, K, V, chunk, dtype);
+  if (st != GDN_SUCCESS) return st;
+  if (workspace_bytes < gdn::bwd_workspace_bytes(B, T, H, K, V, chunk)) return GDN_ERROR_INVALID_VALUE;
+
+  const int64_t esz = dtype == GDN_DTYPE_F32 ? 4 : 2;
+  const int64_t nk = B * T * H * K, nv = B * T * H * V, ng = B * T * H, ns = B * H * V * K;
+  const Range in[] = {range_of(q, nk * esz), range_of(k, nk * esz), range_of(v, nv * esz),
+                      range_of(alpha, ng * 4), range_of(beta, ng * 4),
+                      initial_state ? range_of(initial_state, ns * 4) : Range{0, 0},
+                      range_of(d_o, nv * esz),
+                      d_final_state ? range_of(d_final_state, ns * 4) : Range{0, 0}};
+  const Range out[] = {range_of(dq, nk * esz), range_of(dk, nk * esz), range_of(dv, nv * esz),
+                       range_of(dalpha, ng * 4), range_of(dbeta, ng * 4),
+                       d_initial_state ? range_of(d_initial_state, ns * 4) : Range{0, 0},
+                       range_of(workspace, (int64_t)workspace_bytes)};
+  const int nin = sizeof(in) / sizeof(in[0]), nout = sizeof(out) / sizeof(out[0]);
+  for (int i = 0; i < nout; ++i) {
+    if (out[i].hi == out[i].lo) continue;
+    for (int j = 0; j < nin; ++j)
+      if (in[j].hi != in[j].lo && overlaps(out[i], in[j])) return GDN_ERROR_INVALID_VALUE;
+    for (int j = i + 1; j < nout; ++j)
+      if (out[j].hi != out[j].lo && overlaps(out[i], out[j])) return GDN_ERROR_INVALID_VALUE;
+  }
+
+  gdn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.s0 = initial_state;
+  a.d_o = d_o;
+  a.d_sfinal = d_final_state;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dalpha = dalpha;
+  a.dbeta = dbeta;
+  a.d_s0 = d_initial_state;
+  a.workspace = static_cast<float*>(workspace);
+  a.B = static_cast<int>(B);
+  a.T = static_cast<int>(T);
+  a.H = static_cast<int>(H);
+  a.K = static_cast<int>(K);
+  a.V = static_cast<int>(V);
+  a.chunk = static_cast<int>(chunk);
+  hipError_t err = gdn::launch_bwd(a, dtype == GDN_DTYPE_BF16, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
 }
 

@@ -23,6 +23,32 @@ struct FwdArgs {
 // Float32 q/k/v/o: scalar fp32 kernel (exact fp32 products and sums).
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
+// Chunk-start states only (o may be null): the scalar fp32-arithmetic kernel for
+// either dtype, writing the state at every chunk start to s_ckpt [B,H,NT,V,K].
+hipError_t launch_fwd_states(const FwdArgs& a, bool bf16, float* s_ckpt, hipStream_t stream);
+
+// One backward problem, already validated by the C-ABI layer.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* s0;        // may be null (zeros)
+  const void* d_o;
+  const float* d_sfinal;  // may be null (zeros)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dalpha;
+  float* dbeta;
+  float* d_s0;            // may be null (skip)
+  float* workspace;       // bwd_workspace_bytes(...) bytes
+  int B, T, H, K, V, chunk;
+};
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk);
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
+
 // Bfloat16 q/k/v/o: bf16 MFMA kernel with fp32 accumulation and fp32 state.
 // Returns hipErrorInvalidValue for a shape outside its compiled set.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

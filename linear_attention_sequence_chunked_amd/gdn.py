@@ -36,6 +36,8 @@ SIGNATURES = {
     "gdn_abi_version": (ctypes.c_int, []),
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_chunk_fwd": (ctypes.c_int, [_VP] * 8 + [_I64] * 6 + [ctypes.c_int, _VP]),
+    "gdn_chunk_bwd_workspace_size": (ctypes.c_size_t, [_I64] * 6),
+    "gdn_chunk_bwd": (ctypes.c_int, [_VP] * 15 + [ctypes.c_size_t] + [_I64] * 6 + [ctypes.c_int, _VP]),
 }
 
 _lib = None
@@ -138,3 +140,62 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, *,
                                ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_chunk_fwd")
     return out, final_state
+
+
+def bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, chunk: int = 64) -> int:
+    """Bytes of device workspace ``gdn_chunk_bwd`` needs for these sizes."""
+    return int(load_library().gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk))
+
+
+def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
+              chunk: int = 64, *, want_d_initial_state: bool = True, workspace=None,
+              stream=None):
+    """Reverse mode of :func:`chunk_fwd` through ``gdn_chunk_bwd`` for the loss
+    ``<o, d_o> + <final_state, d_final_state>``.
+
+    Returns ``(dq, dk, dv, dalpha, dbeta, d_initial_state)``; the last is None
+    when ``want_d_initial_state`` is False.  ``workspace`` may be a preallocated
+    uint8 device tensor of at least :func:`bwd_workspace_size` bytes.
+    """
+    lib = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B,T,H,K]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    if q.dtype not in _DTYPES:
+        raise NotImplementedError("dtype %s is not supported (float32 or bfloat16)" % q.dtype)
+    B, T, H, K = q.shape
+    if v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B,T,H,V]")
+    V = v.shape[-1]
+    _check(q, "q", (B, T, H, K), q.dtype, dev)
+    _check(k, "k", (B, T, H, K), q.dtype, dev)
+    _check(v, "v", (B, T, H, V), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check(d_o, "d_o", (B, T, H, V), q.dtype, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, V, K), torch.float32, dev)
+    if d_final_state is not None:
+        _check(d_final_state, "d_final_state", (B, H, V, K), torch.float32, dev)
+    need = lib.gdn_chunk_bwd_workspace_size(B, T, H, K, V, int(chunk))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dalpha = torch.empty_like(alpha)
+    dbeta = torch.empty_like(beta)
+    d_s0 = torch.empty((B, H, V, K), dtype=torch.float32, device=dev) if want_d_initial_state else None
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(dbeta), _ptr(d_s0),
+                               _ptr(workspace), workspace.numel(), B, T, H, K, V, int(chunk),
+                               _DTYPES[q.dtype], ctypes.c_void_p(s.cuda_stream))
+    _raise_for(rc, "gdn_chunk_bwd")
+    return dq, dk, dv, dalpha, dbeta, d_s0

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = gdn.load_library()
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     for code in range(4):
         assert len(gdn.status_string(code)) > 0
     assert gdn.status_string(99) == "unknown status"
@@ -97,3 +97,45 @@ def test_binding_rejects_cpu_tensors():
     g = torch.zeros(1, 4, 1)
     with pytest.raises(ValueError):
         gdn.chunk_fwd(x, x, x, g, g)
+
+
+def call_bwd(B=2, T=100, H=3, K=64, V=64, chunk=64, dtype=gdn.GDN_DTYPE_BF16, ws_bytes=None,
+             null=None, misalign=None, ptr=None):
+    """gdn_chunk_bwd on fake addresses: every case here must fail host validation."""
+    lib = gdn.load_library()
+    names = ["q", "k", "v", "a", "b", "s0", "do", "dsf", "dq", "dk", "dv", "da", "db", "ds0", "ws"]
+    args = []
+    for i, name in enumerate(names):
+        if name == null:
+            args.append(None)
+        elif ptr and name in ptr:
+            args.append(ptr[name])
+        else:
+            args.append(addr(i, 2 if misalign == name else 0))
+    need = lib.gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk)
+    return lib.gdn_chunk_bwd(*args, need if ws_bytes is None else ws_bytes, B, T, H, K, V, chunk,
+                             dtype, None)
+
+
+def test_bwd_workspace_size():
+    lib = gdn.load_library()
+    # two fp32 [V,K] states per (b, h, 32-token chunk)
+    assert lib.gdn_chunk_bwd_workspace_size(2, 100, 3, 64, 32, 64) == 2 * 2 * 3 * 4 * 32 * 64 * 4
+    assert lib.gdn_chunk_bwd_workspace_size(1, 17, 1, 16, 16, 16) == 2 * 2 * 16 * 16 * 4
+    assert lib.gdn_chunk_bwd_workspace_size(0, 17, 1, 16, 16, 16) == 0
+
+
+def test_bwd_rejects_bad_arguments():
+    for name in ("q", "k", "v", "a", "b", "do", "dq", "dk", "dv", "da", "db", "ws"):
+        assert call_bwd(null=name) == gdn.GDN_ERROR_INVALID_VALUE, name
+    for name in ("q", "dq", "ws", "ds0"):
+        assert call_bwd(misalign=name) == gdn.GDN_ERROR_INVALID_VALUE, name
+    assert call_bwd(ws_bytes=1024) == gdn.GDN_ERROR_INVALID_VALUE
+    assert call_bwd(T=0) == gdn.GDN_ERROR_INVALID_VALUE
+    assert call_bwd(K=48) == gdn.GDN_ERROR_NOT_SUPPORTED
+    assert call_bwd(chunk=128) == gdn.GDN_ERROR_NOT_SUPPORTED
+    assert call_bwd(dtype=5) == gdn.GDN_ERROR_NOT_SUPPORTED
+    # dk overlapping dq, workspace overlapping d_o, dv overlapping v
+    assert call_bwd(ptr={"dk": ctypes.c_void_p(BASE + 8 * STEP + 64)}) == gdn.GDN_ERROR_INVALID_VALUE
+    assert call_bwd(ptr={"ws": ctypes.c_void_p(BASE + 6 * STEP)}) == gdn.GDN_ERROR_INVALID_VALUE
+    assert call_bwd(ptr={"dv": ctypes.c_void_p(BASE + 2 * STEP + 128)}) == gdn.GDN_ERROR_INVALID_VALUE
