@@ -92,6 +92,78 @@ def algorithmic_flops(B, T, H, K, V, C):
     return per * B * T * H
 
 
+def backward_flops(B, T, H, K, V, C):
+    """Structural fp32 FLOPs per call of the backward as built (backward chunk C):
+    per token-head 22KV + 8CV + 9CK + C^2 (state recompute 4KV + CV + CK; reverse
+    state-gradient walk 6KV + 2CV + 2CK; token gradients 12KV + 5CV + 6CK; three
+    triangular solves)."""
+    return (22 * K * V + 8 * C * V + 9 * C * K + C * C) * B * T * H
+
+
+def bench_backward(args):
+    """One step = one gdn_chunk_bwd call (state recompute, reverse walk, token
+    gradients) on the forward+backward workload, inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    from linear_attention_sequence_chunked_amd import bwd_workspace_size, chunk_bwd
+    from linear_attention_sequence_chunked_amd.workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS["fwdbwd_bf16"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, T, H, K, V, C = w.B, w.T, w.H, w.K, w.V, w.chunk
+    cpu = workload_inputs(w)
+    g = {n: (t.to(dev) if t is not None else None) for n, t in cpu.items()}
+    ws = torch.empty(bwd_workspace_size(B, T, H, K, V, C), dtype=torch.uint8, device=dev)
+
+    def step():
+        return chunk_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["d_o"],
+                         g["initial_state"], chunk=C, workspace=ws)
+
+    gate = None
+    if not args.no_gate:
+        import oracle
+        got = step()
+        torch.cuda.synchronize()
+        ref = oracle.bwd(cpu["q"], cpu["k"], cpu["v"], cpu["alpha"], cpu["beta"], cpu["d_o"])
+        names = ("dq", "dk", "dv", "dalpha", "dbeta", "d_initial_state")
+        gate = {n: float(np.linalg.norm(x.double().cpu().numpy() - ref[n]) / np.linalg.norm(ref[n]))
+                for n, x in zip(names, got)}
+        if not all(e <= 2e-2 for e in gate.values()):
+            print("correctness gate failed: %s" % json.dumps(gate), file=sys.stderr)
+            sys.exit(1)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    bwd_c = min(C, 32)
+    flops = backward_flops(B, T, H, K, V, bwd_c)
+    tok = B * T * H
+    abytes = tok * (4 * K * 2 + 3 * K * 2 + 2 * 4 + 2 * 4) + B * H * V * K * 4  # q,k,v,dO,gates in; dq,dk,dv,dgates out; dS0
+    print(json.dumps({
+        "metric": "GDN chunk bwd tokens/s at B4\u00b7T2048\u00b7H6\u00b7d128",
+        "value": B * T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in/out, f32 arithmetic", "data": "synthetic",
+        "config": {"workload": "%s: B=%d T=%d H=%d K=%d V=%d chunk=%d (backward chunk %d)"
+                               % (w.name, B, T, H, K, V, C, bwd_c)},
+        "roofline": {"bound": "alu", "achieved": flops / (ms / 1e3) / 1e12, "peak": 157.3,
+                     "unit": "TFLOP/s", "frac": flops / (ms / 1e3) / 1e12 / 157.3,
+                     "traffic": None, "algorithmic_flops": flops,
+                     "hbm_gbs_algorithmic": abytes / (ms / 1e3) / 1e9},
+        "gate": gate,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,9 +174,17 @@ def main():
     ap.add_argument("--workload", default="train_bf16")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the known-size copy used to calibrate HBM counters")
+    ap.add_argument("--backward", action="store_true",
+                    help="time gdn_chunk_bwd on the forward+backward workload instead")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.backward:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only; run with --gpus 1", file=sys.stderr)
+            sys.exit(2)
+        bench_backward(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the (batch, head) streams are independent, so "

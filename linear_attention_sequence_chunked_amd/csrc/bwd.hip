@@ -25,9 +25,10 @@
 //   dg_last += gam_last <dS', S> + sum_r D_r U_r.W_r
 //   d ln alpha_t = sum_{r >= t} dg_r,   dalpha_t = d ln alpha_t / alpha_t
 //
-// Three launches: (1) the scalar forward recomputes the chunk-start states into
-// the workspace; (2) a reverse walk over the chunks carries dS and stores each
-// chunk's dS'; (3) every chunk computes its token gradients independently.
+// Three launches: (1) the forward kernel of the input dtype recomputes the
+// chunk-start states into the workspace; (2) a reverse walk over the chunks
+// carries dS and stores each chunk's dS'; (3) every chunk computes its token
+// gradients independently.
 // All arithmetic is fp32 in a fixed order (bitwise reproducible); inputs and the
 // dq, dk, dv outputs have the dtype of q.  The backward chunk is at most 32
 // tokens (chunk size changes results only by rounding).
@@ -73,18 +74,20 @@ __device__ __forceinline__ void load_gates(const float* alpha, const float* beta
 
 // M (strictly lower, decayed K K^T, no beta), P (lower, decayed Q K^T) and
 // Tm = (I + diag(beta) M)^-1 by forward substitution (one column per thread).
-// Leading dimension C.  Leaves a barrier behind.
+// Key/query rows have leading dimension LK (K + 1: threads reading different
+// rows hit different banks); the C x C results have leading dimension C.
+// Leaves a barrier behind.
 __device__ __forceinline__ void chunk_mats(const float* sq, const float* sk, const float* sg,
                                            const float* sb, float* sM, float* sP, float* sT,
-                                           int n, int C, int K, int tid) {
+                                           int n, int C, int K, int LK, int tid) {
   for (int i = tid; i < C * C; i += kThreads) {
     const int r = i / C, j = i - r * C;
     float m = 0.0f, p = 0.0f;
     if (r < n && j <= r) {
       float dk = 0.0f, dq = 0.0f;
       for (int c = 0; c < K; ++c) {
-        dk = fmaf(sk[r * K + c], sk[j * K + c], dk);
-        dq = fmaf(sq[r * K + c], sk[j * K + c], dq);
+        dk = fmaf(sk[r * LK + c], sk[j * LK + c], dk);
+        dq = fmaf(sq[r * LK + c], sk[j * LK + c], dq);
       }
       const float e = expf(sg[r] - sg[j]);
       if (j < r) m = e * dk;
@@ -118,16 +121,17 @@ bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                   const float* __restrict__ d_sfinal, float* __restrict__ d_s0,
                   float* __restrict__ ws_dS, int T, int H, int K, int V, int C, int VS) {
   extern __shared__ float lds[];
-  float* sq = lds;                 // [C][K]
-  float* sk = sq + C * K;          // [C][K]
-  float* sdo = sk + C * K;         // [C][VS]
-  float* sM = sdo + C * VS;        // [C][C]
+  const int LK = K + 1, LV = VS + 1;  // padded rows: no bank conflicts across rows
+  float* sq = lds;                 // [C][LK]
+  float* sk = sq + C * LK;         // [C][LK]
+  float* sdo = sk + C * LK;        // [C][LV]
+  float* sM = sdo + C * LV;        // [C][C]
   float* sP = sM + C * C;          // [C][C]
   float* sT = sP + C * C;          // [C][C]
-  float* sdU = sT + C * C;         // [C][VS]
-  float* sdR = sdU + C * VS;       // [C][VS]
-  float* sdS = sdR + C * VS;       // [VS][K]
-  float* sg = sdS + VS * K;        // [C]
+  float* sdU = sT + C * C;         // [C][LV]
+  float* sdR = sdU + C * LV;       // [C][LV]
+  float* sdS = sdR + C * LV;       // [VS][LK]
+  float* sg = sdS + VS * LK;       // [C]
   float* sgam = sg + C;
   float* sb = sgam + C;
 
@@ -138,60 +142,61 @@ bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
   const int NT = (T + C - 1) / C;
   const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
 
-  for (int i = tid; i < VS * K; i += kThreads) sdS[i] = d_sfinal ? d_sfinal[state_base + i] : 0.0f;
+  for (int i = tid; i < VS * K; i += kThreads)
+    sdS[(i / K) * LK + i % K] = d_sfinal ? d_sfinal[state_base + i] : 0.0f;
 
   for (int c = NT - 1; c >= 0; --c) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
     __syncthreads();
     float* dst = ws_dS + ((((size_t)b * H + h) * NT + c) * V + v0) * (size_t)K;
-    for (int i = tid; i < VS * K; i += kThreads) dst[i] = sdS[i];
+    for (int i = tid; i < VS * K; i += kThreads) dst[i] = sdS[(i / K) * LK + i % K];
     for (int i = tid; i < n * K; i += kThreads) {
       const int r = i / K, e = i - r * K;
       const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + e;
-      sq[i] = to_f32(q[off]);
-      sk[i] = to_f32(k[off]);
+      sq[r * LK + e] = to_f32(q[off]);
+      sk[r * LK + e] = to_f32(k[off]);
     }
     for (int i = tid; i < n * VS; i += kThreads) {
       const int r = i / VS, e = i - r * VS;
-      sdo[i] = to_f32(d_o[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e]);
+      sdo[r * LV + e] = to_f32(d_o[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e]);
     }
     load_gates(alpha, beta, sg, sgam, sb, b, h, T, H, t0, n, tid);
-    chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, tid);
+    chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, LK, tid);
     const float glast = sg[n - 1];
     // dU = diag(D) K dS'^T + P^T dO
     for (int i = tid; i < n * VS; i += kThreads) {
       const int r = i / VS, e = i - r * VS;
       float w = 0.0f;
-      for (int j = 0; j < K; ++j) w = fmaf(sk[r * K + j], sdS[e * K + j], w);
+      for (int j = 0; j < K; ++j) w = fmaf(sk[r * LK + j], sdS[e * LK + j], w);
       float acc = expf(glast - sg[r]) * w;
-      for (int rr = r; rr < n; ++rr) acc = fmaf(sP[rr * C + r], sdo[rr * VS + e], acc);
-      sdU[i] = acc;
+      for (int rr = r; rr < n; ++rr) acc = fmaf(sP[rr * C + r], sdo[rr * LV + e], acc);
+      sdU[r * LV + e] = acc;
     }
     __syncthreads();
     // dR = Tm^T dU
     for (int i = tid; i < n * VS; i += kThreads) {
       const int r = i / VS, e = i - r * VS;
       float acc = 0.0f;
-      for (int rr = r; rr < n; ++rr) acc = fmaf(sT[rr * C + r], sdU[rr * VS + e], acc);
-      sdR[i] = acc;
+      for (int rr = r; rr < n; ++rr) acc = fmaf(sT[rr * C + r], sdU[rr * LV + e], acc);
+      sdR[r * LV + e] = acc;
     }
     __syncthreads();
     // dS <- gam_last dS + dO^T diag(gam) Q - dR^T diag(beta gam) K
     const float gam_last = sgam[n - 1];
     for (int i = tid; i < VS * K; i += kThreads) {
       const int e = i / K, j = i - e * K;
-      float acc = gam_last * sdS[i];
+      float acc = gam_last * sdS[e * LK + j];
       for (int r = 0; r < n; ++r) {
-        acc = fmaf(sgam[r] * sdo[r * VS + e], sq[r * K + j], acc);
-        acc = fmaf(-sb[r] * sgam[r] * sdR[r * VS + e], sk[r * K + j], acc);
+        acc = fmaf(sgam[r] * sdo[r * LV + e], sq[r * LK + j], acc);
+        acc = fmaf(-sb[r] * sgam[r] * sdR[r * LV + e], sk[r * LK + j], acc);
       }
-      sdS[i] = acc;
+      sdS[e * LK + j] = acc;
     }
   }
   __syncthreads();
   if (d_s0)
-    for (int i = tid; i < VS * K; i += kThreads) d_s0[state_base + i] = sdS[i];
+    for (int i = tid; i < VS * K; i += kThreads) d_s0[state_base + i] = sdS[(i / K) * LK + i % K];
 }
 
 // ---------------------------------------------------------------------------
@@ -211,25 +216,27 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
                  TIn* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta,
                  int T, int H, int K, int V, int C) {
   constexpr int VS = kBwdVS;
+  const int LK = K + 1;            // padded rows: no bank conflicts across rows
+  constexpr int LV = VS + 1;
   extern __shared__ float lds[];
-  float* sq = lds;                 // [C][K]
-  float* sk = sq + C * K;          // [C][K]
-  float* sM = sk + C * K;          // [C][C]
+  float* sq = lds;                 // [C][LK]
+  float* sk = sq + C * LK;         // [C][LK]
+  float* sM = sk + C * LK;         // [C][C]
   float* sP = sM + C * C;
   float* sT = sP + C * C;
   float* sdP = sT + C * C;
   float* sdA = sdP + C * C;
-  float* sv = sdA + C * C;         // [C][VS] slices
-  float* sdo = sv + C * VS;
-  float* sY = sdo + C * VS;
-  float* sZ = sY + C * VS;
-  float* sW = sZ + C * VS;
-  float* sU = sW + C * VS;         // R, then U
-  float* sdU = sU + C * VS;
-  float* sdR = sdU + C * VS;
-  float* sS = sdR + C * VS;        // [VS][K]
-  float* sdS = sS + VS * K;        // [VS][K]
-  float* sg = sdS + VS * K;        // [C]
+  float* sv = sdA + C * C;         // [C][LV] slices
+  float* sdo = sv + C * LV;
+  float* sY = sdo + C * LV;
+  float* sZ = sY + C * LV;
+  float* sW = sZ + C * LV;
+  float* sU = sW + C * LV;         // R, then U
+  float* sdU = sU + C * LV;
+  float* sdR = sdU + C * LV;
+  float* sS = sdR + C * LV;        // [VS][LK]
+  float* sdS = sS + VS * LK;       // [VS][LK]
+  float* sg = sdS + VS * LK;       // [C]
   float* sgam = sg + C;
   float* sb = sgam + C;
   float* sdb = sb + C;             // dbeta accumulator
@@ -248,8 +255,8 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   for (int i = tid; i < n * K; i += kThreads) {
     const int r = i / K, e = i - r * K;
     const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + e;
-    sq[i] = to_f32(q[off]);
-    sk[i] = to_f32(k[off]);
+    sq[r * LK + e] = to_f32(q[off]);
+    sk[r * LK + e] = to_f32(k[off]);
   }
   if (tid < C) {
     sdb[tid] = 0.0f;
@@ -260,7 +267,7 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     sdA[i] = 0.0f;
   }
   load_gates(alpha, beta, sg, sgam, sb, b, h, T, H, t0, n, tid);
-  chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, tid);
+  chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, LK, tid);
   const float glast = sg[n - 1];
   const float gam_last = sgam[n - 1];
 
@@ -275,12 +282,13 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     for (int i = tid; i < n * vs; i += kThreads) {
       const int r = i / vs, e = i - r * vs;
       const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e;
-      sv[r * VS + e] = to_f32(v[off]);
-      sdo[r * VS + e] = to_f32(d_o[off]);
+      sv[r * LV + e] = to_f32(v[off]);
+      sdo[r * LV + e] = to_f32(d_o[off]);
     }
     for (int i = tid; i < vs * K; i += kThreads) {
-      sS[i] = ws_S[ck + (size_t)v0 * K + i];
-      sdS[i] = ws_dS[ck + (size_t)v0 * K + i];
+      const int e = i / K, j = i - e * K;
+      sS[e * LK + j] = ws_S[ck + (size_t)v0 * K + i];
+      sdS[e * LK + j] = ws_dS[ck + (size_t)v0 * K + i];
     }
     __syncthreads();
     // Y = K S^T, Z = Q S^T, W = K dS'^T;  R = diag(beta) V - diag(beta gam) Y
@@ -288,40 +296,43 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
       const int r = i / vs, e = i - r * vs;
       float y = 0.0f, z = 0.0f, w = 0.0f;
       for (int j = 0; j < K; ++j) {
-        const float kk = sk[r * K + j];
-        y = fmaf(kk, sS[e * K + j], y);
-        z = fmaf(sq[r * K + j], sS[e * K + j], z);
-        w = fmaf(kk, sdS[e * K + j], w);
+        const float kk = sk[r * LK + j];
+        y = fmaf(kk, sS[e * LK + j], y);
+        z = fmaf(sq[r * LK + j], sS[e * LK + j], z);
+        w = fmaf(kk, sdS[e * LK + j], w);
       }
-      sY[r * VS + e] = y;
-      sZ[r * VS + e] = z;
-      sW[r * VS + e] = w;
-      sdR[r * VS + e] = sb[r] * sv[r * VS + e] - sb[r] * sgam[r] * y;  // R (temporary)
+      sY[r * LV + e] = y;
+      sZ[r * LV + e] = z;
+      sW[r * LV + e] = w;
+      sdR[r * LV + e] = sb[r] * sv[r * LV + e] - sb[r] * sgam[r] * y;  // R (temporary)
     }
     __syncthreads();
     // U = Tm R;  <dS', S> partials
     for (int i = tid; i < n * vs; i += kThreads) {
       const int r = i / vs, e = i - r * vs;
       float u = 0.0f;
-      for (int j = 0; j <= r; ++j) u = fmaf(sT[r * C + j], sdR[j * VS + e], u);
-      sU[r * VS + e] = u;
+      for (int j = 0; j <= r; ++j) u = fmaf(sT[r * C + j], sdR[j * LV + e], u);
+      sU[r * LV + e] = u;
     }
-    for (int i = tid; i < vs * K; i += kThreads) sdot = fmaf(sdS[i], sS[i], sdot);
+    for (int i = tid; i < vs * K; i += kThreads) {
+      const int e = i / K, j = i - e * K;
+      sdot = fmaf(sdS[e * LK + j], sS[e * LK + j], sdot);
+    }
     __syncthreads();
     // dU = diag(D) W + P^T dO
     for (int i = tid; i < n * vs; i += kThreads) {
       const int r = i / vs, e = i - r * vs;
-      float acc = expf(glast - sg[r]) * sW[r * VS + e];
-      for (int rr = r; rr < n; ++rr) acc = fmaf(sP[rr * C + r], sdo[rr * VS + e], acc);
-      sdU[r * VS + e] = acc;
+      float acc = expf(glast - sg[r]) * sW[r * LV + e];
+      for (int rr = r; rr < n; ++rr) acc = fmaf(sP[rr * C + r], sdo[rr * LV + e], acc);
+      sdU[r * LV + e] = acc;
     }
     __syncthreads();
     // dR = Tm^T dU
     for (int i = tid; i < n * vs; i += kThreads) {
       const int r = i / vs, e = i - r * vs;
       float acc = 0.0f;
-      for (int rr = r; rr < n; ++rr) acc = fmaf(sT[rr * C + r], sdU[rr * VS + e], acc);
-      sdR[r * VS + e] = acc;
+      for (int rr = r; rr < n; ++rr) acc = fmaf(sT[rr * C + r], sdU[rr * LV + e], acc);
+      sdR[r * LV + e] = acc;
     }
     __syncthreads();
     // dP += dO U^T (lower), dA -= dR U^T (strictly lower): each element has one owner
@@ -330,8 +341,8 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
       if (r < n && j <= r) {
         float p = 0.0f, a = 0.0f;
         for (int e = 0; e < vs; ++e) {
-          p = fmaf(sdo[r * VS + e], sU[j * VS + e], p);
-          a = fmaf(sdR[r * VS + e], sU[j * VS + e], a);
+          p = fmaf(sdo[r * LV + e], sU[j * LV + e], p);
+          a = fmaf(sdR[r * LV + e], sU[j * LV + e], a);
         }
         sdP[i] += p;
         if (j < r) sdA[i] -= a;
@@ -345,10 +356,10 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
       if (r < n) {
         float zq = 0.0f, zu = 0.0f, zr = 0.0f;
         for (int e = 0; e < vs; ++e) {
-          const float s = sS[e * K + j];
-          zq = fmaf(sdo[r * VS + e], s, zq);
-          zu = fmaf(sU[r * VS + e], sdS[e * K + j], zu);
-          zr = fmaf(sdR[r * VS + e], s, zr);
+          const float s = sS[e * LK + j];
+          zq = fmaf(sdo[r * LV + e], s, zq);
+          zu = fmaf(sU[r * LV + e], sdS[e * LK + j], zu);
+          zr = fmaf(sdR[r * LV + e], s, zr);
         }
         aq[jj] = fmaf(sgam[r], zq, aq[jj]);
         ak[jj] = fmaf(expf(glast - sg[r]), zu, ak[jj]);
@@ -358,18 +369,18 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     // dV = diag(beta) dR
     for (int i = tid; i < n * vs; i += kThreads) {
       const int r = i / vs, e = i - r * vs;
-      dv[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e] = from_f32<TIn>(sb[r] * sdR[r * VS + e]);
+      dv[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e] = from_f32<TIn>(sb[r] * sdR[r * LV + e]);
     }
     // per-token sums over this slice
     if (tid < n) {
       const int r = tid;
       float db = 0.0f, oz = 0.0f, ry = 0.0f, uw = 0.0f;
       for (int e = 0; e < vs; ++e) {
-        const float y = sY[r * VS + e], dr = sdR[r * VS + e];
-        db = fmaf(dr, sv[r * VS + e] - sgam[r] * y, db);
-        oz = fmaf(sdo[r * VS + e], sZ[r * VS + e], oz);
+        const float y = sY[r * LV + e], dr = sdR[r * LV + e];
+        db = fmaf(dr, sv[r * LV + e] - sgam[r] * y, db);
+        oz = fmaf(sdo[r * LV + e], sZ[r * LV + e], oz);
         ry = fmaf(dr, y, ry);
-        uw = fmaf(sU[r * VS + e], sW[r * VS + e], uw);
+        uw = fmaf(sU[r * LV + e], sW[r * LV + e], uw);
       }
       const float du = expf(glast - sg[r]) * uw;
       sdb[r] += db;
@@ -414,10 +425,10 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     const int r = i / K, j = i - r * K;
     if (r < n) {
       float zq = 0.0f, zk = 0.0f;
-      for (int ii = 0; ii <= r; ++ii) zq = fmaf(sdP[r * C + ii], sk[ii * K + j], zq);
-      for (int rr = r; rr < n; ++rr) zk = fmaf(sdP[rr * C + r], sq[rr * K + j], zk);
-      for (int ii = 0; ii < r; ++ii) zk = fmaf(sdA[r * C + ii], sk[ii * K + j], zk);
-      for (int rr = r + 1; rr < n; ++rr) zk = fmaf(sdA[rr * C + r], sk[rr * K + j], zk);
+      for (int ii = 0; ii <= r; ++ii) zq = fmaf(sdP[r * C + ii], sk[ii * LK + j], zq);
+      for (int rr = r; rr < n; ++rr) zk = fmaf(sdP[rr * C + r], sq[rr * LK + j], zk);
+      for (int ii = 0; ii < r; ++ii) zk = fmaf(sdA[r * C + ii], sk[ii * LK + j], zk);
+      for (int rr = r + 1; rr < n; ++rr) zk = fmaf(sdA[rr * C + r], sk[rr * LK + j], zk);
       const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + j;
       dq[off] = from_f32<TIn>(aq[jj] + zq);
       dk[off] = from_f32<TIn>(ak[jj] + zk);
@@ -470,8 +481,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   // (2) reverse walk
   {
     const int VS = a.V < 32 ? a.V : 32;
-    const size_t lds = sizeof(float) * (size_t)(2 * C * a.K + C * VS + 3 * C * C + 2 * C * VS +
-                                                VS * a.K + 3 * C);
+    const size_t LK = a.K + 1, LV = VS + 1;
+    const size_t lds = sizeof(float) * (2 * C * LK + C * LV + 3 * C * C + 2 * C * LV + VS * LK + 3 * C);
     if ((e = set_lds_limit<TIn>((const void*)bwd_dstate_kernel<TIn>)) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dstate_kernel<TIn>, dim3(a.V / VS, a.H, a.B), dim3(kThreads), lds, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
@@ -481,8 +492,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   }
   // (3) token gradients
   {
-    const size_t lds = sizeof(float) * (size_t)(2 * C * a.K + 5 * C * C + 8 * C * kBwdVS +
-                                                2 * kBwdVS * a.K + 5 * C + kThreads);
+    const size_t LK = a.K + 1, LV = kBwdVS + 1;
+    const size_t lds = sizeof(float) * (2 * C * LK + 5 * C * C + 8 * C * LV + 2 * kBwdVS * LK + 5 * C + kThreads);
     if ((e = set_lds_limit<TIn>((const void*)bwd_local_kernel<TIn>)) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_local_kernel<TIn>, dim3(NT, a.H, a.B), dim3(kThreads), lds, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),

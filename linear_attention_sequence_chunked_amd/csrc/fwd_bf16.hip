@@ -413,7 +413,7 @@ __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_e
 fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const float* __restrict__ alpha, const float* __restrict__ beta,
                 const float* __restrict__ s0, bf16* __restrict__ o, float* __restrict__ s_final,
-                int T, int H, int K, int V, int C, int nslice) {
+                float* __restrict__ s_ckpt, int T, int H, int K, int V, int C, int nslice) {
   using SM = Smem<KD, VS, CP>;
   constexpr int LDC = SM::LDC;
   constexpr int NTB = CP / 16;          // token blocks per chunk tile
@@ -575,6 +575,12 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     for (int i = 0; i < 4; ++i) lds_barrier();
     for (int x = 0; x < NT; ++x) {
       lds_barrier();
+      if (s_ckpt) {  // chunk-start state [B, H, NT, V, K] (for the backward)
+        float* dst = s_ckpt + ((((size_t)b * H + h) * NT + x) * V + v0 + 16 * vb + ls) * (size_t)K + 4 * lg;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          if (16 * cb < K) *reinterpret_cast<f32x4*>(dst + 16 * cb) = S[cb];
+      }
       const int gs = x % 3;
       constexpr int LDK = KD + 8;
       const lbf16* kr = pin(lds(sm.k[gs]) + rows_lane(LDK, lane));      // K rows
@@ -687,6 +693,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       const int t0 = x * C;
       const int n = min(C, T - t0);
       bf16* obase = o + ((size_t)b * T + t0) * tok_v + (size_t)h * V + v0 + 16 * vb + 4 * lg;
+      if (o)  // no output when only states are wanted
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         f32x4 O = Z[tb];
@@ -803,7 +810,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP>), dim3(nblk), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                      static_cast<const bf16*>(a.v), a.alpha, a.beta, a.s0,
-                     static_cast<bf16*>(a.o), a.s_final, a.T, a.H, a.K, a.V, a.chunk, nslice);
+                     static_cast<bf16*>(a.o), a.s_final, a.s_ckpt, a.T, a.H, a.K, a.V, a.chunk, nslice);
   return hipGetLastError();
 }
 

@@ -21,7 +21,6 @@
 // order, so the result is bitwise reproducible.
 #include "launch.h"
 
-#include <hip/hip_bf16.h>
 
 namespace gdn {
 namespace {
@@ -29,12 +28,8 @@ namespace {
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
-template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(float x) {
-  return __float2bfloat16(x);  // round to nearest even
-}
 
 template <typename TIn>
 __global__ void __launch_bounds__(kThreads)
@@ -43,15 +38,16 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
                const float* __restrict__ s0, TIn* __restrict__ o, float* __restrict__ s_final,
                float* __restrict__ s_ckpt, int T, int H, int K, int V, int C, int VS) {
   extern __shared__ float lds[];
-  float* sq = lds;                 // [C][K]
-  float* sk = sq + C * K;          // [C][K]
-  float* sv = sk + C * K;          // [C][VS]
+  const int LK = K + 1;            // padded rows: threads reading different rows use different banks
+  float* sq = lds;                 // [C][LK]
+  float* sk = sq + C * LK;         // [C][LK]
+  float* sv = sk + C * LK;         // [C][VS]
   float* sA = sv + C * VS;         // [C][C]  A, later P
   float* sT = sA + C * C;          // [C][C]
   float* sR = sT + C * C;          // [C][VS] R, later Z = diag(gam) Q S^T
   float* sU = sR + C * VS;         // [C][VS]
-  float* sS = sU + C * VS;         // [VS][K] state slice
-  float* sg = sS + VS * K;         // [C] cumulative log gate
+  float* sS = sU + C * VS;         // [VS][LK] state slice
+  float* sg = sS + VS * LK;        // [C] cumulative log gate
   float* sgam = sg + C;            // [C] exp(g)
   float* sb = sgam + C;            // [C] beta
 
@@ -61,7 +57,7 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
   const int b = blockIdx.z;
   const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
 
-  for (int i = tid; i < VS * K; i += kThreads) sS[i] = s0 ? s0[state_base + i] : 0.0f;
+  for (int i = tid; i < VS * K; i += kThreads) sS[(i / K) * LK + i % K] = s0 ? s0[state_base + i] : 0.0f;
 
   for (int t0 = 0; t0 < T; t0 += C) {
     const int n = min(C, T - t0);
@@ -69,13 +65,13 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
     if (s_ckpt) {  // chunk-start state, [B, H, NT, V, K]
       const int NT = (T + C - 1) / C;
       float* dst = s_ckpt + ((((size_t)b * H + h) * NT + t0 / C) * V + v0) * (size_t)K;
-      for (int i = tid; i < VS * K; i += kThreads) dst[i] = sS[i];
+      for (int i = tid; i < VS * K; i += kThreads) dst[i] = sS[(i / K) * LK + i % K];
     }
     for (int i = tid; i < n * K; i += kThreads) {
       const int r = i / K, c = i - r * K;
       const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + c;
-      sq[i] = to_f32(q[off]);
-      sk[i] = to_f32(k[off]);
+      sq[r * LK + c] = to_f32(q[off]);
+      sk[r * LK + c] = to_f32(k[off]);
     }
     for (int i = tid; i < n * VS; i += kThreads) {
       const int r = i / VS, c = i - r * VS;
@@ -102,7 +98,7 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
       float val = 0.0f;
       if (j < r) {
         float d = 0.0f;
-        for (int c = 0; c < K; ++c) d = fmaf(sk[r * K + c], sk[j * K + c], d);
+        for (int c = 0; c < K; ++c) d = fmaf(sk[r * LK + c], sk[j * LK + c], d);
         val = sb[r] * expf(sg[r] - sg[j]) * d;
       }
       sA[r * C + j] = val;
@@ -113,9 +109,9 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
       const int r = i / VS, c = i - r * VS;
       float dk = 0.0f, dq = 0.0f;
       for (int e = 0; e < K; ++e) {
-        const float s = sS[c * K + e];
-        dk = fmaf(sk[r * K + e], s, dk);
-        dq = fmaf(sq[r * K + e], s, dq);
+        const float s = sS[c * LK + e];
+        dk = fmaf(sk[r * LK + e], s, dk);
+        dq = fmaf(sq[r * LK + e], s, dq);
       }
       sR[r * VS + c] = sb[r] * sv[r * VS + c] - sb[r] * sgam[r] * dk;
       sU[r * VS + c] = sgam[r] * dq;
@@ -138,7 +134,7 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
       float val = 0.0f;
       if (j <= r) {
         float d = 0.0f;
-        for (int c = 0; c < K; ++c) d = fmaf(sq[r * K + c], sk[j * K + c], d);
+        for (int c = 0; c < K; ++c) d = fmaf(sq[r * LK + c], sk[j * LK + c], d);
         val = expf(sg[r] - sg[j]) * d;
       }
       sA[r * C + j] = val;
@@ -162,22 +158,22 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
     const float gam_n = sgam[n - 1];
     for (int i = tid; i < VS * K; i += kThreads) {
       const int c = i / K, e = i - c * K;
-      float acc = gam_n * sS[i];
-      for (int j = 0; j < n; ++j) acc = fmaf(sv[j * VS + c] * expf(gn - sg[j]), sk[j * K + e], acc);
-      sS[i] = acc;
+      float acc = gam_n * sS[c * LK + e];
+      for (int j = 0; j < n; ++j) acc = fmaf(sv[j * VS + c] * expf(gn - sg[j]), sk[j * LK + e], acc);
+      sS[c * LK + e] = acc;
     }
   }
   __syncthreads();
   if (s_final)
-    for (int i = tid; i < VS * K; i += kThreads) s_final[state_base + i] = sS[i];
+    for (int i = tid; i < VS * K; i += kThreads) s_final[state_base + i] = sS[(i / K) * LK + i % K];
 }
 
 template <typename TIn>
 hipError_t launch_scalar(const FwdArgs& a, float* s_ckpt, hipStream_t stream) {
   const int VS = a.V < 16 ? a.V : 16;
   const int C = a.chunk;
-  const size_t lds = sizeof(float) * (size_t)(2 * C * a.K + C * VS + 2 * C * C + 2 * C * VS +
-                                              VS * a.K + 3 * C);
+  const size_t LK = a.K + 1;
+  const size_t lds = sizeof(float) * (2 * C * LK + C * VS + 2 * C * C + 2 * C * VS + VS * LK + 3 * C);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)fwd_f32_kernel<TIn>,
@@ -200,7 +196,10 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_states(const FwdArgs& a, bool bf16, float* s_ckpt, hipStream_t stream) {
-  return bf16 ? launch_scalar<__hip_bfloat16>(a, s_ckpt, stream) : launch_scalar<float>(a, s_ckpt, stream);
+  if (!bf16) return launch_scalar<float>(a, s_ckpt, stream);
+  FwdArgs b = a;
+  b.s_ckpt = s_ckpt;
+  return launch_fwd_bf16(b, stream);
 }
 
 

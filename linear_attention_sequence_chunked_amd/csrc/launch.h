@@ -18,13 +18,15 @@ struct FwdArgs {
   void* o;
   float* s_final;   // may be null (skip)
   int B, T, H, K, V, chunk;
+  float* s_ckpt = nullptr;  // optional chunk-start states [B, H, NT, V, K]
 };
 
 // Float32 q/k/v/o: scalar fp32 kernel (exact fp32 products and sums).
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
-// Chunk-start states only (o may be null): the scalar fp32-arithmetic kernel for
-// either dtype, writing the state at every chunk start to s_ckpt [B,H,NT,V,K].
+// Chunk-start states only (o null): the state at every chunk start to s_ckpt
+// [B,H,NT,V,K] -- the scalar fp32 kernel for float32 inputs, the MFMA kernel for
+// bfloat16 inputs.
 hipError_t launch_fwd_states(const FwdArgs& a, bool bf16, float* s_ckpt, hipStream_t stream);
 
 // One backward problem, already validated by the C-ABI layer.
