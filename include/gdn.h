@@ -109,10 +109,11 @@ GDN_API gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v,
 
 /*
  * gdn_chunk_bwd_workspace_size -- bytes of device workspace gdn_chunk_bwd needs
- * for these sizes: two float32 [V, K] states per (batch, head, backward chunk),
- * the backward chunk being min(chunk, 32) tokens, i.e.
- * 2 * B * H * ceil(T / min(chunk, 32)) * V * K * 4 bytes.  Returns 0 when a size
- * is not positive.
+ * for these sizes.  Per (batch, head, backward chunk of C = min(chunk, 32)
+ * tokens) it holds two float32 [V, K] states and the chunk's float32 factors
+ * (three C x C matrices and three C-vectors):
+ *     B * H * ceil(T / C) * (2 * V * K + 3 * C * C + 3 * C) * 4 bytes.
+ * Returns 0 when a size is not positive.
  */
 GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K,
                                             int64_t V, int64_t chunk);

@@ -25,10 +25,11 @@
 //   dg_last += gam_last <dS', S> + sum_r D_r U_r.W_r
 //   d ln alpha_t = sum_{r >= t} dg_r,   dalpha_t = d ln alpha_t / alpha_t
 //
-// Three launches: (1) the forward kernel of the input dtype recomputes the
-// chunk-start states into the workspace; (2) a reverse walk over the chunks
-// carries dS and stores each chunk's dS'; (3) every chunk computes its token
-// gradients independently.
+// Four launches: (1) the forward kernel of the input dtype recomputes the
+// chunk-start states into the workspace; (2a) every chunk builds its
+// state-independent factors M, P, Tm and gates in parallel; (2b) a reverse walk
+// over the chunks carries dS and stores each chunk's dS'; (3) every chunk
+// computes its token gradients independently.
 // All arithmetic is fp32 in a fixed order (bitwise reproducible); inputs and the
 // dq, dk, dv outputs have the dtype of q.  The backward chunk is at most 32
 // tokens (chunk size changes results only by rounding).
@@ -110,8 +111,77 @@ __device__ __forceinline__ void chunk_mats(const float* sq, const float* sk, con
   __syncthreads();
 }
 
+// Per-chunk factor record in the workspace: M, P, Tm (C x C each), then g, gam,
+// beta (C each).
+__host__ __device__ constexpr int factor_floats(int C) { return 3 * C * C + 3 * C; }
+
+// Copy a chunk's factor record into LDS (M skipped when sM is null).  Leaves a
+// barrier behind.
+__device__ __forceinline__ void load_factors(const float* f, float* sM, float* sP, float* sT,
+                                             float* sg, float* sgam, float* sb, int C, int tid) {
+  const int CC = C * C;
+  for (int i = tid; i < CC; i += kThreads) {
+    if (sM) sM[i] = f[i];
+    sP[i] = f[CC + i];
+    sT[i] = f[2 * CC + i];
+  }
+  if (tid < C) {
+    sg[tid] = f[3 * CC + tid];
+    sgam[tid] = f[3 * CC + C + tid];
+    sb[tid] = f[3 * CC + 2 * C + tid];
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
-// (2) Reverse walk: one workgroup per (batch, head, value slice of VS rows).
+// (2a) State-independent factors of every chunk, in parallel: one workgroup per
+// (chunk, head, batch).
+template <typename TIn>
+__global__ void __launch_bounds__(kThreads)
+bwd_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                const float* __restrict__ alpha, const float* __restrict__ beta,
+                float* __restrict__ ws_F, int T, int H, int K, int C) {
+  extern __shared__ float lds[];
+  const int LK = K + 1;
+  float* sq = lds;                 // [C][LK]
+  float* sk = sq + C * LK;         // [C][LK]
+  float* sM = sk + C * LK;         // [C][C]
+  float* sP = sM + C * C;
+  float* sT = sP + C * C;
+  float* sg = sT + C * C;          // [C]
+  float* sgam = sg + C;
+  float* sb = sgam + C;
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int NT = (T + C - 1) / C;
+  const int t0 = c * C;
+  const int n = min(C, T - t0);
+  for (int i = tid; i < n * K; i += kThreads) {
+    const int r = i / K, e = i - r * K;
+    const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + e;
+    sq[r * LK + e] = to_f32(q[off]);
+    sk[r * LK + e] = to_f32(k[off]);
+  }
+  load_gates(alpha, beta, sg, sgam, sb, b, h, T, H, t0, n, tid);
+  chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, LK, tid);
+  float* f = ws_F + (((size_t)b * H + h) * NT + c) * factor_floats(C);
+  const int CC = C * C;
+  for (int i = tid; i < CC; i += kThreads) {
+    const int r = i / C, j = i - r * C;
+    const bool in = r < n && j < n;  // rows and columns past the tail are zero
+    f[i] = sM[i];
+    f[CC + i] = sP[i];
+    f[2 * CC + i] = in ? sT[i] : 0.0f;
+  }
+  if (tid < C) {
+    f[3 * CC + tid] = tid < n ? sg[tid] : 0.0f;
+    f[3 * CC + C + tid] = tid < n ? sgam[tid] : 0.0f;
+    f[3 * CC + 2 * C + tid] = tid < n ? sb[tid] : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// (2b) Reverse walk: one workgroup per (batch, head, value slice of VS rows).
 // Stores dS' of every chunk to ws_dS [B, H, NT, V, K] and the gradient of the
 // initial state.
 template <typename TIn>
@@ -119,7 +189,8 @@ __global__ void __launch_bounds__(kThreads)
 bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ d_o,
                   const float* __restrict__ alpha, const float* __restrict__ beta,
                   const float* __restrict__ d_sfinal, float* __restrict__ d_s0,
-                  float* __restrict__ ws_dS, int T, int H, int K, int V, int C, int VS) {
+                  const float* __restrict__ ws_F, float* __restrict__ ws_dS, int T, int H, int K,
+                  int V, int C, int VS) {
   extern __shared__ float lds[];
   const int LK = K + 1, LV = VS + 1;  // padded rows: no bank conflicts across rows
   float* sq = lds;                 // [C][LK]
@@ -161,8 +232,8 @@ bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
       const int r = i / VS, e = i - r * VS;
       sdo[r * LV + e] = to_f32(d_o[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e]);
     }
-    load_gates(alpha, beta, sg, sgam, sb, b, h, T, H, t0, n, tid);
-    chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, LK, tid);
+    load_factors(ws_F + (((size_t)b * H + h) * NT + c) * factor_floats(C), nullptr, sP, sT, sg,
+                 sgam, sb, C, tid);
     const float glast = sg[n - 1];
     // dU = diag(D) K dS'^T + P^T dO
     for (int i = tid; i < n * VS; i += kThreads) {
@@ -212,7 +283,8 @@ __global__ void __launch_bounds__(kThreads)
 bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                  const TIn* __restrict__ d_o, const float* __restrict__ alpha,
                  const float* __restrict__ beta, const float* __restrict__ ws_S,
-                 const float* __restrict__ ws_dS, TIn* __restrict__ dq, TIn* __restrict__ dk,
+                 const float* __restrict__ ws_dS, const float* __restrict__ ws_F,
+                 TIn* __restrict__ dq, TIn* __restrict__ dk,
                  TIn* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta,
                  int T, int H, int K, int V, int C) {
   constexpr int VS = kBwdVS;
@@ -266,8 +338,8 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
     sdP[i] = 0.0f;
     sdA[i] = 0.0f;
   }
-  load_gates(alpha, beta, sg, sgam, sb, b, h, T, H, t0, n, tid);
-  chunk_mats(sq, sk, sg, sb, sM, sP, sT, n, C, K, LK, tid);
+  load_factors(ws_F + (((size_t)b * H + h) * NT + c) * factor_floats(C), sM, sP, sT, sg, sgam, sb,
+               C, tid);
   const float glast = sg[n - 1];
   const float gam_last = sgam[n - 1];
 
@@ -457,6 +529,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int NT = (a.T + C - 1) / C;
   float* ws_S = a.workspace;
   float* ws_dS = ws_S + (size_t)a.B * a.H * NT * a.V * a.K;
+  float* ws_F = ws_dS + (size_t)a.B * a.H * NT * a.V * a.K;
   hipError_t e;
 
   // (1) chunk-start states
@@ -478,16 +551,26 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   e = launch_fwd_states(f, sizeof(TIn) == 2, ws_S, stream);
   if (e != hipSuccess) return e;
 
-  // (2) reverse walk
+  // (2a) chunk factors
   {
-    const int VS = a.V < 32 ? a.V : 32;
+    const size_t LK = a.K + 1;
+    const size_t lds = sizeof(float) * (2 * C * LK + 3 * C * C + 3 * C);
+    if ((e = set_lds_limit<TIn>((const void*)bwd_prep_kernel<TIn>)) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_prep_kernel<TIn>, dim3(NT, a.H, a.B), dim3(kThreads), lds, stream,
+                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), a.alpha, a.beta,
+                       ws_F, a.T, a.H, a.K, C);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // (2b) reverse walk
+  {
+    const int VS = 16;
     const size_t LK = a.K + 1, LV = VS + 1;
     const size_t lds = sizeof(float) * (2 * C * LK + C * LV + 3 * C * C + 2 * C * LV + VS * LK + 3 * C);
     if ((e = set_lds_limit<TIn>((const void*)bwd_dstate_kernel<TIn>)) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dstate_kernel<TIn>, dim3(a.V / VS, a.H, a.B), dim3(kThreads), lds, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.d_o), a.alpha, a.beta, a.d_sfinal, a.d_s0, ws_dS,
-                       a.T, a.H, a.K, a.V, C, VS);
+                       static_cast<const TIn*>(a.d_o), a.alpha, a.beta, a.d_sfinal, a.d_s0, ws_F,
+                       ws_dS, a.T, a.H, a.K, a.V, C, VS);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // (3) token gradients
@@ -498,7 +581,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_local_kernel<TIn>, dim3(NT, a.H, a.B), dim3(kThreads), lds, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), static_cast<const TIn*>(a.d_o), a.alpha,
-                       a.beta, ws_S, ws_dS, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),
+                       a.beta, ws_S, ws_dS, ws_F, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),
                        static_cast<TIn*>(a.dv), a.dalpha, a.dbeta, a.T, a.H, a.K, a.V, C);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -510,7 +593,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk) {
   const int64_t C = chunk < kBwdC ? chunk : kBwdC;
   const int64_t NT = (T + C - 1) / C;
-  return (size_t)(2 * B * H * NT * V * K) * sizeof(float);
+  return (size_t)(2 * B * H * NT * V * K + B * H * NT * factor_floats((int)C)) * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {

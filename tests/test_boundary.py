@@ -119,9 +119,11 @@ def call_bwd(B=2, T=100, H=3, K=64, V=64, chunk=64, dtype=gdn.GDN_DTYPE_BF16, ws
 
 def test_bwd_workspace_size():
     lib = gdn.load_library()
-    # two fp32 [V,K] states per (b, h, 32-token chunk)
-    assert lib.gdn_chunk_bwd_workspace_size(2, 100, 3, 64, 32, 64) == 2 * 2 * 3 * 4 * 32 * 64 * 4
-    assert lib.gdn_chunk_bwd_workspace_size(1, 17, 1, 16, 16, 16) == 2 * 2 * 16 * 16 * 4
+    # per (b, h, chunk of min(chunk, 32) tokens): two fp32 [V,K] states, 3 CxC + 3 C factors
+    assert lib.gdn_chunk_bwd_workspace_size(2, 100, 3, 64, 32, 64) == \
+        2 * 3 * 4 * (2 * 32 * 64 + 3 * 32 * 32 + 3 * 32) * 4
+    assert lib.gdn_chunk_bwd_workspace_size(1, 17, 1, 16, 16, 16) == \
+        2 * (2 * 16 * 16 + 3 * 16 * 16 + 3 * 16) * 4
     assert lib.gdn_chunk_bwd_workspace_size(0, 17, 1, 16, 16, 16) == 0
 
 
