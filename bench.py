@@ -164,6 +164,76 @@ def bench_backward(args):
     }), flush=True)
 
 
+def bench_decode(args):
+    """One step = one gdn_decode_step call (one token for 64 streams x 16 heads,
+    K = V = 128).  Five state buffers (5 x 64 MiB) rotate so the Infinity Cache
+    cannot hold the state between steps; the state is read and written once per
+    step, so the bound is HBM."""
+    import numpy as np
+    import torch
+
+    from linear_attention_sequence_chunked_amd import decode_step
+    from linear_attention_sequence_chunked_amd.workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS["decode_bf16"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, K, V = w.B, w.H, w.K, w.V
+    cpu = workload_inputs(w)
+    g = {n: (t[:, 0].contiguous().to(dev) if t is not None and n != "initial_state" else None)
+         for n, t in cpu.items()}
+    nsets = 5
+    states = [cpu["initial_state"].to(dev) for _ in range(nsets)]
+    out = torch.empty(B, H, V, dtype=w.dtype, device=dev)
+
+    def step(i):
+        decode_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], states[i % nsets], out=out)
+
+    gate = None
+    if not args.no_gate:
+        import oracle
+        step(0)
+        torch.cuda.synchronize()
+        ro, rs = oracle.fwd(cpu["q"], cpu["k"], cpu["v"], cpu["alpha"], cpu["beta"],
+                            cpu["initial_state"])
+        gate = {"rel_l2_o": float(np.linalg.norm(out.double().cpu().numpy() - ro[:, 0]) / np.linalg.norm(ro)),
+                "rel_l2_state": float(np.linalg.norm(states[0].double().cpu().numpy() - rs) / np.linalg.norm(rs))}
+        if not (gate["rel_l2_o"] <= 2e-2 and gate["rel_l2_state"] <= 1e-5):
+            print("correctness gate failed: %s" % json.dumps(gate), file=sys.stderr)
+            sys.exit(1)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = t0.elapsed_time(t1) / args.steps
+    abytes = B * H * (2 * V * K * 4 + (2 * K + 2 * V) * 2 + 8)
+    gbs = abytes / (kern_ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "GDN decode step tokens/s at B64\u00b7H16\u00b7d128",
+        "value": B / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in/out, f32 state", "data": "synthetic",
+        "config": {"workload": "%s: B=%d H=%d K=%d V=%d, one token per call, 5 rotating states"
+                               % (w.name, B, H, K, V)},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel_ms": kern_ms,
+                     "algorithmic_bytes": abytes},
+        "gate": gate,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,9 +246,17 @@ def main():
                     help="only run the known-size copy used to calibrate HBM counters")
     ap.add_argument("--backward", action="store_true",
                     help="time gdn_chunk_bwd on the forward+backward workload instead")
+    ap.add_argument("--decode", action="store_true",
+                    help="time gdn_decode_step on the decode workload instead")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.decode:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only; run with --gpus 1", file=sys.stderr)
+            sys.exit(2)
+        bench_decode(args)
         return
     if args.backward:
         if args.gpus != 1:

@@ -1,6 +1,6 @@
 /*
- * gdn.h -- C ABI of the chunkwise gated-delta-rule forward and backward for
- * AMD Instinct MI355X (gfx950).
+ * gdn.h -- C ABI of the chunkwise gated-delta-rule forward and backward, and
+ * of its single-token decode step, for AMD Instinct MI355X (gfx950).
  *
  * The operation.  For every batch b and head h, with state S of shape [V, K]:
  *
@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -106,6 +106,30 @@ GDN_API gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v,
                            void *o, float *final_state,
                            int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                            int64_t chunk, gdn_dtype_t dtype, void *stream);
+
+/*
+ * gdn_decode_step -- one token of the recurrence for every (batch, head), the
+ * state advanced in place (the decode path of "Sparse Delta Memory: layer and
+ * kernels", sections "What the layer computes" and "Execution"):
+ *
+ *     S <- alpha S (I - beta k k^T) + beta v k^T;   o = S q
+ *
+ *   q, k       [B,H,K] dtype     this token's query and key (read only)
+ *   v          [B,H,V] dtype     this token's value (read only)
+ *   alpha, beta [B,H]  float32   gates (read only)
+ *   state      [B,H,V,K] float32 read and overwritten with the new state
+ *   o          [B,H,V] dtype     output (written)
+ *   K, V       16, 32, 64 or 128 each
+ *
+ * Equal, up to float32 rounding, to gdn_chunk_fwd with T = 1 and
+ * final_state == initial_state == state.  Arithmetic is float32 in a fixed order
+ * (bitwise reproducible).  No buffer may overlap another.  Errors as for
+ * gdn_chunk_fwd.
+ */
+GDN_API gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta, float *state,
+                             void *o, int64_t B, int64_t H, int64_t K, int64_t V,
+                             gdn_dtype_t dtype, void *stream);
 
 /*
  * gdn_chunk_bwd_workspace_size -- bytes of device workspace gdn_chunk_bwd needs

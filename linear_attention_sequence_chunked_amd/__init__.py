@@ -1,8 +1,10 @@
-"""Chunkwise gated-delta rule (forward and backward) for AMD Instinct MI355X (gfx950).
+"""Chunkwise gated-delta rule (forward, backward, decode step) for AMD Instinct MI355X (gfx950).
 
 The computation lives in hand-written HIP kernels behind the C ABI of
 ``include/gdn.h`` (``libgdn.so``); :mod:`.gdn` is the thin ctypes binding.
 """
-from .gdn import bwd_workspace_size, chunk_bwd, chunk_fwd, load_library, status_string  # noqa: F401
+from .gdn import (bwd_workspace_size, chunk_bwd, chunk_fwd, decode_step,  # noqa: F401
+                  load_library, status_string)
 
-__all__ = ["chunk_fwd", "chunk_bwd", "bwd_workspace_size", "load_library", "status_string"]
+__all__ = ["chunk_fwd", "chunk_bwd", "bwd_workspace_size", "decode_step", "load_library",
+           "status_string"]

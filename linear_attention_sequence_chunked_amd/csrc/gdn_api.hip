@@ -118,6 +118,40 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
   return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
 }
 
+gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, float* state, void* o, int64_t B, int64_t H,
+                             int64_t K, int64_t V, gdn_dtype_t dtype, void* stream) {
+  if (!q || !k || !v || !alpha || !beta || !state || !o) return GDN_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {q, k, v, alpha, beta, state, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GDN_ERROR_INVALID_VALUE;
+  const gdn_status_t st = check_shape(B, 1, H, K, V, 16, dtype);
+  if (st != GDN_SUCCESS) return st;
+  if (B * H >= (INT64_C(1) << 31) / (K > V ? K : V)) return GDN_ERROR_NOT_SUPPORTED;
+  const int64_t esz = dtype == GDN_DTYPE_F32 ? 4 : 2;
+  const Range in[] = {range_of(q, B * H * K * esz), range_of(k, B * H * K * esz),
+                      range_of(v, B * H * V * esz), range_of(alpha, B * H * 4),
+                      range_of(beta, B * H * 4)};
+  const Range rs = range_of(state, B * H * V * K * 4), ro = range_of(o, B * H * V * esz);
+  for (const Range& r : in)
+    if (overlaps(rs, r) || overlaps(ro, r)) return GDN_ERROR_INVALID_VALUE;
+  if (overlaps(rs, ro)) return GDN_ERROR_INVALID_VALUE;
+  gdn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.B = static_cast<int>(B);
+  a.H = static_cast<int>(H);
+  a.K = static_cast<int>(K);
+  a.V = static_cast<int>(V);
+  hipError_t err = gdn::launch_decode(a, dtype == GDN_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
+}
+
 size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                     int64_t chunk) {
   if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0) return 0;

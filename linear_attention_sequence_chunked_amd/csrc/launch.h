@@ -51,6 +51,19 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 
+// One decode step (T = 1), already validated by the C-ABI layer.
+struct DecodeArgs {
+  const void* q;      // [B, H, K]
+  const void* k;      // [B, H, K]
+  const void* v;      // [B, H, V]
+  const float* alpha; // [B, H]
+  const float* beta;  // [B, H]
+  float* state;       // [B, H, V, K], updated in place
+  void* o;            // [B, H, V]
+  int B, H, K, V;
+};
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+
 // Bfloat16 q/k/v/o: bf16 MFMA kernel with fp32 accumulation and fp32 state.
 // Returns hipErrorInvalidValue for a shape outside its compiled set.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

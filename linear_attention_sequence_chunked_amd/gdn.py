@@ -36,6 +36,7 @@ SIGNATURES = {
     "gdn_abi_version": (ctypes.c_int, []),
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_chunk_fwd": (ctypes.c_int, [_VP] * 8 + [_I64] * 6 + [ctypes.c_int, _VP]),
+    "gdn_decode_step": (ctypes.c_int, [_VP] * 7 + [_I64] * 4 + [ctypes.c_int, _VP]),
     "gdn_chunk_bwd_workspace_size": (ctypes.c_size_t, [_I64] * 6),
     "gdn_chunk_bwd": (ctypes.c_int, [_VP] * 15 + [ctypes.c_size_t] + [_I64] * 6 + [ctypes.c_int, _VP]),
 }
@@ -199,3 +200,37 @@ def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
                                _DTYPES[q.dtype], ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_chunk_bwd")
     return dq, dk, dv, dalpha, dbeta, d_s0
+
+
+def decode_step(q, k, v, alpha, beta, state, *, out=None, stream=None):
+    """One token through ``gdn_decode_step``: ``state`` [B,H,V,K] float32 is
+    advanced in place and ``o`` [B,H,V] is returned.  q, k [B,H,K], v [B,H,V] in
+    float32 or bfloat16, alpha and beta [B,H] float32."""
+    lib = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [B,H,K]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    if q.dtype not in _DTYPES:
+        raise NotImplementedError("dtype %s is not supported (float32 or bfloat16)" % q.dtype)
+    B, H, K = q.shape
+    if v.dim() != 3:
+        raise ValueError("v must be a 3-D tensor [B,H,V]")
+    V = v.shape[-1]
+    _check(k, "k", (B, H, K), q.dtype, dev)
+    _check(v, "v", (B, H, V), q.dtype, dev)
+    _check(alpha, "alpha", (B, H), torch.float32, dev)
+    _check(beta, "beta", (B, H), torch.float32, dev)
+    _check(state, "state", (B, H, V, K), torch.float32, dev)
+    _check(q, "q", (B, H, K), q.dtype, dev)
+    if out is None:
+        out = torch.empty((B, H, V), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", (B, H, V), q.dtype, dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+                                 _ptr(out), B, H, K, V, _DTYPES[q.dtype], ctypes.c_void_p(s.cuda_stream))
+    _raise_for(rc, "gdn_decode_step")
+    return out

@@ -42,7 +42,8 @@ class Workload:
     note: str = field(default="", compare=False)
 
 
-# The five workloads.  Seeds equal the workload number.
+# The five workloads of the operator (seeds equal the workload number), plus a decode
+# batch (seed 6).
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", 1, 64, 2, 16, 16, 16, torch.float32, "sigmoid", seed=1,
                           note="tiny fp32, B1 T64 H2 K=V=16, chunk 16"),
@@ -53,6 +54,10 @@ WORKLOADS = {
     "fwdbwd_bf16": Workload("fwdbwd_bf16", 4, 2048, 6, 128, 128, 64, torch.bfloat16, "decay",
                             with_do=True, seed=4,
                             note="forward+backward shape, B4 T2048 H6 K=V=128, chunk 64"),
+    "decode_bf16": Workload("decode_bf16", 64, 1, 16, 128, 128, 64, torch.bfloat16, "decay",
+                            s0_std=0.02, seed=6,
+                            note="decode step, 64 streams x 16 heads, K=V=128, one token per "
+                                 "call, S0 ~ 0.02 N(0,1)"),
     "long_bf16": Workload("long_bf16", 1, 32768, 16, 128, 128, 64, torch.bfloat16, "decay",
                           s0_std=0.02, split_at=16384, seed=5,
                           note="long-context streaming prefill, B1 T32768 H16 K=V=128, "

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = gdn.load_library()
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     for code in range(4):
         assert len(gdn.status_string(code)) > 0
     assert gdn.status_string(99) == "unknown status"
@@ -141,3 +141,26 @@ def test_bwd_rejects_bad_arguments():
     assert call_bwd(ptr={"dk": ctypes.c_void_p(BASE + 8 * STEP + 64)}) == gdn.GDN_ERROR_INVALID_VALUE
     assert call_bwd(ptr={"ws": ctypes.c_void_p(BASE + 6 * STEP)}) == gdn.GDN_ERROR_INVALID_VALUE
     assert call_bwd(ptr={"dv": ctypes.c_void_p(BASE + 2 * STEP + 128)}) == gdn.GDN_ERROR_INVALID_VALUE
+
+
+def test_decode_rejects_bad_arguments():
+    lib = gdn.load_library()
+
+    def dcall(null=None, misalign=None, K=64, V=64, dtype=gdn.GDN_DTYPE_BF16, same=None):
+        ptrs = []
+        for i, name in enumerate(["q", "k", "v", "a", "b", "s", "o"]):
+            if name == null:
+                ptrs.append(None)
+            elif same and name == same[1]:
+                ptrs.append(addr(["q", "k", "v", "a", "b", "s", "o"].index(same[0])))
+            else:
+                ptrs.append(addr(i, 2 if name == misalign else 0))
+        return lib.gdn_decode_step(*ptrs, 2, 3, K, V, dtype, None)
+
+    for name in ("q", "k", "v", "a", "b", "s", "o"):
+        assert dcall(null=name) == gdn.GDN_ERROR_INVALID_VALUE, name
+        assert dcall(misalign=name) == gdn.GDN_ERROR_INVALID_VALUE, name
+    assert dcall(K=48) == gdn.GDN_ERROR_NOT_SUPPORTED
+    assert dcall(dtype=3) == gdn.GDN_ERROR_NOT_SUPPORTED
+    assert dcall(same=("s", "o")) == gdn.GDN_ERROR_INVALID_VALUE      # o aliases the state
+    assert dcall(same=("q", "s")) == gdn.GDN_ERROR_INVALID_VALUE      # state aliases q
