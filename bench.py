@@ -234,6 +234,82 @@ def bench_decode(args):
     }), flush=True)
 
 
+def varlen_lengths(n=24, lo=128, hi=8192, seed=7):
+    """Seeded ragged length mix: n lengths log-uniform in [lo, hi]."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in np.exp(rng.uniform(np.log(lo), np.log(hi), n))]
+
+
+def bench_varlen(args):
+    """One step = one gdn_chunk_fwd_varlen call over a packed batch of 24 sequences
+    (lengths log-uniform in [128, 8192], seeded), H = 6, K = V = 128, bf16, chunk 64.
+    The call's time is set by the longest sequence (each (sequence, head, value
+    slice) is one workgroup walking its chunks in order)."""
+    import numpy as np
+    import torch
+
+    from linear_attention_sequence_chunked_amd import chunk_fwd_varlen
+    from linear_attention_sequence_chunked_amd.workloads import make_inputs
+
+    lengths = varlen_lengths()
+    N, T, H, K, V, C = len(lengths), int(sum(lengths)), 6, 128, 128, 64
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(1, T, H, K, V, dtype=torch.bfloat16, seed=8, gate="decay")
+    g = {n: (t.to(dev) if t is not None else None) for n, t in inp.items()}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=dev)
+    out = torch.empty(1, T, H, V, dtype=torch.bfloat16, device=dev)
+    sf = torch.empty(N, H, V, K, dtype=torch.float32, device=dev)
+
+    def step():
+        chunk_fwd_varlen(g["q"], g["k"], g["v"], g["alpha"], g["beta"], cu, None, chunk=C,
+                         out=out, final_state=sf)
+
+    gate = None
+    if not args.no_gate:
+        import oracle
+        step()
+        torch.cuda.synchronize()
+        i = int(np.argmax(lengths))
+        a, b = int(cu[i]), int(cu[i + 1])
+        ro, rs = oracle.fwd(*(inp[n][:, a:b].contiguous() for n in ("q", "k", "v", "alpha", "beta")))
+        gate = {"longest_sequence": lengths[i],
+                "rel_l2_o": float(np.linalg.norm(out[:, a:b].double().cpu().numpy() - ro) / np.linalg.norm(ro)),
+                "rel_l2_state": float(np.linalg.norm(sf[i].double().cpu().numpy() - rs[0]) / np.linalg.norm(rs))}
+        if not (gate["rel_l2_o"] <= 2e-2 and gate["rel_l2_state"] <= 2e-2):
+            print("correctness gate failed: %s" % json.dumps(gate), file=sys.stderr)
+            sys.exit(1)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    abytes = T * H * 1032 + N * H * V * K * 4
+    longest_chunks = -(-max(lengths) // C)
+    print(json.dumps({
+        "metric": "GDN chunk fwd (packed ragged batch) tokens/s",
+        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "varlen_bf16: %d sequences, %d tokens, lengths log-uniform in "
+                               "[128, 8192] (longest %d), H=%d K=V=%d chunk=%d"
+                               % (N, T, max(lengths), H, K, C)},
+        "roofline": {"bound": "hbm", "achieved": abytes / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": abytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": abytes},
+        "us_per_chunk_of_longest": ms * 1e3 / longest_chunks,
+        "gate": gate,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,9 +324,17 @@ def main():
                     help="time gdn_chunk_bwd on the forward+backward workload instead")
     ap.add_argument("--decode", action="store_true",
                     help="time gdn_decode_step on the decode workload instead")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time gdn_chunk_fwd_varlen on a packed ragged batch instead")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.varlen:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only; run with --gpus 1", file=sys.stderr)
+            sys.exit(2)
+        bench_varlen(args)
         return
     if args.decode:
         if args.gpus != 1:

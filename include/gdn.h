@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -106,6 +106,38 @@ GDN_API gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v,
                            void *o, float *final_state,
                            int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                            int64_t chunk, gdn_dtype_t dtype, void *stream);
+
+/*
+ * gdn_chunk_fwd_varlen -- gdn_chunk_fwd over a packed batch of N independent
+ * sequences of different lengths (each starts from its own state; no state
+ * passes between sequences).
+ *
+ *   q, k           [T,H,K] dtype        the N sequences back to back (T tokens in all)
+ *   v, o           [T,H,V] dtype
+ *   alpha, beta    [T,H]   float32
+ *   cu_seqlens     [N+1]   int32        DEVICE array of offsets: sequence n is tokens
+ *                                       cu_seqlens[n] .. cu_seqlens[n+1]-1; must be
+ *                                       non-decreasing from 0 to T (empty sequences
+ *                                       allowed).  Read on the device, not checked:
+ *                                       offsets are clamped into [0, T], so a bad
+ *                                       table gives wrong results, never an access
+ *                                       outside the tensors.  4-byte aligned.
+ *   N              number of sequences, N >= 1
+ *   initial_state, final_state  [N,H,V,K] float32, NULL allowed as for gdn_chunk_fwd
+ *   T, H, K, V, chunk, dtype, stream    as for gdn_chunk_fwd (chunks restart at
+ *                                       every sequence start)
+ *
+ * Equal (bitwise) to N separate gdn_chunk_fwd calls with B = 1.  "OpenGDN 0.1.0",
+ * section "Scope", lists packed variable-length batches as outside its operator;
+ * this entry point adds them with the same per-sequence contract.
+ */
+GDN_API gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v,
+                                  const float *alpha, const float *beta,
+                                  const int32_t *cu_seqlens, int64_t N,
+                                  const float *initial_state,
+                                  void *o, float *final_state,
+                                  int64_t T, int64_t H, int64_t K, int64_t V,
+                                  int64_t chunk, gdn_dtype_t dtype, void *stream);
 
 /*
  * gdn_decode_step -- one token of the recurrence for every (batch, head), the

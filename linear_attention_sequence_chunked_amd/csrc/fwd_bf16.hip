@@ -413,7 +413,8 @@ __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_e
 fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const float* __restrict__ alpha, const float* __restrict__ beta,
                 const float* __restrict__ s0, bf16* __restrict__ o, float* __restrict__ s_final,
-                float* __restrict__ s_ckpt, int T, int H, int K, int V, int C, int nslice) {
+                float* __restrict__ s_ckpt, const int* __restrict__ cu, int T, int H, int K, int V,
+                int C, int nslice) {
   using SM = Smem<KD, VS, CP>;
   constexpr int LDC = SM::LDC;
   constexpr int NTB = CP / 16;          // token blocks per chunk tile
@@ -448,7 +449,17 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const size_t tok_k = (size_t)H * K;
   const size_t tok_v = (size_t)H * V;
   const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
-  const int NT = (T + C - 1) / C;
+  // This workgroup's sequence: row b of a dense batch, or the packed sequence
+  // [cu[b], cu[b+1]) (offsets clamped into [0, T], so a bad table can give wrong
+  // results but never an access outside the tensors).
+  size_t seq0 = (size_t)b * T;
+  int Tn = T;
+  if (cu) {
+    const int s = min(max(cu[b], 0), T), e = min(max(cu[b + 1], s), T);
+    seq0 = s;
+    Tn = e - s;
+  }
+  const int NT = (Tn + C - 1) / C;
 
   // ---- zero the P and Tm rings: their upper blocks are read as zeros
   for (int i = tid; i < 2 * CP * LDC; i += kThreads) {
@@ -503,10 +514,10 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
   auto load_chunk = [&](int c, StageRegs& R) {
     const int t0 = c * C;
-    const int n = min(C, T - t0);
-    const bf16* kb = k + ((size_t)b * T + t0) * tok_k + (size_t)h * K;
-    const bf16* qb = q + ((size_t)b * T + t0) * tok_k + (size_t)h * K;
-    const bf16* vbp = v + ((size_t)b * T + t0) * tok_v + (size_t)h * V + v0;
+    const int n = min(C, Tn - t0);
+    const bf16* kb = k + (seq0 + t0) * tok_k + (size_t)h * K;
+    const bf16* qb = q + (seq0 + t0) * tok_k + (size_t)h * K;
+    const bf16* vbp = v + (seq0 + t0) * tok_v + (size_t)h * V + v0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       R.k[j] = zero8();
@@ -524,7 +535,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     R.a = 1.0f;
     R.b = 0.0f;
     if (wave == W_GATE && lane < n) {  // one Gram wave holds the gates
-      const size_t go = ((size_t)b * T + t0 + lane) * H + h;
+      const size_t go = (seq0 + t0 + lane) * H + h;
       R.a = alpha[go];
       R.b = beta[go];
     }
@@ -691,8 +702,8 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       // O^T = Z^T diag(gam) + U^T P^T: lane (g, s) ends with O[token 16 tb + s]
       // [v 16 vb + 4g .. 4g + 3], stored as one 8-byte write.
       const int t0 = x * C;
-      const int n = min(C, T - t0);
-      bf16* obase = o + ((size_t)b * T + t0) * tok_v + (size_t)h * V + v0 + 16 * vb + 4 * lg;
+      const int n = min(C, Tn - t0);
+      bf16* obase = o + (seq0 + t0) * tok_v + (size_t)h * V + v0 + 16 * vb + 4 * lg;
       if (o)  // no output when only states are wanted
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
@@ -810,7 +821,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP>), dim3(nblk), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                      static_cast<const bf16*>(a.v), a.alpha, a.beta, a.s0,
-                     static_cast<bf16*>(a.o), a.s_final, a.s_ckpt, a.T, a.H, a.K, a.V, a.chunk, nslice);
+                     static_cast<bf16*>(a.o), a.s_final, a.s_ckpt, a.cu_seqlens, a.T, a.H, a.K, a.V,
+                     a.chunk, nslice);
   return hipGetLastError();
 }
 

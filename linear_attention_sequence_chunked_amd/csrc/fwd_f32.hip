@@ -36,7 +36,8 @@ __global__ void __launch_bounds__(kThreads)
 fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                const float* __restrict__ alpha, const float* __restrict__ beta,
                const float* __restrict__ s0, TIn* __restrict__ o, float* __restrict__ s_final,
-               float* __restrict__ s_ckpt, int T, int H, int K, int V, int C, int VS) {
+               float* __restrict__ s_ckpt, const int* __restrict__ cu, int T, int H, int K,
+               int V, int C, int VS) {
   extern __shared__ float lds[];
   const int LK = K + 1;            // padded rows: threads reading different rows use different banks
   float* sq = lds;                 // [C][LK]
@@ -59,26 +60,35 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
 
   for (int i = tid; i < VS * K; i += kThreads) sS[(i / K) * LK + i % K] = s0 ? s0[state_base + i] : 0.0f;
 
-  for (int t0 = 0; t0 < T; t0 += C) {
-    const int n = min(C, T - t0);
+  // the sequence: row b of a dense batch, or the packed sequence [cu[b], cu[b+1])
+  // with offsets clamped into [0, T]
+  size_t seq0 = (size_t)b * T;
+  int Tn = T;
+  if (cu) {
+    const int s = min(max(cu[b], 0), T), e = min(max(cu[b + 1], s), T);
+    seq0 = s;
+    Tn = e - s;
+  }
+  for (int t0 = 0; t0 < Tn; t0 += C) {
+    const int n = min(C, Tn - t0);
     __syncthreads();  // previous chunk finished with the tiles
     if (s_ckpt) {  // chunk-start state, [B, H, NT, V, K]
-      const int NT = (T + C - 1) / C;
+      const int NT = (Tn + C - 1) / C;
       float* dst = s_ckpt + ((((size_t)b * H + h) * NT + t0 / C) * V + v0) * (size_t)K;
       for (int i = tid; i < VS * K; i += kThreads) dst[i] = sS[(i / K) * LK + i % K];
     }
     for (int i = tid; i < n * K; i += kThreads) {
       const int r = i / K, c = i - r * K;
-      const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + c;
+      const size_t off = ((seq0 + t0 + r) * H + h) * (size_t)K + c;
       sq[r * LK + c] = to_f32(q[off]);
       sk[r * LK + c] = to_f32(k[off]);
     }
     for (int i = tid; i < n * VS; i += kThreads) {
       const int r = i / VS, c = i - r * VS;
-      sv[i] = to_f32(v[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + c]);
+      sv[i] = to_f32(v[((seq0 + t0 + r) * H + h) * (size_t)V + v0 + c]);
     }
     if (tid < n) {
-      const size_t go = ((size_t)b * T + t0 + tid) * H + h;
+      const size_t go = (seq0 + t0 + tid) * H + h;
       sg[tid] = logf(alpha[go]);
       sb[tid] = beta[go];
     }
@@ -151,7 +161,7 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
       const int r = i / VS, c = i - r * VS;
       float acc = sU[r * VS + c];
       for (int j = 0; j <= r; ++j) acc = fmaf(sA[r * C + j], sv[j * VS + c], acc);
-      o[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + c] = from_f32<TIn>(acc);
+      o[((seq0 + t0 + r) * H + h) * (size_t)V + v0 + c] = from_f32<TIn>(acc);
     }
     // S <- gam_n S + U^T diag(gam_n / gam) K
     const float gn = sg[n - 1];
@@ -185,7 +195,7 @@ hipError_t launch_scalar(const FwdArgs& a, float* s_ckpt, hipStream_t stream) {
   hipLaunchKernelGGL(fwd_f32_kernel<TIn>, grid, dim3(kThreads), lds, stream,
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                      static_cast<const TIn*>(a.v), a.alpha, a.beta, a.s0,
-                     static_cast<TIn*>(a.o), a.s_final, s_ckpt, a.T, a.H, a.K, a.V, C, VS);
+                     static_cast<TIn*>(a.o), a.s_final, s_ckpt, a.cu_seqlens, a.T, a.H, a.K, a.V, C, VS);
   return hipGetLastError();
 }
 

@@ -61,37 +61,42 @@ const char* gdn_status_string(gdn_status_t status) {
   return "unknown status";
 }
 
-gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* initial_state, void* o,
-                           float* final_state, int64_t B, int64_t T, int64_t H, int64_t K,
-                           int64_t V, int64_t chunk, gdn_dtype_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the dense and packed forward entry points.  The token tensors
+// hold NTOK = Bt * T token rows (Bt = B dense, 1 packed); states hold B rows.
+gdn_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* beta, const int32_t* cu_seqlens, const float* initial_state,
+                            void* o, float* final_state, int64_t B, int64_t Bt, int64_t T,
+                            int64_t H, int64_t K, int64_t V, int64_t chunk, gdn_dtype_t dtype,
+                            void* stream) {
   if (!q || !k || !v || !alpha || !beta || !o) return GDN_ERROR_INVALID_VALUE;
-  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_ERROR_INVALID_VALUE;
   const void* ptrs[] = {q, k, v, alpha, beta, initial_state, o, final_state};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
-  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERROR_NOT_SUPPORTED;
-  if (!width_supported(K) || !width_supported(V)) return GDN_ERROR_NOT_SUPPORTED;
-  if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
-  const int64_t maxd = K > V ? K : V;
-  if (B > (INT64_C(1) << 31) || T > (INT64_C(1) << 31) || H > (INT64_C(1) << 31) ||
-      B * T > (INT64_C(1) << 31) || B * T * H * maxd >= (INT64_C(1) << 31))
-    return GDN_ERROR_NOT_SUPPORTED;
+  const gdn_status_t st = check_shape(Bt, T, H, K, V, chunk, dtype);
+  if (st != GDN_SUCCESS) return st;
+  if (B <= 0) return GDN_ERROR_INVALID_VALUE;
+  if (B > (INT64_C(1) << 31) / (H * V * K)) return GDN_ERROR_NOT_SUPPORTED;
 
+  const int64_t ntok = Bt * T;
   const int64_t esz = dtype == GDN_DTYPE_F32 ? 4 : 2;
-  const Range rq = range_of(q, B * T * H * K * esz), rk = range_of(k, B * T * H * K * esz),
-              rv = range_of(v, B * T * H * V * esz), ra = range_of(alpha, B * T * H * 4),
-              rb = range_of(beta, B * T * H * 4), ro = range_of(o, B * T * H * V * esz);
+  const Range rq = range_of(q, ntok * H * K * esz), rk = range_of(k, ntok * H * K * esz),
+              rv = range_of(v, ntok * H * V * esz), ra = range_of(alpha, ntok * H * 4),
+              rb = range_of(beta, ntok * H * 4), ro = range_of(o, ntok * H * V * esz);
   const int64_t state_bytes = B * H * V * K * 4;
-  const Range inputs[] = {rq, rk, rv, ra, rb};
+  const Range inputs[] = {rq, rk, rv, ra, rb,
+                          cu_seqlens ? range_of(cu_seqlens, (B + 1) * 4) : Range{0, 0}};
   for (const Range& r : inputs)
-    if (overlaps(ro, r)) return GDN_ERROR_INVALID_VALUE;
+    if (r.hi != r.lo && overlaps(ro, r)) return GDN_ERROR_INVALID_VALUE;
   if (initial_state && overlaps(ro, range_of(initial_state, state_bytes)))
     return GDN_ERROR_INVALID_VALUE;
   if (final_state) {
     const Range rf = range_of(final_state, state_bytes);
     for (const Range& r : inputs)
-      if (overlaps(rf, r)) return GDN_ERROR_INVALID_VALUE;
+      if (r.hi != r.lo && overlaps(rf, r)) return GDN_ERROR_INVALID_VALUE;
     if (overlaps(rf, ro)) return GDN_ERROR_INVALID_VALUE;
     if (initial_state && initial_state != final_state &&
         overlaps(rf, range_of(initial_state, state_bytes)))
@@ -113,9 +118,34 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
   a.K = static_cast<int>(K);
   a.V = static_cast<int>(V);
   a.chunk = static_cast<int>(chunk);
+  a.cu_seqlens = cu_seqlens;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = dtype == GDN_DTYPE_F32 ? gdn::launch_fwd_f32(a, s) : gdn::launch_fwd_bf16(a, s);
   return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* initial_state, void* o,
+                           float* final_state, int64_t B, int64_t T, int64_t H, int64_t K,
+                           int64_t V, int64_t chunk, gdn_dtype_t dtype, void* stream) {
+  if (B <= 0) return GDN_ERROR_INVALID_VALUE;
+  return chunk_fwd_impl(q, k, v, alpha, beta, nullptr, initial_state, o, final_state, B, B, T, H,
+                        K, V, chunk, dtype, stream);
+}
+
+gdn_status_t gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* beta, const int32_t* cu_seqlens, int64_t N,
+                                  const float* initial_state, void* o, float* final_state,
+                                  int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk,
+                                  gdn_dtype_t dtype, void* stream) {
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0 || N <= 0)
+    return GDN_ERROR_INVALID_VALUE;
+  return chunk_fwd_impl(q, k, v, alpha, beta, cu_seqlens, initial_state, o, final_state, N, 1, T,
+                        H, K, V, chunk, dtype, stream);
 }
 
 gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,

@@ -19,6 +19,9 @@ struct FwdArgs {
   float* s_final;   // may be null (skip)
   int B, T, H, K, V, chunk;
   float* s_ckpt = nullptr;  // optional chunk-start states [B, H, NT, V, K]
+  // optional packed batch: B sequences, sequence b = tokens [cu[b], cu[b+1]) of
+  // the [1, T, H, *] tensors; states are [B, H, V, K]
+  const int* cu_seqlens = nullptr;
 };
 
 // Float32 q/k/v/o: scalar fp32 kernel (exact fp32 products and sums).

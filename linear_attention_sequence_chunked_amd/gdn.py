@@ -36,6 +36,8 @@ SIGNATURES = {
     "gdn_abi_version": (ctypes.c_int, []),
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_chunk_fwd": (ctypes.c_int, [_VP] * 8 + [_I64] * 6 + [ctypes.c_int, _VP]),
+    "gdn_chunk_fwd_varlen": (ctypes.c_int, [_VP] * 6 + [_I64] + [_VP] * 3 + [_I64] * 5 +
+                             [ctypes.c_int, _VP]),
     "gdn_decode_step": (ctypes.c_int, [_VP] * 7 + [_I64] * 4 + [ctypes.c_int, _VP]),
     "gdn_chunk_bwd_workspace_size": (ctypes.c_size_t, [_I64] * 6),
     "gdn_chunk_bwd": (ctypes.c_int, [_VP] * 15 + [ctypes.c_size_t] + [_I64] * 6 + [ctypes.c_int, _VP]),
@@ -234,3 +236,52 @@ def decode_step(q, k, v, alpha, beta, state, *, out=None, stream=None):
                                  _ptr(out), B, H, K, V, _DTYPES[q.dtype], ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_decode_step")
     return out
+
+
+def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, chunk: int = 64, *,
+                     out=None, final_state=None, want_final_state: bool = True, stream=None):
+    """Packed variable-length forward through ``gdn_chunk_fwd_varlen``.
+
+    q, k [1,T,H,K], v [1,T,H,V], alpha, beta [1,T,H] hold N sequences back to back;
+    ``cu_seqlens`` is an int32 device tensor [N+1] of offsets (0 .. T).  States are
+    [N,H,V,K].  Returns ``(o, final_state)``.
+    """
+    lib = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4 or q.shape[0] != 1:
+        raise ValueError("q must be a 4-D tensor [1,T,H,K] (sequences packed along T)")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    if q.dtype not in _DTYPES:
+        raise NotImplementedError("dtype %s is not supported (float32 or bfloat16)" % q.dtype)
+    _, T, H, K = q.shape
+    if v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [1,T,H,V]")
+    V = v.shape[-1]
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor [N+1]")
+    N = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _check(k, "k", (1, T, H, K), q.dtype, dev)
+    _check(v, "v", (1, T, H, V), q.dtype, dev)
+    _check(alpha, "alpha", (1, T, H), torch.float32, dev)
+    _check(beta, "beta", (1, T, H), torch.float32, dev)
+    _check(q, "q", (1, T, H, K), q.dtype, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, V, K), torch.float32, dev)
+    if out is None:
+        out = torch.empty((1, T, H, V), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", (1, T, H, V), q.dtype, dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (N, H, V, K), torch.float32, dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = lib.gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                      _ptr(cu_seqlens), N, _ptr(initial_state), _ptr(out),
+                                      _ptr(final_state), T, H, K, V, int(chunk), _DTYPES[q.dtype],
+                                      ctypes.c_void_p(s.cuda_stream))
+    _raise_for(rc, "gdn_chunk_fwd_varlen")
+    return out, final_state

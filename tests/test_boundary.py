@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = gdn.load_library()
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     for code in range(4):
         assert len(gdn.status_string(code)) > 0
     assert gdn.status_string(99) == "unknown status"
@@ -164,3 +164,22 @@ def test_decode_rejects_bad_arguments():
     assert dcall(dtype=3) == gdn.GDN_ERROR_NOT_SUPPORTED
     assert dcall(same=("s", "o")) == gdn.GDN_ERROR_INVALID_VALUE      # o aliases the state
     assert dcall(same=("q", "s")) == gdn.GDN_ERROR_INVALID_VALUE      # state aliases q
+
+
+def test_varlen_rejects_bad_arguments():
+    lib = gdn.load_library()
+
+    def vcall(cu=8, N=3, misalign=None, null=None, T=100, K=64):
+        names = ["q", "k", "v", "a", "b"]
+        args = [None if n == null else addr(i, 2 if n == misalign else 0) for i, n in enumerate(names)]
+        cu_ptr = None if cu is None else (addr(cu) if isinstance(cu, int) else cu)
+        return lib.gdn_chunk_fwd_varlen(*args, cu_ptr, N, None, addr(6), None, T, 2, K, 64, 64,
+                                        gdn.GDN_DTYPE_BF16, None)
+
+    assert vcall(cu=None) == gdn.GDN_ERROR_INVALID_VALUE
+    assert vcall(cu=ctypes.c_void_p(BASE + 8 * STEP + 2)) == gdn.GDN_ERROR_INVALID_VALUE  # misaligned table
+    assert vcall(N=0) == gdn.GDN_ERROR_INVALID_VALUE
+    assert vcall(null="q") == gdn.GDN_ERROR_INVALID_VALUE
+    assert vcall(misalign="v") == gdn.GDN_ERROR_INVALID_VALUE
+    assert vcall(K=48) == gdn.GDN_ERROR_NOT_SUPPORTED
+    assert vcall(cu=ctypes.c_void_p(BASE + 6 * STEP + 64)) == gdn.GDN_ERROR_INVALID_VALUE  # o overlaps the table
