@@ -298,13 +298,14 @@ __device__ __forceinline__ void levels_part(bf16* tt, const bf16* ap, int lane, 
 }
 
 // Gram tiles of one chunk for token-block rows R0 and R1 (compile-time, so all
-// fragments stay in registers): TYPE 0 builds A (strictly lower, beta and decay
-// applied; diagonal blocks to `ad` in fp32, the off-diagonal blocks the solve
-// needs to `ap`), TYPE 1 builds P (lower, decay applied) into the P ring.  The
-// key fragments of rows 0..R1 are read once and reused across tiles.
+// fragments stay in registers).  TYPE 0 builds A (strictly lower, beta and
+// decay applied; diagonal blocks to `ad` in fp32, the off-diagonal blocks the
+// solve needs to `ap`), TYPE 1 builds P (lower, decay applied) into the P ring,
+// TYPE 2 builds both from one read of the key fragments.  The key fragments of
+// rows 0..R1 are read once and reused across tiles.
 template <int KD, int CP, int TYPE, int R0, int R1, typename SM>
 __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
-  constexpr int NTB = CP / 16;
+  constexpr bool DA = TYPE != 1, DP = TYPE != 0;
   constexpr int KS = KD / 32;
   constexpr int LDC = SM::LDC, LDA = SM::LDA;
   const int ls = lane & 15, lg = lane >> 4;
@@ -316,61 +317,68 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
   const lf32* g1 = pin(gl + ls);
   const lf32* g4 = pin(gl + 4 * lg);
   constexpr int BOFF = SM::BETA;
-  // every operand and gate value is requested before the first MFMA
+  // Every operand and gate value is requested before the first MFMA, gates
+  // first and fragments in k-step order, so the first round of MFMAs waits only
+  // for its own fragments.
   bf16x8 kf[R1 + 1][KS], af[2][KS];
   f32x4 gr[2], br[2];
   float gi[R1 + 1];
 #pragma unroll
-  for (int tb = 0; tb <= R1; ++tb) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = ld8(kr + 16 * tb * LDK + 32 * ks);
-    gi[tb] = g1[16 * tb];
-  }
+  for (int tb = 0; tb <= R1; ++tb) gi[tb] = g1[16 * tb];
 #pragma unroll
   for (int ri = 0; ri < 2; ++ri) {
     const int tr = ri == 0 ? R0 : R1;
-    if (TYPE == 1) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) af[ri][ks] = ld8(qr + 16 * tr * LDK + 32 * ks);
-    }
     gr[ri] = *reinterpret_cast<const lf32x4*>(g4 + 16 * tr);
-    br[ri] = *reinterpret_cast<const lf32x4*>(g4 + BOFF + 16 * tr);
+    if (DA) br[ri] = *reinterpret_cast<const lf32x4*>(g4 + BOFF + 16 * tr);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int tb = 0; tb <= R1; ++tb) kf[tb][ks] = ld8(kr + 16 * tb * LDK + 32 * ks);
+    if (DP) {
+#pragma unroll
+      for (int ri = 0; ri < 2; ++ri) af[ri][ks] = ld8(qr + 16 * (ri == 0 ? R0 : R1) * LDK + 32 * ks);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // all tiles advance together over the k-steps: independent accumulators
+  // All tiles advance together over the k-steps (independent accumulators); the
+  // scheduling barrier after each round keeps that order.
   constexpr int NT0 = R0 + 1, NTILE = R0 + 1 + R1 + 1;
-  f32x4 acc[NTILE];
+  f32x4 accA[NTILE], accP[NTILE];
 #pragma unroll
-  for (int t = 0; t < NTILE; ++t) acc[t] = zero4();
+  for (int t = 0; t < NTILE; ++t) accA[t] = accP[t] = zero4();
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
       const int ri = t < NT0 ? 0 : 1;
       const int tr = ri == 0 ? R0 : R1;
       const int tc = ri == 0 ? t : t - NT0;
-      acc[t] = mma(TYPE == 0 ? kf[tr][ks] : af[ri][ks], kf[tc][ks], acc[t]);
+      if (DA) accA[t] = mma(kf[tr][ks], kf[tc][ks], accA[t]);
+      if (DP) accP[t] = mma(af[ri][ks], kf[tc][ks], accP[t]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // Decay 2^(g_r - g_i).  Diagonal tiles: per element, masked before the
   // exponential.  Off-diagonal tiles (every i < r): 2^(g_r - g_ref) 2^(g_ref - g_i)
-  // with g_ref the gate of the row block's first token, both factors <= 1; the
-  // row factor (times beta for A) is shared by the row block's tiles.
-  lbf16* pw = nullptr;
-  lbf16* aw = nullptr;
-  lf32* adw = nullptr;
-  if (TYPE == 1) pw = pin(lds(sm.pt[c % 2]) + ls * LDC + 4 * lg);
-  if (TYPE == 0) {
-    aw = pin(lds(sm.ap[c % 2]) + ls * LDA + 4 * lg);
-    adw = pin(lds(sm.ad) + ls * 16 + 4 * lg);
-  }
+  // with g_ref the gate of the row block's first token (broadcast from lane 0's
+  // column gates), both factors <= 1; the row factor is shared by the row
+  // block's tiles.
+  float gref[2];
   f32x4 rowf[2];
 #pragma unroll
   for (int ri = 0; ri < 2; ++ri) {
-    const int tr = ri == 0 ? R0 : R1;
-    const float gref = gl[16 * tr];
+    gref[ri] = bits_f(__builtin_amdgcn_readlane(f_bits(gi[ri == 0 ? R0 : R1]), 0));
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      rowf[ri][e] = (TYPE == 0 ? br[ri][e] : 1.0f) * __builtin_amdgcn_exp2f(gr[ri][e] - gref);
+    for (int e = 0; e < 4; ++e) rowf[ri][e] = __builtin_amdgcn_exp2f(gr[ri][e] - gref[ri]);
+  }
+  lbf16* pw = nullptr;
+  lbf16* aw = nullptr;
+  lf32* adw = nullptr;
+  if (DP) pw = pin(lds(sm.pt[c % 2]) + ls * LDC + 4 * lg);
+  if (DA) {
+    aw = pin(lds(sm.ap[c % 2]) + ls * LDA + 4 * lg);
+    adw = pin(lds(sm.ad) + ls * 16 + 4 * lg);
   }
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
@@ -378,34 +386,45 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
     const int tr = ri == 0 ? R0 : R1;
     const int tc = ri == 0 ? t : t - NT0;
     const int i = 16 * tc + ls;
-    f32x4 val;
+    // per-element decay of this tile, shared by A and P (the mask differs on
+    // the diagonal: strict for A, inclusive for P)
+    f32x4 decA, decP;
     if (tc == tr) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * tr + 4 * lg + e;
-        const bool keep = TYPE == 0 ? (i < r) : (i <= r);
-        const float dec = __builtin_amdgcn_exp2f(keep ? gr[ri][e] - gi[tc] : -INFINITY);
-        val[e] = (TYPE == 0 ? br[ri][e] : 1.0f) * dec * acc[t][e];
+        const float d = gr[ri][e] - gi[tc];
+        if (DA) decA[e] = __builtin_amdgcn_exp2f(i < r ? d : -INFINITY);
+        if (DP) decP[e] = __builtin_amdgcn_exp2f(i <= r ? d : -INFINITY);
       }
     } else {
-      const float colf = __builtin_amdgcn_exp2f(gl[16 * tr] - gi[tc]);
+      const float colf = __builtin_amdgcn_exp2f(gref[ri] - gi[tc]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = rowf[ri][e] * (colf * acc[t][e]);
+      for (int e = 0; e < 4; ++e) decA[e] = decP[e] = rowf[ri][e] * colf;
     }
     // accumulator tiles are stored transposed: lane (g, s) writes row s of the
     // transposed tile, 4 consecutive bf16 (or fp32) at column 4g
-    const bf16x4 vb4 = bf16x4{(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
-    if (TYPE == 1) {
-      *reinterpret_cast<lds_bf16x4*>(pw + 16 * tc * LDC + 16 * tr) = vb4;
-    } else if (tc == tr) {
-      *reinterpret_cast<lf32x4*>(adw + tr * SM::ADS) = val;  // [c][r]
-    } else {
-      // packed A^T blocks: (1,0) -> 0, (3,2) -> 16, (2,0..1) -> 32.., (3,0..1) -> 64..
-      const int off = tr == 1 ? 0 : (tr == 3 && tc == 2 ? 16 : (tr == 2 ? 32 : 64) + 16 * tc);
-      *reinterpret_cast<lds_bf16x4*>(aw + off * LDA) = vb4;
+    if (DP) {
+      f32x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = decP[e] * accP[t][e];
+      *reinterpret_cast<lds_bf16x4*>(pw + 16 * tc * LDC + 16 * tr) =
+          bf16x4{(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
+    }
+    if (DA) {
+      f32x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = br[ri][e] * (decA[e] * accA[t][e]);
+      if (tc == tr) {
+        *reinterpret_cast<lf32x4*>(adw + tr * SM::ADS) = val;  // [c][r]
+      } else {
+        // packed A^T blocks: (1,0) -> 0, (3,2) -> 16, (2,0..1) -> 32.., (3,0..1) -> 64..
+        const int off = tr == 1 ? 0 : (tr == 3 && tc == 2 ? 16 : (tr == 2 ? 32 : 64) + 16 * tc);
+        *reinterpret_cast<lds_bf16x4*>(aw + off * LDA) =
+            bf16x4{(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
+      }
     }
   }
-  (void)NTB;
 }
 
 template <int KD, int VS, int CP>
