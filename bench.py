@@ -324,6 +324,8 @@ def main():
                     help="time gdn_chunk_bwd on the forward+backward workload instead")
     ap.add_argument("--decode", action="store_true",
                     help="time gdn_decode_step on the decode workload instead")
+    ap.add_argument("--segments", type=int, default=1,
+                    help="run the forward segment-parallel with this many segments per sequence")
     ap.add_argument("--varlen", action="store_true",
                     help="time gdn_chunk_fwd_varlen on a packed ragged batch instead")
     args = ap.parse_args()
@@ -357,7 +359,7 @@ def main():
     import numpy as np
     import torch
 
-    from linear_attention_sequence_chunked_amd import chunk_fwd
+    from linear_attention_sequence_chunked_amd import chunk_fwd, chunk_fwd_segmented, segmented_workspace_size
     from linear_attention_sequence_chunked_amd.workloads import WORKLOADS, workload_inputs
 
     w = WORKLOADS[args.workload]
@@ -370,10 +372,20 @@ def main():
     outs = [torch.empty(B, T, H, V, dtype=w.dtype, device=dev) for _ in range(nsets)]
     states = [torch.empty(B, H, V, K, dtype=torch.float32, device=dev) for _ in range(nsets)]
 
+    seg_ws = None
+    if args.segments > 1:
+        seg_ws = torch.empty(segmented_workspace_size(B, T, H, K, V, C, args.segments),
+                             dtype=torch.uint8, device=dev)
+
     def step(i):
         s = sets[i % nsets]
-        chunk_fwd(s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["initial_state"], chunk=C,
-                  out=outs[i % nsets], final_state=states[i % nsets])
+        if seg_ws is None:
+            chunk_fwd(s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["initial_state"], chunk=C,
+                      out=outs[i % nsets], final_state=states[i % nsets])
+        else:
+            chunk_fwd_segmented(s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["initial_state"],
+                                chunk=C, segments=args.segments, out=outs[i % nsets],
+                                final_state=states[i % nsets], workspace=seg_ws)
 
     # correctness gate on input set 0
     gate = None
@@ -449,7 +461,9 @@ def main():
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": "%s: B=%d T=%d H=%d K=%d V=%d chunk=%d, inputs resident in HBM, "
-                               "3 rotating input sets" % (w.name, B, T, H, K, V, C),
+                               "3 rotating input sets%s" % (w.name, B, T, H, K, V, C,
+                                                            ", %d segments per sequence" % args.segments
+                                                            if args.segments > 1 else ""),
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": K,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -138,6 +138,50 @@ GDN_API gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const vo
                                   void *o, float *final_state,
                                   int64_t T, int64_t H, int64_t K, int64_t V,
                                   int64_t chunk, gdn_dtype_t dtype, void *stream);
+
+/*
+ * gdn_chunk_fwd_segmented_workspace_size -- bytes of device workspace that
+ * gdn_chunk_fwd_segmented needs (0 when a size is not positive).  It holds, per
+ * (batch, segment, head), a K x K transition, three [V, K] states and a K x K
+ * identity, all float32, plus the segment table.
+ */
+GDN_API size_t gdn_chunk_fwd_segmented_workspace_size(int64_t B, int64_t T, int64_t H,
+                                                      int64_t K, int64_t V, int64_t chunk,
+                                                      int64_t segments);
+
+/*
+ * gdn_chunk_fwd_segmented -- the result of gdn_chunk_fwd (same arguments and
+ * outputs, up to float rounding) computed with every sequence split into
+ * `segments` pieces of equal chunk-aligned length that run in parallel:
+ *
+ *   1. every segment from a zero state gives its end state N_s, and from an
+ *      identity [K, K] state with zero values gives its transition A_s
+ *      (the token step is affine in the state: S_end = S_start A_s + N_s);
+ *   2. per stream, start_{s+1} = start_s A_s + N_s from start_0 = initial_state;
+ *   3. every segment again from its true start writes o (and the last one the
+ *      final state).
+ *
+ * State passing between chunks is the chunk recurrence of "Sparse Delta Memory:
+ * layer and kernels", section "What the layer computes", applied between
+ * segments.  It costs about 2.5 times the work of gdn_chunk_fwd and shortens the
+ * sequential part `segments` times, so it pays only when B * H alone leaves most
+ * of the GPU idle (long sequences, few streams).
+ *
+ *   segments       1 <= segments <= T (1 is exactly gdn_chunk_fwd, no workspace used)
+ *   workspace      device scratch of at least
+ *                  gdn_chunk_fwd_segmented_workspace_size(...) bytes, 16-byte
+ *                  aligned, owned by the caller, contents undefined afterwards;
+ *                  it may not overlap any other buffer
+ *   the rest       as for gdn_chunk_fwd
+ */
+GDN_API gdn_status_t gdn_chunk_fwd_segmented(const void *q, const void *k, const void *v,
+                                     const float *alpha, const float *beta,
+                                     const float *initial_state,
+                                     void *o, float *final_state,
+                                     int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                     int64_t chunk, int64_t segments,
+                                     void *workspace, size_t workspace_bytes,
+                                     gdn_dtype_t dtype, void *stream);
 
 /*
  * gdn_decode_step -- one token of the recurrence for every (batch, head), the

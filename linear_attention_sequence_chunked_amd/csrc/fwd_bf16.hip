@@ -536,7 +536,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     const int n = min(C, Tn - t0);
     const bf16* kb = k + (seq0 + t0) * tok_k + (size_t)h * K;
     const bf16* qb = q + (seq0 + t0) * tok_k + (size_t)h * K;
-    const bf16* vbp = v + (seq0 + t0) * tok_v + (size_t)h * V + v0;
+    const bf16* vbp = v ? v + (seq0 + t0) * tok_v + (size_t)h * V + v0 : nullptr;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       R.k[j] = zero8();
@@ -549,7 +549,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       R.v[j] = zero8();
-      if (vrow[j] < n) R.v[j] = *reinterpret_cast<const bf16x8*>(vbp + vgo[j]);
+      if (v && vrow[j] < n) R.v[j] = *reinterpret_cast<const bf16x8*>(vbp + vgo[j]);  // no v: zeros
     }
     R.a = 1.0f;
     R.b = 0.0f;

@@ -85,7 +85,7 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
     }
     for (int i = tid; i < n * VS; i += kThreads) {
       const int r = i / VS, c = i - r * VS;
-      sv[i] = to_f32(v[((seq0 + t0 + r) * H + h) * (size_t)V + v0 + c]);
+      sv[i] = v ? to_f32(v[((seq0 + t0 + r) * H + h) * (size_t)V + v0 + c]) : 0.0f;  // no v: zeros
     }
     if (tid < n) {
       const size_t go = (seq0 + t0 + tid) * H + h;

@@ -148,6 +148,74 @@ gdn_status_t gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
                         H, K, V, chunk, dtype, stream);
 }
 
+size_t gdn_chunk_fwd_segmented_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K,
+                                              int64_t V, int64_t chunk, int64_t segments) {
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0 || segments <= 0) return 0;
+  return gdn::fwd_segmented_workspace_bytes(B, T, H, K, V, chunk, segments);
+}
+
+gdn_status_t gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                     const float* alpha, const float* beta,
+                                     const float* initial_state, void* o, float* final_state,
+                                     int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                     int64_t chunk, int64_t segments, void* workspace,
+                                     size_t workspace_bytes, gdn_dtype_t dtype, void* stream) {
+  if (segments <= 0) return GDN_ERROR_INVALID_VALUE;
+  if (segments == 1)
+    return chunk_fwd_impl(q, k, v, alpha, beta, nullptr, initial_state, o, final_state, B, B, T,
+                          H, K, V, chunk, dtype, stream);
+  if (!workspace || !aligned16(workspace)) return GDN_ERROR_INVALID_VALUE;
+  // shape checks of the dense call, plus the B * segments packed states
+  const gdn_status_t st = check_shape(B, T, H, K, V, chunk, dtype);
+  if (st != GDN_SUCCESS) return st;
+  if (segments > T || B * segments > (INT64_C(1) << 31) / (H * K * (K > V ? K : V)))
+    return GDN_ERROR_NOT_SUPPORTED;
+  if (workspace_bytes < gdn::fwd_segmented_workspace_bytes(B, T, H, K, V, chunk, segments))
+    return GDN_ERROR_INVALID_VALUE;
+  const int64_t esz = dtype == GDN_DTYPE_F32 ? 4 : 2;
+  const Range rw = range_of(workspace, (int64_t)workspace_bytes);
+  const Range others[] = {range_of(q, B * T * H * K * esz), range_of(k, B * T * H * K * esz),
+                          range_of(v, B * T * H * V * esz), range_of(alpha, B * T * H * 4),
+                          range_of(beta, B * T * H * 4), range_of(o, B * T * H * V * esz),
+                          initial_state ? range_of(initial_state, B * H * V * K * 4) : Range{0, 0},
+                          final_state ? range_of(final_state, B * H * V * K * 4) : Range{0, 0}};
+  for (const Range& r : others)
+    if (r.hi != r.lo && overlaps(rw, r)) return GDN_ERROR_INVALID_VALUE;
+  // the pointer, alignment and overlap checks of the dense call
+  if (!q || !k || !v || !alpha || !beta || !o) return GDN_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {q, k, v, alpha, beta, initial_state, o, final_state};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
+  const Range ro = range_of(o, B * T * H * V * esz);
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(ro, others[i])) return GDN_ERROR_INVALID_VALUE;
+  if (initial_state && overlaps(ro, others[6])) return GDN_ERROR_INVALID_VALUE;
+  if (final_state) {
+    for (int i = 0; i < 6; ++i)
+      if (overlaps(others[7], others[i])) return GDN_ERROR_INVALID_VALUE;
+    if (initial_state && initial_state != final_state && overlaps(others[7], others[6]))
+      return GDN_ERROR_INVALID_VALUE;
+  }
+  gdn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.s0 = initial_state;
+  a.o = o;
+  a.s_final = final_state;
+  a.B = static_cast<int>(B);
+  a.T = static_cast<int>(T);
+  a.H = static_cast<int>(H);
+  a.K = static_cast<int>(K);
+  a.V = static_cast<int>(V);
+  a.chunk = static_cast<int>(chunk);
+  hipError_t err = gdn::launch_fwd_segmented(a, dtype == GDN_DTYPE_BF16, static_cast<int>(segments),
+                                             workspace, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
+}
+
 gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, float* state, void* o, int64_t B, int64_t H,
                              int64_t K, int64_t V, gdn_dtype_t dtype, void* stream) {

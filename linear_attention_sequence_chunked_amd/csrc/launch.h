@@ -54,6 +54,12 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 
+// Segment-parallel forward (P segments per sequence) with a caller workspace.
+size_t fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                     int64_t chunk, int64_t segments);
+hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int segments, void* workspace,
+                                hipStream_t stream);
+
 // One decode step (T = 1), already validated by the C-ABI layer.
 struct DecodeArgs {
   const void* q;      // [B, H, K]

@@ -38,6 +38,9 @@ SIGNATURES = {
     "gdn_chunk_fwd": (ctypes.c_int, [_VP] * 8 + [_I64] * 6 + [ctypes.c_int, _VP]),
     "gdn_chunk_fwd_varlen": (ctypes.c_int, [_VP] * 6 + [_I64] + [_VP] * 3 + [_I64] * 5 +
                              [ctypes.c_int, _VP]),
+    "gdn_chunk_fwd_segmented_workspace_size": (ctypes.c_size_t, [_I64] * 7),
+    "gdn_chunk_fwd_segmented": (ctypes.c_int, [_VP] * 8 + [_I64] * 7 + [_VP, ctypes.c_size_t] +
+                                [ctypes.c_int, _VP]),
     "gdn_decode_step": (ctypes.c_int, [_VP] * 7 + [_I64] * 4 + [ctypes.c_int, _VP]),
     "gdn_chunk_bwd_workspace_size": (ctypes.c_size_t, [_I64] * 6),
     "gdn_chunk_bwd": (ctypes.c_int, [_VP] * 15 + [ctypes.c_size_t] + [_I64] * 6 + [ctypes.c_int, _VP]),
@@ -284,4 +287,57 @@ def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, chunk
                                       _ptr(final_state), T, H, K, V, int(chunk), _DTYPES[q.dtype],
                                       ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_chunk_fwd_varlen")
+    return out, final_state
+
+
+def segmented_workspace_size(B: int, T: int, H: int, K: int, V: int, chunk: int, segments: int) -> int:
+    """Bytes of device workspace ``gdn_chunk_fwd_segmented`` needs."""
+    return int(load_library().gdn_chunk_fwd_segmented_workspace_size(B, T, H, K, V, chunk, segments))
+
+
+def chunk_fwd_segmented(q, k, v, alpha, beta, initial_state=None, chunk: int = 64,
+                        segments: int = 2, *, out=None, final_state=None,
+                        want_final_state: bool = True, workspace=None, stream=None):
+    """:func:`chunk_fwd` computed segment-parallel (``gdn_chunk_fwd_segmented``):
+    each sequence is split into ``segments`` pieces processed in parallel, joined by
+    their affine state maps.  Returns ``(o, final_state)``."""
+    lib = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B,T,H,K]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    if q.dtype not in _DTYPES:
+        raise NotImplementedError("dtype %s is not supported (float32 or bfloat16)" % q.dtype)
+    B, T, H, K = q.shape
+    if v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B,T,H,V]")
+    V = v.shape[-1]
+    _check(k, "k", (B, T, H, K), q.dtype, dev)
+    _check(v, "v", (B, T, H, V), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, V, K), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", (B, T, H, V), q.dtype, dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, H, V, K), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (B, H, V, K), torch.float32, dev)
+    need = int(lib.gdn_chunk_fwd_segmented_workspace_size(B, T, H, K, V, int(chunk), int(segments)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = lib.gdn_chunk_fwd_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                         _ptr(initial_state), _ptr(out), _ptr(final_state), B, T,
+                                         H, K, V, int(chunk), int(segments), _ptr(workspace),
+                                         workspace.numel(), _DTYPES[q.dtype],
+                                         ctypes.c_void_p(s.cuda_stream))
+    _raise_for(rc, "gdn_chunk_fwd_segmented")
     return out, final_state

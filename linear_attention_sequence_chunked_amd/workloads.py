@@ -43,7 +43,7 @@ class Workload:
 
 
 # The five workloads of the operator (seeds equal the workload number), plus a decode
-# batch (seed 6).
+# batch (seed 6) and a few-stream long context (seed 9).
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", 1, 64, 2, 16, 16, 16, torch.float32, "sigmoid", seed=1,
                           note="tiny fp32, B1 T64 H2 K=V=16, chunk 16"),
@@ -54,6 +54,10 @@ WORKLOADS = {
     "fwdbwd_bf16": Workload("fwdbwd_bf16", 4, 2048, 6, 128, 128, 64, torch.bfloat16, "decay",
                             with_do=True, seed=4,
                             note="forward+backward shape, B4 T2048 H6 K=V=128, chunk 64"),
+    "long_few_bf16": Workload("long_few_bf16", 1, 32768, 2, 128, 128, 64, torch.bfloat16, "decay",
+                              s0_std=0.02, seed=9,
+                              note="long context with few streams, B1 T32768 H2 K=V=128, chunk 64 "
+                                   "(the case segment parallelism is for)"),
     "decode_bf16": Workload("decode_bf16", 64, 1, 16, 128, 128, 64, torch.bfloat16, "decay",
                             s0_std=0.02, seed=6,
                             note="decode step, 64 streams x 16 heads, K=V=128, one token per "

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = gdn.load_library()
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
     for code in range(4):
         assert len(gdn.status_string(code)) > 0
     assert gdn.status_string(99) == "unknown status"
@@ -183,3 +183,26 @@ def test_varlen_rejects_bad_arguments():
     assert vcall(misalign="v") == gdn.GDN_ERROR_INVALID_VALUE
     assert vcall(K=48) == gdn.GDN_ERROR_NOT_SUPPORTED
     assert vcall(cu=ctypes.c_void_p(BASE + 6 * STEP + 64)) == gdn.GDN_ERROR_INVALID_VALUE  # o overlaps the table
+
+
+def test_segmented_rejects_bad_arguments():
+    lib = gdn.load_library()
+
+    def scall(segments=4, ws_bytes=None, ws=None, T=1000, K=64, null=None):
+        names = ["q", "k", "v", "a", "b", "s0", "o", "sf"]
+        args = [None if (n == null or n in ("s0", "sf")) else addr(i) for i, n in enumerate(names)]
+        need = lib.gdn_chunk_fwd_segmented_workspace_size(2, T, 3, K, 64, 64, segments)
+        wsp = addr(9) if ws is None else ws
+        return lib.gdn_chunk_fwd_segmented(*args, 2, T, 3, K, 64, 64, segments, wsp,
+                                           need if ws_bytes is None else ws_bytes,
+                                           gdn.GDN_DTYPE_BF16, None)
+
+    assert lib.gdn_chunk_fwd_segmented_workspace_size(2, 1000, 3, 64, 64, 64, 4) > 0
+    assert lib.gdn_chunk_fwd_segmented_workspace_size(2, 1000, 3, 64, 64, 64, 0) == 0
+    assert scall(segments=0) == gdn.GDN_ERROR_INVALID_VALUE
+    assert scall(ws_bytes=100) == gdn.GDN_ERROR_INVALID_VALUE
+    assert scall(ws=ctypes.c_void_p(BASE + 9 * STEP + 4)) == gdn.GDN_ERROR_INVALID_VALUE  # misaligned
+    assert scall(ws=ctypes.c_void_p(BASE + 1 * STEP)) == gdn.GDN_ERROR_INVALID_VALUE      # overlaps k
+    assert scall(null="q") == gdn.GDN_ERROR_INVALID_VALUE
+    assert scall(K=48) == gdn.GDN_ERROR_NOT_SUPPORTED
+    assert scall(segments=2000) == gdn.GDN_ERROR_NOT_SUPPORTED                             # more than T
