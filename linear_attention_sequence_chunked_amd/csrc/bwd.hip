@@ -37,10 +37,13 @@
 
 #include <hip/hip_bf16.h>
 
+#include <type_traits>
+
 namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBwdC = 32;   // backward chunk (tokens)
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
@@ -184,23 +187,36 @@ bwd_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 // (2b) Reverse walk: one workgroup per (batch, head, value slice of VS rows).
 // Stores dS' of every chunk to ws_dS [B, H, NT, V, K] and the gradient of the
 // initial state.
-template <typename TIn>
+// Eight consecutive elements as floats (16 bytes of bf16 or 32 bytes of fp32).
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const __hip_bfloat16* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <typename TIn, int K>
 __global__ void __launch_bounds__(kThreads)
 bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ d_o,
-                  const float* __restrict__ alpha, const float* __restrict__ beta,
                   const float* __restrict__ d_sfinal, float* __restrict__ d_s0,
-                  const float* __restrict__ ws_F, float* __restrict__ ws_dS, int T, int H, int K,
+                  const float* __restrict__ ws_F, float* __restrict__ ws_dS, int T, int H,
                   int V, int C, int VS) {
   extern __shared__ float lds[];
   const int LK = K + 1, LV = VS + 1;  // padded rows: no bank conflicts across rows
   float* sq = lds;                 // [C][LK]
   float* sk = sq + C * LK;         // [C][LK]
-  float* sdo = sk + C * LK;        // [C][LV]
-  float* sM = sdo + C * LV;        // [C][C]
-  float* sP = sM + C * C;          // [C][C]
+  float* sdo = sk + C * LK;        // [C][LV]  diag(gam) dO
+  float* sP = sdo + C * LV;        // [C][C]
   float* sT = sP + C * C;          // [C][C]
   float* sdU = sT + C * C;         // [C][LV]
-  float* sdR = sdU + C * LV;       // [C][LV]
+  float* sdR = sdU + C * LV;       // [C][LV]  -diag(beta gam) dR
   float* sdS = sdR + C * LV;       // [VS][LK]
   float* sg = sdS + VS * LK;       // [C]
   float* sgam = sg + C;
@@ -213,8 +229,45 @@ bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
   const int NT = (T + C - 1) / C;
   const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
 
+  // Registers of the next chunk's inputs: they are requested while the current
+  // chunk is computed.  Pieces of 8 elements: q/k rows (KP8 per thread), the dO
+  // slice, and the chunk's P, Tm and gates.
+  constexpr int KP8 = kBwdC * 128 / 8 / kThreads;   // 2
+  float nq[KP8][8], nk[KP8][8], ndo[2], nP[4], nT[4], ng[3];
+  auto fetch = [&](int c) {
+    const int t0 = c * C, n = min(C, T - t0);
+#pragma unroll
+    for (int u = 0; u < KP8; ++u) {
+      const int piece = tid + u * kThreads, r = piece / (K / 8), e8 = (piece % (K / 8)) * 8;
+      if (r < n) {
+        const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + e8;
+        load8(q + off, nq[u]);
+        load8(k + off, nk[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + u * kThreads, r = i / VS, e = i - r * VS;
+      ndo[u] = r < n ? to_f32(d_o[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e]) : 0.0f;
+    }
+    const float* f = ws_F + (((size_t)b * H + h) * NT + c) * factor_floats(C);
+    const int CC = C * C;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + u * kThreads;
+      nP[u] = i < CC ? f[CC + i] : 0.0f;
+      nT[u] = i < CC ? f[2 * CC + i] : 0.0f;
+    }
+    if (tid < C) {
+      ng[0] = f[3 * CC + tid];
+      ng[1] = f[3 * CC + C + tid];
+      ng[2] = f[3 * CC + 2 * C + tid];
+    }
+  };
+
   for (int i = tid; i < VS * K; i += kThreads)
     sdS[(i / K) * LK + i % K] = d_sfinal ? d_sfinal[state_base + i] : 0.0f;
+  fetch(NT - 1);
 
   for (int c = NT - 1; c >= 0; --c) {
     const int t0 = c * C;
@@ -222,19 +275,41 @@ bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     __syncthreads();
     float* dst = ws_dS + ((((size_t)b * H + h) * NT + c) * V + v0) * (size_t)K;
     for (int i = tid; i < VS * K; i += kThreads) dst[i] = sdS[(i / K) * LK + i % K];
-    for (int i = tid; i < n * K; i += kThreads) {
-      const int r = i / K, e = i - r * K;
-      const size_t off = (((size_t)b * T + t0 + r) * H + h) * (size_t)K + e;
-      sq[r * LK + e] = to_f32(q[off]);
-      sk[r * LK + e] = to_f32(k[off]);
+    // stage the fetched chunk
+#pragma unroll
+    for (int u = 0; u < KP8; ++u) {
+      const int piece = tid + u * kThreads, r = piece / (K / 8), e8 = (piece % (K / 8)) * 8;
+      if (r < n) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sq[r * LK + e8 + j] = nq[u][j];
+          sk[r * LK + e8 + j] = nk[u][j];
+        }
+      }
     }
-    for (int i = tid; i < n * VS; i += kThreads) {
-      const int r = i / VS, e = i - r * VS;
-      sdo[r * LV + e] = to_f32(d_o[(((size_t)b * T + t0 + r) * H + h) * (size_t)V + v0 + e]);
+    const int CC = C * C;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < CC) {
+        sP[i] = nP[u];
+        sT[i] = nT[u];
+      }
     }
-    load_factors(ws_F + (((size_t)b * H + h) * NT + c) * factor_floats(C), nullptr, sP, sT, sg,
-                 sgam, sb, C, tid);
+    if (tid < C) {
+      sg[tid] = ng[0];
+      sgam[tid] = ng[1];
+      sb[tid] = ng[2];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + u * kThreads, r = i / VS, e = i - r * VS;
+      if (r < C) sdo[r * LV + e] = ndo[u];
+    }
+    if (c > 0) fetch(c - 1);  // overlaps the arithmetic below
     const float glast = sg[n - 1];
+    __syncthreads();
     // dU = diag(D) K dS'^T + P^T dO
     for (int i = tid; i < n * VS; i += kThreads) {
       const int r = i / VS, e = i - r * VS;
@@ -245,24 +320,40 @@ bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
       sdU[r * LV + e] = acc;
     }
     __syncthreads();
-    // dR = Tm^T dU
+    // dR = Tm^T dU, kept scaled by -beta gam; dO scaled by gam (for the update)
     for (int i = tid; i < n * VS; i += kThreads) {
       const int r = i / VS, e = i - r * VS;
       float acc = 0.0f;
       for (int rr = r; rr < n; ++rr) acc = fmaf(sT[rr * C + r], sdU[rr * LV + e], acc);
-      sdR[r * LV + e] = acc;
+      sdR[r * LV + e] = -sb[r] * sgam[r] * acc;
     }
     __syncthreads();
-    // dS <- gam_last dS + dO^T diag(gam) Q - dR^T diag(beta gam) K
+    for (int i = tid; i < n * VS; i += kThreads) {
+      const int r = i / VS, e = i - r * VS;
+      sdo[r * LV + e] *= sgam[r];
+    }
+    __syncthreads();
+    // dS <- gam_last dS + dO^T diag(gam) Q - dR^T diag(beta gam) K.  A thread
+    // owns one channel j and the rows e = e0, e0 + 2, ..: q and k of token r are
+    // read once for all of them.
     const float gam_last = sgam[n - 1];
-    for (int i = tid; i < VS * K; i += kThreads) {
-      const int e = i / K, j = i - e * K;
-      float acc = gam_last * sdS[e * LK + j];
+    {
+      const int j = tid % K, e0 = tid / K, es = kThreads / K;
+      float acc[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u] = (e0 + u * es < VS) ? gam_last * sdS[(e0 + u * es) * LK + j] : 0.0f;
       for (int r = 0; r < n; ++r) {
-        acc = fmaf(sgam[r] * sdo[r * LV + e], sq[r * LK + j], acc);
-        acc = fmaf(-sb[r] * sgam[r] * sdR[r * LV + e], sk[r * LK + j], acc);
+        const float qv = sq[r * LK + j], kv = sk[r * LK + j];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + u * es;
+          if (e < VS) acc[u] = fmaf(sdR[r * LV + e], kv, fmaf(sdo[r * LV + e], qv, acc[u]));
+        }
       }
-      sdS[e * LK + j] = acc;
+      __syncthreads();  // every thread has read the old dS
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (e0 + u * es < VS) sdS[(e0 + u * es) * LK + j] = acc[u];
     }
   }
   __syncthreads();
@@ -274,11 +365,10 @@ bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 // (3) Token gradients of one chunk: one workgroup per (chunk, head, batch).
 // dQ and dK accumulate in registers (QPT elements per thread), dP and dA in
 // LDS; the value axis is walked in slices of VS.
-constexpr int kBwdC = 32;   // backward chunk (tokens)
 constexpr int kBwdVS = 32;  // value slice of the local kernel
 constexpr int kQPT = kBwdC * 128 / kThreads;
 
-template <typename TIn>
+template <typename TIn, int K>
 __global__ void __launch_bounds__(kThreads)
 bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                  const TIn* __restrict__ d_o, const float* __restrict__ alpha,
@@ -286,7 +376,7 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
                  const float* __restrict__ ws_dS, const float* __restrict__ ws_F,
                  TIn* __restrict__ dq, TIn* __restrict__ dk,
                  TIn* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta,
-                 int T, int H, int K, int V, int C) {
+                 int T, int H, int V, int C) {
   constexpr int VS = kBwdVS;
   const int LK = K + 1;            // padded rows: no bank conflicts across rows
   constexpr int LV = VS + 1;
@@ -518,6 +608,18 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   }
 }
 
+// Calls f with std::integral_constant<int, K> for K in {16, 32, 64, 128}.
+template <typename F>
+hipError_t with_k(int K, F&& f) {
+  switch (K) {
+    case 16: return f(std::integral_constant<int, 16>());
+    case 32: return f(std::integral_constant<int, 32>());
+    case 64: return f(std::integral_constant<int, 64>());
+    case 128: return f(std::integral_constant<int, 128>());
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename TIn>
 hipError_t set_lds_limit(const void* fn) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -565,25 +667,35 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   {
     const int VS = 16;
     const size_t LK = a.K + 1, LV = VS + 1;
-    const size_t lds = sizeof(float) * (2 * C * LK + C * LV + 3 * C * C + 2 * C * LV + VS * LK + 3 * C);
-    if ((e = set_lds_limit<TIn>((const void*)bwd_dstate_kernel<TIn>)) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dstate_kernel<TIn>, dim3(a.V / VS, a.H, a.B), dim3(kThreads), lds, stream,
-                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.d_o), a.alpha, a.beta, a.d_sfinal, a.d_s0, ws_F,
-                       ws_dS, a.T, a.H, a.K, a.V, C, VS);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t lds = sizeof(float) * (2 * C * LK + C * LV + 2 * C * C + 2 * C * LV + VS * LK + 3 * C);
+    auto run = [&](auto kc) -> hipError_t {
+      constexpr int KK = decltype(kc)::value;
+      hipError_t r;
+      if ((r = set_lds_limit<TIn>((const void*)bwd_dstate_kernel<TIn, KK>)) != hipSuccess) return r;
+      hipLaunchKernelGGL((bwd_dstate_kernel<TIn, KK>), dim3(a.V / VS, a.H, a.B), dim3(kThreads), lds,
+                         stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                         static_cast<const TIn*>(a.d_o), a.d_sfinal, a.d_s0, ws_F, ws_dS, a.T, a.H,
+                         a.V, C, VS);
+      return hipGetLastError();
+    };
+    if ((e = with_k(a.K, run)) != hipSuccess) return e;
   }
   // (3) token gradients
   {
     const size_t LK = a.K + 1, LV = kBwdVS + 1;
     const size_t lds = sizeof(float) * (2 * C * LK + 5 * C * C + 8 * C * LV + 2 * kBwdVS * LK + 5 * C + kThreads);
-    if ((e = set_lds_limit<TIn>((const void*)bwd_local_kernel<TIn>)) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_local_kernel<TIn>, dim3(NT, a.H, a.B), dim3(kThreads), lds, stream,
-                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.v), static_cast<const TIn*>(a.d_o), a.alpha,
-                       a.beta, ws_S, ws_dS, ws_F, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),
-                       static_cast<TIn*>(a.dv), a.dalpha, a.dbeta, a.T, a.H, a.K, a.V, C);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    auto run = [&](auto kc) -> hipError_t {
+      constexpr int KK = decltype(kc)::value;
+      hipError_t r;
+      if ((r = set_lds_limit<TIn>((const void*)bwd_local_kernel<TIn, KK>)) != hipSuccess) return r;
+      hipLaunchKernelGGL((bwd_local_kernel<TIn, KK>), dim3(NT, a.H, a.B), dim3(kThreads), lds, stream,
+                         static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                         static_cast<const TIn*>(a.v), static_cast<const TIn*>(a.d_o), a.alpha,
+                         a.beta, ws_S, ws_dS, ws_F, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),
+                         static_cast<TIn*>(a.dv), a.dalpha, a.dbeta, a.T, a.H, a.V, C);
+      return hipGetLastError();
+    };
+    if ((e = with_k(a.K, run)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
