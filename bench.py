@@ -93,7 +93,7 @@ def algorithmic_flops(B, T, H, K, V, C):
 
 
 def backward_flops(B, T, H, K, V, C):
-    """Structural fp32 FLOPs per call of the backward as built (backward chunk C):
+    """Structural FLOPs per call of the backward as built (backward chunk C):
     per token-head 22KV + 8CV + 9CK + C^2 (state recompute 4KV + CV + CK; reverse
     state-gradient walk 6KV + 2CV + 2CK; token gradients 12KV + 5CV + 6CK; three
     triangular solves)."""
@@ -145,19 +145,23 @@ def bench_backward(args):
         b.record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    bwd_c = min(C, 32)
+    # bf16 inputs with chunk >= 64 take the MFMA path (64-token chunks, bf16
+    # operands, fp32 accumulation); otherwise the fp32 path with 32-token chunks
+    mfma = w.dtype == torch.bfloat16 and C >= 64
+    bwd_c = 64 if mfma else min(C, 32)
     flops = backward_flops(B, T, H, K, V, bwd_c)
+    peak = 2500.0 if mfma else 157.3
     tok = B * T * H
     abytes = tok * (4 * K * 2 + 3 * K * 2 + 2 * 4 + 2 * 4) + B * H * V * K * 4  # q,k,v,dO,gates in; dq,dk,dv,dgates out; dS0
     print(json.dumps({
         "metric": "GDN chunk bwd tokens/s at B4\u00b7T2048\u00b7H6\u00b7d128",
         "value": B * T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16 in/out, f32 arithmetic", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16" if mfma else "f32", "data": "synthetic",
         "config": {"workload": "%s: B=%d T=%d H=%d K=%d V=%d chunk=%d (backward chunk %d)"
                                % (w.name, B, T, H, K, V, C, bwd_c)},
-        "roofline": {"bound": "alu", "achieved": flops / (ms / 1e3) / 1e12, "peak": 157.3,
-                     "unit": "TFLOP/s", "frac": flops / (ms / 1e3) / 1e12 / 157.3,
+        "roofline": {"bound": "mfma" if mfma else "alu", "achieved": flops / (ms / 1e3) / 1e12,
+                     "peak": peak, "unit": "TFLOP/s", "frac": flops / (ms / 1e3) / 1e12 / peak,
                      "traffic": None, "algorithmic_flops": flops,
                      "hbm_gbs_algorithmic": abytes / (ms / 1e3) / 1e9},
         "gate": gate,

@@ -1,0 +1,828 @@
+// Chunkwise gated-delta-rule backward for bfloat16 inputs on MFMA (gfx950).
+//
+// Same reverse mode as bwd.hip (the chunk algebra and its derivatives are
+// written out at the top of that file: "Sparse Delta Memory: layer and
+// kernels", section "What the layer computes"; operator contract of "OpenGDN
+// 0.1.0", section "Core operator reference"), with chunks of C = 64 tokens and
+// every matrix product on v_mfma_f32_16x16x32_bf16: bf16 operands, fp32
+// accumulation.  Elementwise work, the triangular solve and all reductions are
+// fp32.  Each output element has one writer and every sum a fixed order, so
+// results are bitwise reproducible.
+//
+// Launches:
+//   (1) the bf16 forward kernel writes the fp32 chunk-start states S_c;
+//   (2) prep, one workgroup per chunk: gates, the Gram matrices A = diag(beta) M
+//       and P, Tm = (I + A)^-1 by fp32 substitution; record = Tm, P, M (bf16)
+//       and the gates (fp32);
+//   (3) reverse walk, one workgroup per (stream, 16 value rows): the state
+//       gradient dS^T lives in MFMA accumulator tiles across chunks (like the
+//       forward's state); stores every chunk's end-state gradient dS'_c;
+//   (4) token gradients, one workgroup per chunk, fully parallel.
+//
+// Layout conventions of the products in (4): quantities with a token axis and
+// a value or channel axis are computed transposed (accumulator rows = value or
+// channel, columns = tokens), so per-token scalars are one value per lane and
+// the tiles go to LDS as row-major [token][*] with 8-byte writes; an operand
+// whose contraction runs over tokens is then read from such an array with
+// transpose reads.
+#include "launch.h"
+#include "mfma_common.h"
+
+#include <type_traits>
+
+namespace gdn {
+namespace {
+
+using namespace mfma;
+
+constexpr int kC = 64;          // backward chunk (tokens)
+constexpr int kLDC = kC + 8;    // row stride of C x C bf16 tiles in LDS
+// Per-chunk record: Tm, P, M as bf16 [C][C] row-major (M strictly lower, P
+// lower, Tm unit lower), then g (cumulative log2 gate) and beta as fp32 [C].
+// Padding tokens past a sequence's end have alpha = 1 and beta = 0.
+constexpr int kRecTm = 0, kRecP = kC * kC * 2, kRecM = 2 * kC * kC * 2;
+constexpr int kRecG = 3 * kC * kC * 2, kRecB = kRecG + kC * 4;
+constexpr int kRecBytes = kRecB + kC * 4;
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+
+// Eight bf16 <- eight fp32 (round to nearest even).
+__device__ __forceinline__ bf16x8 to_bf8(const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)x[j];
+  return r;
+}
+
+__device__ __forceinline__ void store_bf4(bf16* p, f32x4 d) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]};
+}
+
+// ===========================================================================
+// (2) prep: one workgroup (4 waves) per (chunk, head, batch).
+template <int KD>
+struct alignas(16) PrepSmem {
+  static constexpr int LDK = KD + 8;
+  bf16 k[kC * LDK], q[kC * LDK];   // [token][channel]
+  float a[kC][kC + 1];             // A = diag(beta) M, strictly lower
+  float x[kC][kC + 1];             // Tm, built column by column
+  bf16 out[3][kC * kC];            // Tm, P, M as they go to the record
+  float g[kC], bt[kC];
+};
+
+template <int KD>
+__global__ void __launch_bounds__(256)
+bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                  const float* __restrict__ alpha, const float* __restrict__ beta,
+                  unsigned char* __restrict__ rec, int T, int H) {
+  using SM = PrepSmem<KD>;
+  constexpr int LDK = SM::LDK;
+  constexpr int KS = KD / 32;
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int NT = (T + kC - 1) / kC;
+  const int t0 = c * kC, n = min(kC, T - t0);
+  const size_t tok = (size_t)H * KD;
+
+  // keys and queries (zero rows past the end), the output tiles zeroed
+  for (int p = tid; p < kC * KD / 8; p += 256) {
+    const int r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+    bf16x8 kv = zero8(), qv = zero8();
+    if (r < n) {
+      const size_t off = ((size_t)b * T + t0 + r) * tok + (size_t)h * KD + c8;
+      kv = *reinterpret_cast<const bf16x8*>(k + off);
+      qv = *reinterpret_cast<const bf16x8*>(q + off);
+    }
+    *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv;
+    *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv;
+  }
+  for (int p = tid; p < 3 * kC * kC / 8; p += 256)
+    *reinterpret_cast<bf16x8*>(&sm.out[0][0] + 8 * p) = zero8();
+  // gates: g = cumulative log2(alpha) by a wave scan; padding alpha = 1, beta = 0
+  if (wave == 0) {
+    const size_t go = ((size_t)b * T + t0 + lane) * H + h;
+    const float la = lane < n ? __builtin_amdgcn_logf(alpha[go]) : 0.0f;
+    sm.g[lane] = wave_scan(la, lane);
+    sm.bt[lane] = lane < n ? beta[go] : 0.0f;
+  }
+  __syncthreads();
+
+  // Gram tiles of row block w: A (strict) to fp32 LDS, M and P to bf16
+  {
+    const int w = wave, ls = lane & 15, lg = lane >> 4;
+    for (int tc = 0; tc <= w; ++tc) {
+      f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kc = frag_rows(sm.k, LDK, 16 * tc, 32 * ks, lane);
+        accA = mma(frag_rows(sm.k, LDK, 16 * w, 32 * ks, lane), kc, accA);
+        accP = mma(frag_rows(sm.q, LDK, 16 * w, 32 * ks, lane), kc, accP);
+      }
+      // accumulator: row r = 16 w + 4 lg + e, column i = 16 tc + ls
+      const int i = 16 * tc + ls;
+      const float gi = sm.g[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * lg + e;
+        const float dec = __builtin_amdgcn_exp2f(i <= r ? sm.g[r] - gi : -INFINITY);
+        const float m = i < r ? dec * accA[e] : 0.0f;
+        sm.a[r][i] = sm.bt[r] * m;
+        sm.out[2][r * kC + i] = (bf16)m;
+        sm.out[1][r * kC + i] = (bf16)(dec * accP[e]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Tm = (I + A)^-1, column j by forward substitution:
+  //   x_j = 1,  x_r = -sum_{j <= i < r} A[r][i] x_i  (r > j).
+  // Four lanes per column split each sum by i mod 4 and combine with two
+  // shuffles (fixed order); lane qq keeps the x_i with i = qq mod 4, which only
+  // it reads again.
+  {
+    const int j = tid >> 2, qq = tid & 3;
+    if ((j & 3) == qq) sm.x[j][j] = 1.0f;
+    const int i0 = j + ((qq - (j & 3)) & 3);
+    for (int r = j + 1; r < kC; ++r) {
+      float s = 0.0f;
+      for (int i = i0; i < r; i += 4) s = fmaf(sm.a[r][i], sm.x[i][j], s);
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if ((r & 3) == qq) sm.x[r][j] = -s;
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < kC * kC; p += 256) {
+    const int r = p / kC, jj = p % kC;
+    if (jj <= r) sm.out[0][p] = (bf16)sm.x[r][jj];
+  }
+  __syncthreads();
+  unsigned char* dst = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
+  for (int p = tid; p < 3 * kC * kC / 8; p += 256)
+    *reinterpret_cast<bf16x8*>(dst + 16 * p) = *reinterpret_cast<const bf16x8*>(&sm.out[0][0] + 8 * p);
+  if (tid < kC) {
+    reinterpret_cast<float*>(dst + kRecG)[tid] = sm.g[tid];
+    reinterpret_cast<float*>(dst + kRecB)[tid] = sm.bt[tid];
+  }
+}
+
+// ===========================================================================
+// (3) reverse walk: one workgroup per (value block of 16 rows, head, batch).
+// Wave 0 carries dS^T (tile cb: lane (g, s) holds dS[v0 + s][16 cb + 4g + e]);
+// waves 1..3 stage the next chunk (in reverse order) into the other LDS slot.
+// Per chunk with dS' the gradient of the chunk-end state:
+//   W = K dS'^T,  dU = diag(D) W + P^T dO,  dR = Tm^T dU,
+//   dS <- gam_n dS' + dO^T diag(gam) Q - dR^T diag(beta gam) K.
+constexpr int kLDV = 48;  // [token][16 values] rows of 96 bytes (transpose reads)
+
+template <int KD>
+struct alignas(16) WalkSlot {
+  static constexpr int LDK = KD + 8;
+  bf16 k[kC * LDK], q[kC * LDK];   // [token][channel]
+  bf16 tm[kC * kLDC], p[kC * kLDC];
+  bf16 dob[kC * kLDV], dog[kC * kLDV];  // dO and diag(gam) dO: [token][value]
+  float d[kC], nbg[kC];            // D_r = gam_n / gam_r,  -beta_r gam_r
+  float gamn[4];
+};
+
+template <int KD>
+__global__ void __launch_bounds__(256)
+bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                    const bf16* __restrict__ d_o, const float* __restrict__ d_sfinal,
+                    float* __restrict__ d_s0, const unsigned char* __restrict__ rec,
+                    float* __restrict__ ws_dS, int T, int H, int V) {
+  using SL = WalkSlot<KD>;
+  constexpr int LDK = SL::LDK;
+  constexpr int KS = KD / 32, NCB = KD / 16;
+  __shared__ SL slot[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ls = lane & 15, lg = lane >> 4;
+  const int v0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
+  const int NT = (T + kC - 1) / kC;
+  const size_t tokk = (size_t)H * KD, tokv = (size_t)H * V;
+  const size_t sbase = ((size_t)b * H + h) * (size_t)V * KD + (size_t)v0 * KD;
+  const unsigned char* rec_bh = rec + ((size_t)b * H + h) * NT * (size_t)kRecBytes;
+
+  if (wave == 0) {
+    // ============================== chain wave ==============================
+    f32x4 dS[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      dS[cb] = d_sfinal ? *reinterpret_cast<const f32x4*>(&d_sfinal[sbase + (size_t)ls * KD + 16 * cb + 4 * lg])
+                        : zero4();
+    for (int c = NT - 1; c >= 0; --c) {
+      lds_barrier();
+      const SL& sl = slot[c & 1];
+      float* dst = ws_dS + (((size_t)b * H + h) * NT + c) * (size_t)V * KD + (size_t)(v0 + ls) * KD + 4 * lg;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<f32x4*>(dst + 16 * cb) = dS[cb];
+      bf16x8 sbf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sbf[ks] = acc_pair_to_frag(dS[2 * ks], dS[2 * ks + 1]);
+      // W = K dS'^T and P^T dO  ->  dU
+      f32x4 dU[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 w = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) w = mma(frag_rows(sl.k, LDK, 16 * tb, 32 * ks, lane), sbf[ks], w);
+        f32x4 pd = zero4();
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs)
+          if (32 * cs + 31 >= 16 * tb)  // P^T is upper triangular
+            pd = mma(frag_cols(sl.p, kLDC, 16 * tb, 32 * cs, lane), frag_cols(sl.dob, kLDV, 0, 32 * cs, lane), pd);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(&sl.d[16 * tb + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dU[tb][e] = fmaf(dd[e], w[e], pd[e]);
+      }
+      bf16x8 duf[2];
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) duf[cs] = acc_pair_to_frag(dU[2 * cs], dU[2 * cs + 1]);
+      // dR = Tm^T dU, scaled by -beta gam for the update
+      f32x4 dR[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 r = zero4();
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs)
+          if (32 * cs + 31 >= 16 * tb) r = mma(frag_cols(sl.tm, kLDC, 16 * tb, 32 * cs, lane), duf[cs], r);
+        const f32x4 nb = *reinterpret_cast<const f32x4*>(&sl.nbg[16 * tb + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dR[tb][e] = nb[e] * r[e];
+      }
+      bf16x8 drf[2], gof[2];
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        drf[cs] = acc_pair_to_frag(dR[2 * cs], dR[2 * cs + 1]);
+        gof[cs] = frag_cols(sl.dog, kLDV, 0, 32 * cs, lane);
+      }
+      const float gamn = sl.gamn[0];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        f32x4 acc = dS[cb] * gamn;
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+          acc = mma(frag_cols(sl.q, LDK, 16 * cb, 32 * cs, lane), gof[cs], acc);
+          acc = mma(frag_cols(sl.k, LDK, 16 * cb, 32 * cs, lane), drf[cs], acc);
+        }
+        dS[cb] = acc;
+      }
+    }
+    if (d_s0)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        *reinterpret_cast<f32x4*>(&d_s0[sbase + (size_t)ls * KD + 16 * cb + 4 * lg]) = dS[cb];
+  } else {
+    // ============================= staging waves =============================
+    // Chunk c is loaded into registers one iteration before it is written to
+    // LDS; 192 staging lanes.
+    constexpr int NSL = 192;
+    constexpr int NKP = kC * KD / 8;              // 16-byte pieces of a key tile
+    constexpr int KPL = (NKP + NSL - 1) / NSL;
+    constexpr int NMP = kC * kC / 8;              // pieces of a C x C tile
+    constexpr int MPL = (NMP + NSL - 1) / NSL;
+    const int sl = tid - 64;
+    struct Regs {
+      bf16x8 k[KPL], q[KPL], tm[MPL], p[MPL], dof;
+      float g, gl, gn, bt;
+    };
+    auto load = [&](int c, Regs& R) {
+      const int t0 = c * kC, n = min(kC, T - t0);
+      const unsigned char* rc = rec_bh + (size_t)c * kRecBytes;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int p = sl + NSL * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+        R.k[j] = zero8();
+        R.q[j] = zero8();
+        if (p < NKP && r < n) {
+          const size_t off = ((size_t)b * T + t0 + r) * tokk + (size_t)h * KD + c8;
+          R.k[j] = *reinterpret_cast<const bf16x8*>(k + off);
+          R.q[j] = *reinterpret_cast<const bf16x8*>(q + off);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < MPL; ++j) {
+        const int p = sl + NSL * j;
+        if (p < NMP) {
+          R.tm[j] = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * p);
+          R.p[j] = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * p);
+        }
+      }
+      // dO piece: token sl / 2, values 8 (sl % 2) .. + 7 (128 pieces)
+      const int dr = sl >> 1;
+      R.dof = zero8();
+      R.g = 0.0f;
+      if (sl < 128) {
+        if (dr < n)
+          R.dof = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)b * T + t0 + dr) * tokv + (size_t)h * V + v0 + 8 * (sl & 1));
+        R.g = reinterpret_cast<const float*>(rc + kRecG)[dr];
+      }
+      // gates of token sl (first 64 lanes)
+      if (sl < kC) {
+        R.gl = reinterpret_cast<const float*>(rc + kRecG)[sl];
+        R.gn = reinterpret_cast<const float*>(rc + kRecG)[kC - 1];
+        R.bt = reinterpret_cast<const float*>(rc + kRecB)[sl];
+      }
+    };
+    auto stage = [&](int c, const Regs& R) {
+      SL& s = slot[c & 1];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int p = sl + NSL * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+        if (p < NKP) {
+          *reinterpret_cast<bf16x8*>(&s.k[r * LDK + c8]) = R.k[j];
+          *reinterpret_cast<bf16x8*>(&s.q[r * LDK + c8]) = R.q[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < MPL; ++j) {
+        const int p = sl + NSL * j, r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
+        if (p < NMP) {
+          *reinterpret_cast<bf16x8*>(&s.tm[r * kLDC + c8]) = R.tm[j];
+          *reinterpret_cast<bf16x8*>(&s.p[r * kLDC + c8]) = R.p[j];
+        }
+      }
+      if (sl < 128) {
+        const int dr = sl >> 1, c8 = 8 * (sl & 1);
+        const float gm = __builtin_amdgcn_exp2f(R.g);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = gm * bf2f(R.dof[j]);
+        *reinterpret_cast<bf16x8*>(&s.dob[dr * kLDV + c8]) = R.dof;
+        *reinterpret_cast<bf16x8*>(&s.dog[dr * kLDV + c8]) = to_bf8(x);
+      }
+      if (sl < kC) {
+        s.d[sl] = __builtin_amdgcn_exp2f(R.gn - R.gl);
+        s.nbg[sl] = -R.bt * __builtin_amdgcn_exp2f(R.gl);
+        if (sl == 0) s.gamn[0] = __builtin_amdgcn_exp2f(R.gn);
+      }
+    };
+    Regs R;
+    load(NT - 1, R);
+    stage(NT - 1, R);
+    if (NT >= 2) load(NT - 2, R);
+    for (int c = NT - 1; c >= 0; --c) {
+      lds_barrier();
+      if (c >= 1) {
+        stage(c - 1, R);
+        if (c >= 2) load(c - 2, R);
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// (4) token gradients: one workgroup (8 waves) per (chunk, head, batch).  The
+// value axis is walked in slices of VSL columns; dP, dA and the S / dS' parts
+// of dQ and dK accumulate in registers across slices.
+template <int KD, int VD>
+struct alignas(16) LocalSmem {
+  static constexpr int VSL = VD < 64 ? VD : 64;   // value slice
+  static constexpr int LDK = KD + 8, LDW = VSL + 8;
+  bf16 k[kC * LDK], q[kC * LDK];       // [token][channel]
+  bf16 tm[kC * kLDC], p[kC * kLDC];    // Tm, P [row][col]
+  union {
+    struct {
+      bf16 s[VSL * LDK], ds[VSL * LDK];  // slice rows of S and dS' [value][channel]
+      bf16 dob[kC * LDW];                // dO slice [token][value]
+      bf16 rb[kC * LDW], ub[kC * LDW], dub[kC * LDW], drb[kC * LDW];  // R, U, dU, dR [token][value]
+    } sl;
+    struct {
+      bf16 dpe[kC * kLDC], dae[kC * kLDC];  // (dP o E), (dA o beta E) [row][col]
+      bf16 m[kC * kLDC];                    // M [row][col]
+      float xp[kC][kC + 4], xa[kC][kC + 4]; // dP o P and dA o M, [row][col]
+    } fin;
+  } u;
+  float g[kC], bt[kC];
+  float red[4][16][16];                // per-token row sums of the slice tiles
+  float dgs[kC], dbs[kC];              // per-token gate gradients
+  float dot[8];                        // <dS', S> partials per wave
+};
+
+template <int KD, int VD>
+__global__ void __launch_bounds__(512)
+bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                   const bf16* __restrict__ v, const bf16* __restrict__ d_o,
+                   const float* __restrict__ alpha, const float* __restrict__ ws_S,
+                   const float* __restrict__ ws_dS, const unsigned char* __restrict__ rec,
+                   bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
+                   float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H) {
+  using SM = LocalSmem<KD, VD>;
+  constexpr int LDK = SM::LDK, LDW = SM::LDW, VSL = SM::VSL;
+  constexpr int KS = KD / 32, VKS = VSL / 32;
+  constexpr int NVB = VSL / 16;            // value blocks per slice
+  constexpr int NCB = KD / 16;             // channel blocks
+  constexpr int NST = NVB * 4 / 8;         // slice tiles (value block, token block) per wave
+  constexpr int NQT = NCB * 4 / 8;         // dQ / dK tiles per wave
+  static_assert(NST >= 1 && NQT >= 1, "shape too small for 8 waves");
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ls = lane & 15, lg = lane >> 4;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int NT = (T + kC - 1) / kC;
+  const int t0 = c * kC, n = min(kC, T - t0);
+  const size_t tokk = (size_t)H * KD, tokv = (size_t)H * VD;
+  const unsigned char* rc = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
+  const size_t ck = (((size_t)b * H + h) * NT + c) * (size_t)VD * KD;
+
+  // ---- chunk operands: keys, queries, Tm, P, gates
+  for (int p = tid; p < kC * KD / 8; p += 512) {
+    const int r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+    bf16x8 kv = zero8(), qv = zero8();
+    if (r < n) {
+      const size_t off = ((size_t)b * T + t0 + r) * tokk + (size_t)h * KD + c8;
+      kv = *reinterpret_cast<const bf16x8*>(k + off);
+      qv = *reinterpret_cast<const bf16x8*>(q + off);
+    }
+    *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv;
+    *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv;
+  }
+  for (int p = tid; p < kC * kC / 8; p += 512) {
+    const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&sm.tm[r * kLDC + c8]) = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * p);
+    *reinterpret_cast<bf16x8*>(&sm.p[r * kLDC + c8]) = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * p);
+  }
+  if (tid < kC) {
+    sm.g[tid] = reinterpret_cast<const float*>(rc + kRecG)[tid];
+    sm.bt[tid] = reinterpret_cast<const float*>(rc + kRecB)[tid];
+  }
+
+  // per-wave accumulators
+  // slice tiles: t = wave + 8 u -> value block t % NVB, token block t / NVB
+  float rs_oz[NST], rs_uw[NST], rs_db[NST], rs_ry[NST];   // per-lane row-sum partials
+#pragma unroll
+  for (int u = 0; u < NST; ++u) rs_oz[u] = rs_uw[u] = rs_db[u] = rs_ry[u] = 0.0f;
+  // dP^T / dA^T tiles: job j = wave + 8 u < 20 (10 upper (i, r) block pairs each)
+  f32x4 pa[3];
+#pragma unroll
+  for (int u = 0; u < 3; ++u) pa[u] = zero4();
+  // dQ^T / dK^T tiles: t = wave + 8 u -> channel block t % NCB, token block t / NCB
+  f32x4 aq[NQT], ak1[NQT], ak2[NQT];
+#pragma unroll
+  for (int u = 0; u < NQT; ++u) aq[u] = ak1[u] = ak2[u] = zero4();
+  float dot = 0.0f;
+
+  for (int vs0 = 0; vs0 < VD; vs0 += VSL) {
+    __syncthreads();
+    // ---- slice operands: S and dS' rows as bf16, dO slice
+    for (int p = tid; p < VSL * KD / 8; p += 512) {
+      const int r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+      const float* sp = ws_S + ck + (size_t)(vs0 + r) * KD + c8;
+      const float* dp = ws_dS + ck + (size_t)(vs0 + r) * KD + c8;
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sp), s1 = *reinterpret_cast<const f32x4*>(sp + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dp), d1 = *reinterpret_cast<const f32x4*>(dp + 4);
+      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const float dvv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dot = fmaf(dvv[j], sv[j], dot);
+      *reinterpret_cast<bf16x8*>(&sm.u.sl.s[r * LDK + c8]) = to_bf8(sv);
+      *reinterpret_cast<bf16x8*>(&sm.u.sl.ds[r * LDK + c8]) = to_bf8(dvv);
+    }
+    for (int p = tid; p < kC * VSL / 8; p += 512) {
+      const int r = p / (VSL / 8), c8 = (p % (VSL / 8)) * 8;
+      bf16x8 x = zero8();
+      if (r < n) x = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)b * T + t0 + r) * tokv + (size_t)h * VD + vs0 + c8);
+      *reinterpret_cast<bf16x8*>(&sm.u.sl.dob[r * LDW + c8]) = x;
+    }
+    __syncthreads();
+
+    // ---- (a) Y^T = S K^T, Z^T = S Q^T, W^T = dS' K^T; R^T = beta V^T - beta gam Y^T
+    f32x4 YT[NST], WT[NST], VT[NST];
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
+      f32x4 y = zero4(), z = zero4(), w = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 sa = frag_rows(sm.u.sl.s, LDK, 16 * vb, 32 * ks, lane);
+        const bf16x8 da = frag_rows(sm.u.sl.ds, LDK, 16 * vb, 32 * ks, lane);
+        const bf16x8 kb = frag_rows(sm.k, LDK, 16 * tb, 32 * ks, lane);
+        y = mma(sa, kb, y);
+        z = mma(sa, frag_rows(sm.q, LDK, 16 * tb, 32 * ks, lane), z);
+        w = mma(da, kb, w);
+      }
+      // lane: values vs0 + 16 vb + 4 lg + e, token tk = 16 tb + ls
+      const int tk = 16 * tb + ls;
+      const float gm = __builtin_amdgcn_exp2f(sm.g[tk]), bt = sm.bt[tk];
+      f32x4 vv = zero4();
+      if (tk < n) {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(v + ((size_t)b * T + t0 + tk) * tokv + (size_t)h * VD + vs0 + 16 * vb + 4 * lg);
+        vv = f32x4{bf2f(x[0]), bf2f(x[1]), bf2f(x[2]), bf2f(x[3])};
+      }
+      const bf16x4 ov = *reinterpret_cast<const bf16x4*>(&sm.u.sl.dob[tk * LDW + 16 * vb + 4 * lg]);
+      f32x4 r;
+      float oz = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r[e] = bt * vv[e] - bt * gm * y[e];
+        oz = fmaf(bf2f(ov[e]), z[e], oz);
+      }
+      rs_oz[u] += oz;
+      store_tile_t(sm.u.sl.rb, LDW, 16 * tb, 16 * vb, r, lane);
+      YT[u] = y;
+      WT[u] = w;
+      VT[u] = vv;
+    }
+    __syncthreads();
+    // ---- (b) U^T = R^T Tm^T,  dU^T = diag(D) W^T + dO^T P
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
+      f32x4 uu = zero4(), du = zero4();
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        if (32 * cs <= 16 * tb + 15)  // Tm lower
+          uu = mma(frag_cols(sm.u.sl.rb, LDW, 16 * vb, 32 * cs, lane), frag_rows(sm.tm, kLDC, 16 * tb, 32 * cs, lane), uu);
+        if (32 * cs + 31 >= 16 * tb)  // P lower: rows r >= i
+          du = mma(frag_cols(sm.u.sl.dob, LDW, 16 * vb, 32 * cs, lane), frag_cols(sm.p, kLDC, 16 * tb, 32 * cs, lane), du);
+      }
+      const int tk = 16 * tb + ls;
+      const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[tk]);
+      float uw = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        du[e] = fmaf(dd, WT[u][e], du[e]);
+        uw = fmaf(uu[e], WT[u][e], uw);
+      }
+      rs_uw[u] += uw;
+      store_tile_t(sm.u.sl.ub, LDW, 16 * tb, 16 * vb, uu, lane);
+      store_tile_t(sm.u.sl.dub, LDW, 16 * tb, 16 * vb, du, lane);
+    }
+    __syncthreads();
+    // ---- (c) dR^T = dU^T Tm;  dV = diag(beta) dR
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
+      f32x4 dr = zero4();
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs)
+        if (32 * cs + 31 >= 16 * tb)  // Tm[i][r] with i >= r
+          dr = mma(frag_cols(sm.u.sl.dub, LDW, 16 * vb, 32 * cs, lane), frag_cols(sm.tm, kLDC, 16 * tb, 32 * cs, lane), dr);
+      const int tk = 16 * tb + ls;
+      const float gm = __builtin_amdgcn_exp2f(sm.g[tk]), bt = sm.bt[tk];
+      float db = 0.0f, ry = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        db = fmaf(dr[e], VT[u][e] - gm * YT[u][e], db);
+        ry = fmaf(dr[e], YT[u][e], ry);
+      }
+      rs_db[u] += db;
+      rs_ry[u] += ry;
+      if (tk < n) store_bf4(dv + ((size_t)b * T + t0 + tk) * tokv + (size_t)h * VD + vs0 + 16 * vb + 4 * lg, dr * bt);
+      store_tile_t(sm.u.sl.drb, LDW, 16 * tb, 16 * vb, dr, lane);
+    }
+    __syncthreads();
+    // ---- (d) dP^T += U dO^T,  dA^T -= U dR^T   (upper (i, r) blocks, i <= r)
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int j = wave + 8 * u;
+      if (j < 20) {
+        const int jt = j % 10;
+        const int rbk = jt < 1 ? 0 : (jt < 3 ? 1 : (jt < 6 ? 2 : 3));   // r block
+        const int ibk = jt - rbk * (rbk + 1) / 2;                        // i block <= r block
+        const bf16* bsrc = j < 10 ? sm.u.sl.dob : sm.u.sl.drb;
+#pragma unroll
+        for (int ks = 0; ks < VKS; ++ks)
+          pa[u] = mma(frag_rows(sm.u.sl.ub, LDW, 16 * ibk, 32 * ks, lane), frag_rows(bsrc, LDW, 16 * rbk, 32 * ks, lane), pa[u]);
+      }
+    }
+    // ---- (e) dQ^T += S^T dO^T,  dK^T += dS'^T U^T (part 1), S^T dR^T (part 2)
+#pragma unroll
+    for (int u = 0; u < NQT; ++u) {
+      const int t = wave + 8 * u, cb = t % NCB, tb = t / NCB;
+#pragma unroll
+      for (int ks = 0; ks < VKS; ++ks) {
+        const bf16x8 st = frag_cols(sm.u.sl.s, LDK, 16 * cb, 32 * ks, lane);
+        aq[u] = mma(st, frag_rows(sm.u.sl.dob, LDW, 16 * tb, 32 * ks, lane), aq[u]);
+        ak1[u] = mma(frag_cols(sm.u.sl.ds, LDK, 16 * cb, 32 * ks, lane), frag_rows(sm.u.sl.ub, LDW, 16 * tb, 32 * ks, lane), ak1[u]);
+        ak2[u] = mma(st, frag_rows(sm.u.sl.drb, LDW, 16 * tb, 32 * ks, lane), ak2[u]);
+      }
+    }
+  }
+  // per-token row sums of the slice tiles: reduce over the four lane groups
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    float x[4] = {rs_oz[u], rs_uw[u], rs_db[u], rs_ry[u]};
+#pragma unroll
+    for (int qn = 0; qn < 4; ++qn) {
+      x[qn] += __shfl_xor(x[qn], 16);
+      x[qn] += __shfl_xor(x[qn], 32);
+    }
+    const int t = wave + 8 * u;
+    if (lg == 0)
+#pragma unroll
+      for (int qn = 0; qn < 4; ++qn) sm.red[qn][t][ls] = x[qn];
+  }
+  // <dS', S>: wave partial
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+  if (lane == 0) sm.dot[wave] = dot;
+  __syncthreads();   // every slice array is dead from here
+
+  // ---- (f) dP o E, dA o beta E to LDS (bf16, [r][i]); dP o P and dA o M (fp32)
+  for (int p = tid; p < kC * kC / 8; p += 512) {
+    const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&sm.u.fin.m[r * kLDC + c8]) = *reinterpret_cast<const bf16x8*>(rc + kRecM + 16 * p);
+  }
+  for (int p = tid; p < kC * kC / 8; p += 512) {   // zero the tiles no job writes
+    const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&sm.u.fin.dpe[r * kLDC + c8]) = zero8();
+    *reinterpret_cast<bf16x8*>(&sm.u.fin.dae[r * kLDC + c8]) = zero8();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int j = wave + 8 * u;
+    if (j < 20) {
+      const int jt = j % 10;
+      const int rbk = jt < 1 ? 0 : (jt < 3 ? 1 : (jt < 6 ? 2 : 3));
+      const int ibk = jt - rbk * (rbk + 1) / 2;
+      // lane: i = 16 ibk + 4 lg + e, r = 16 rbk + ls
+      const int r = 16 * rbk + ls;
+      const float gr = sm.g[r], br = sm.bt[r];
+      f32x4 val, prod;
+      if (j < 10) {
+        const bf16x4 pv = *reinterpret_cast<const bf16x4*>(&sm.p[r * kLDC + 16 * ibk + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * ibk + 4 * lg + e;
+          const float ee = __builtin_amdgcn_exp2f(i <= r ? gr - sm.g[i] : -INFINITY);
+          const float dp = i <= r ? pa[u][e] : 0.0f;
+          val[e] = dp * ee;
+          prod[e] = dp * bf2f(pv[e]);
+        }
+        store_tile_t(sm.u.fin.dpe, kLDC, 16 * rbk, 16 * ibk, val, lane);
+        *reinterpret_cast<f32x4*>(&sm.u.fin.xp[r][16 * ibk + 4 * lg]) = prod;
+      } else {
+        const bf16x4 mv = *reinterpret_cast<const bf16x4*>(&sm.u.fin.m[r * kLDC + 16 * ibk + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * ibk + 4 * lg + e;
+          const float ee = __builtin_amdgcn_exp2f(i < r ? gr - sm.g[i] : -INFINITY);
+          const float da = i < r ? -pa[u][e] : 0.0f;
+          val[e] = da * br * ee;
+          prod[e] = da * bf2f(mv[e]);
+        }
+        store_tile_t(sm.u.fin.dae, kLDC, 16 * rbk, 16 * ibk, val, lane);
+        *reinterpret_cast<f32x4*>(&sm.u.fin.xa[r][16 * ibk + 4 * lg]) = prod;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- (g) dQ^T = diag(gam) S^T dO^T + K^T (dP o E)^T
+  //          dK^T = D dS'^T U^T - beta gam S^T dR^T + Q^T (dP o E) + K^T (dA o bE)^T + K^T (dA o bE)
+#pragma unroll
+  for (int u = 0; u < NQT; ++u) {
+    const int t = wave + 8 * u, cb = t % NCB, tb = t / NCB;
+    const int tk = 16 * tb + ls;
+    const float gm = __builtin_amdgcn_exp2f(sm.g[tk]);
+    const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[tk]);
+    const float bg = sm.bt[tk] * gm;
+    f32x4 xq = aq[u] * gm;
+    f32x4 xk = ak1[u] * dd - ak2[u] * bg;
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      const bf16x8 kt = frag_cols(sm.k, LDK, 16 * cb, 32 * cs, lane);
+      if (32 * cs <= 16 * tb + 15) {   // (dP o E)[t][i], (dA o bE)[t][i]: i <= t
+        xq = mma(kt, frag_rows(sm.u.fin.dpe, kLDC, 16 * tb, 32 * cs, lane), xq);
+        xk = mma(kt, frag_rows(sm.u.fin.dae, kLDC, 16 * tb, 32 * cs, lane), xk);
+      }
+      if (32 * cs + 31 >= 16 * tb) {   // (dP o E)[r][t], (dA o bE)[r][t]: r >= t
+        xk = mma(frag_cols(sm.q, LDK, 16 * cb, 32 * cs, lane), frag_cols(sm.u.fin.dpe, kLDC, 16 * tb, 32 * cs, lane), xk);
+        xk = mma(kt, frag_cols(sm.u.fin.dae, kLDC, 16 * tb, 32 * cs, lane), xk);
+      }
+    }
+    if (tk < n) {
+      const size_t off = ((size_t)b * T + t0 + tk) * tokk + (size_t)h * KD + 16 * cb + 4 * lg;
+      store_bf4(dq + off, xq);
+      store_bf4(dk + off, xk);
+    }
+  }
+  // ---- (h) per-token gate gradients (one lane per token, fixed order)
+  if (tid < kC) {
+    const int r = tid, tb = r / 16, s = r % 16;
+    float oz = 0.0f, uw = 0.0f, db = 0.0f, ry = 0.0f;
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      oz += sm.red[0][tb * NVB + vb][s];
+      uw += sm.red[1][tb * NVB + vb][s];
+      db += sm.red[2][tb * NVB + vb][s];
+      ry += sm.red[3][tb * NVB + vb][s];
+    }
+    const float gm = __builtin_amdgcn_exp2f(sm.g[r]), br = sm.bt[r];
+    const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[r]);
+    float sp = 0.0f, sa = 0.0f;
+    for (int i = 0; i <= r; ++i) {
+      sp += sm.u.fin.xp[r][i];
+      sa += sm.u.fin.xa[r][i];
+    }
+    float cp = 0.0f, ca = 0.0f;
+    for (int rr = r; rr < kC; ++rr) {
+      cp += sm.u.fin.xp[rr][r];
+      ca += sm.bt[rr] * sm.u.fin.xa[rr][r];
+    }
+    float dg = gm * oz - br * gm * ry - dd * uw + (sp - cp) + (br * sa - ca);
+    const float du = dd * uw;
+    // the chunk-end terms go to the last real token
+    float esum = du;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);  // tokens >= n add zeros
+    float dsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) dsum += sm.dot[w];
+    if (r == n - 1) dg += __builtin_amdgcn_exp2f(sm.g[kC - 1]) * dsum + esum;
+    sm.dgs[r] = dg;
+    sm.dbs[r] = db + sa;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.0f;  // d ln alpha_t = sum_{t <= r < n} dg_r
+    for (int r = n - 1; r >= 0; --r) {
+      acc += sm.dgs[r];
+      const size_t go = ((size_t)b * T + t0 + r) * H + h;
+      dalpha[go] = acc / alpha[go];
+      dbeta[go] = sm.dbs[r];
+    }
+  }
+}
+
+template <typename F>
+hipError_t with_kd(int K, F&& f) {
+  switch (K) {
+    case 32: return f(std::integral_constant<int, 32>());
+    case 64: return f(std::integral_constant<int, 64>());
+    case 128: return f(std::integral_constant<int, 128>());
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool bwd_bf16_supported(int K, int V, int chunk) {
+  return chunk >= kC && (K == 32 || K == 64 || K == 128) && (V == 32 || V == 64 || V == 128);
+}
+
+size_t bwd_bf16_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
+  const int64_t NT = (T + kC - 1) / kC;
+  return (size_t)(2 * B * H * NT * V * K * 4 + B * H * NT * (int64_t)kRecBytes);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  if (!bwd_bf16_supported(a.K, a.V, a.chunk)) return hipErrorInvalidValue;
+  const int NT = (a.T + kC - 1) / kC;
+  float* ws_S = a.workspace;
+  float* ws_dS = ws_S + (size_t)a.B * a.H * NT * a.V * a.K;
+  unsigned char* rec = reinterpret_cast<unsigned char*>(ws_dS + (size_t)a.B * a.H * NT * a.V * a.K);
+  hipError_t e;
+  // (1) chunk-start states
+  FwdArgs f;
+  f.q = a.q;
+  f.k = a.k;
+  f.v = a.v;
+  f.alpha = a.alpha;
+  f.beta = a.beta;
+  f.s0 = a.s0;
+  f.o = nullptr;
+  f.s_final = nullptr;
+  f.B = a.B;
+  f.T = a.T;
+  f.H = a.H;
+  f.K = a.K;
+  f.V = a.V;
+  f.chunk = kC;
+  if ((e = launch_fwd_states(f, true, ws_S, stream)) != hipSuccess) return e;
+  const bf16* q = static_cast<const bf16*>(a.q);
+  const bf16* k = static_cast<const bf16*>(a.k);
+  const bf16* v = static_cast<const bf16*>(a.v);
+  const bf16* d_o = static_cast<const bf16*>(a.d_o);
+  auto run = [&](auto kc) -> hipError_t {
+    constexpr int KD = decltype(kc)::value;
+    hipLaunchKernelGGL((bwd16_prep_kernel<KD>), dim3(NT, a.H, a.B), dim3(256), 0, stream, q, k, a.alpha,
+                       a.beta, rec, a.T, a.H);
+    hipError_t r;
+    if ((r = hipGetLastError()) != hipSuccess) return r;
+    hipLaunchKernelGGL((bwd16_dstate_kernel<KD>), dim3(a.V / 16, a.H, a.B), dim3(256), 0, stream, q, k,
+                       d_o, a.d_sfinal, a.d_s0, rec, ws_dS, a.T, a.H, a.V);
+    if ((r = hipGetLastError()) != hipSuccess) return r;
+    auto local = [&](auto vc) -> hipError_t {
+      constexpr int VD = decltype(vc)::value;
+      hipLaunchKernelGGL((bwd16_local_kernel<KD, VD>), dim3(NT, a.H, a.B), dim3(512), 0, stream, q, k, v,
+                         d_o, a.alpha, ws_S, ws_dS, rec, static_cast<bf16*>(a.dq), static_cast<bf16*>(a.dk),
+                         static_cast<bf16*>(a.dv), a.dalpha, a.dbeta, a.T, a.H);
+      return hipGetLastError();
+    };
+    switch (a.V) {
+      case 32: return local(std::integral_constant<int, 32>());
+      case 64: return local(std::integral_constant<int, 64>());
+      case 128: return local(std::integral_constant<int, 128>());
+    }
+    return hipErrorInvalidValue;
+  };
+  return with_kd(a.K, run);
+}
+
+}  // namespace gdn
