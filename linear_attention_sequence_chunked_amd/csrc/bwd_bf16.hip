@@ -64,9 +64,8 @@ template <int KD>
 struct alignas(16) PrepSmem {
   static constexpr int LDK = KD + 8;
   bf16 k[kC * LDK], q[kC * LDK];   // [token][channel]
-  float a[kC][kC + 1];             // A = diag(beta) M, strictly lower
-  float x[kC][kC + 1];             // Tm, built column by column
-  bf16 out[3][kC * kC];            // Tm, P, M as they go to the record
+  float a[kC][kC + 4];             // A = diag(beta) M, strictly lower
+  float x[kC][kC + 4];             // Tm (lower); upper blocks hold level scratch
   float g[kC], bt[kC];
 };
 
@@ -85,8 +84,12 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int NT = (T + kC - 1) / kC;
   const int t0 = c * kC, n = min(kC, T - t0);
   const size_t tok = (size_t)H * KD;
+  unsigned char* dst = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
+  bf16* rtm = reinterpret_cast<bf16*>(dst + kRecTm);
+  bf16* rp = reinterpret_cast<bf16*>(dst + kRecP);
+  bf16* rm = reinterpret_cast<bf16*>(dst + kRecM);
 
-  // keys and queries (zero rows past the end), the output tiles zeroed
+  // keys and queries (zero rows past the end)
   for (int p = tid; p < kC * KD / 8; p += 256) {
     const int r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
     bf16x8 kv = zero8(), qv = zero8();
@@ -98,27 +101,33 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv;
     *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv;
   }
-  for (int p = tid; p < 3 * kC * kC / 8; p += 256)
-    *reinterpret_cast<bf16x8*>(&sm.out[0][0] + 8 * p) = zero8();
   // gates: g = cumulative log2(alpha) by a wave scan; padding alpha = 1, beta = 0
   if (wave == 0) {
     const size_t go = ((size_t)b * T + t0 + lane) * H + h;
     const float la = lane < n ? __builtin_amdgcn_logf(alpha[go]) : 0.0f;
-    sm.g[lane] = wave_scan(la, lane);
-    sm.bt[lane] = lane < n ? beta[go] : 0.0f;
+    const float g = wave_scan(la, lane);
+    const float bt = lane < n ? beta[go] : 0.0f;
+    sm.g[lane] = g;
+    sm.bt[lane] = bt;
+    reinterpret_cast<float*>(dst + kRecG)[lane] = g;
+    reinterpret_cast<float*>(dst + kRecB)[lane] = bt;
   }
   __syncthreads();
 
-  // Gram tiles of row block w: A (strict) to fp32 LDS, M and P to bf16
+  // Gram tiles of row block w: A (strict) to fp32 LDS; M and P to the record
+  // (tiles above the diagonal as zeros)
+  const int ls = lane & 15, lg = lane >> 4;
   {
-    const int w = wave, ls = lane & 15, lg = lane >> 4;
-    for (int tc = 0; tc <= w; ++tc) {
+    const int w = wave;
+    for (int tc = 0; tc < 4; ++tc) {
       f32x4 accA = zero4(), accP = zero4();
+      if (tc <= w) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kc = frag_rows(sm.k, LDK, 16 * tc, 32 * ks, lane);
-        accA = mma(frag_rows(sm.k, LDK, 16 * w, 32 * ks, lane), kc, accA);
-        accP = mma(frag_rows(sm.q, LDK, 16 * w, 32 * ks, lane), kc, accP);
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 kc = frag_rows(sm.k, LDK, 16 * tc, 32 * ks, lane);
+          accA = mma(frag_rows(sm.k, LDK, 16 * w, 32 * ks, lane), kc, accA);
+          accP = mma(frag_rows(sm.q, LDK, 16 * w, 32 * ks, lane), kc, accP);
+        }
       }
       // accumulator: row r = 16 w + 4 lg + e, column i = 16 tc + ls
       const int i = 16 * tc + ls;
@@ -129,42 +138,61 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const float dec = __builtin_amdgcn_exp2f(i <= r ? sm.g[r] - gi : -INFINITY);
         const float m = i < r ? dec * accA[e] : 0.0f;
         sm.a[r][i] = sm.bt[r] * m;
-        sm.out[2][r * kC + i] = (bf16)m;
-        sm.out[1][r * kC + i] = (bf16)(dec * accP[e]);
+        rm[r * kC + i] = (bf16)m;
+        rp[r * kC + i] = (bf16)(dec * accP[e]);
       }
     }
   }
   __syncthreads();
 
-  // Tm = (I + A)^-1, column j by forward substitution:
-  //   x_j = 1,  x_r = -sum_{j <= i < r} A[r][i] x_i  (r > j).
-  // Four lanes per column split each sum by i mod 4 and combine with two
-  // shuffles (fixed order); lane qq keeps the x_i with i = qq mod 4, which only
-  // it reads again.
-  {
-    const int j = tid >> 2, qq = tid & 3;
-    if ((j & 3) == qq) sm.x[j][j] = 1.0f;
-    const int i0 = j + ((qq - (j & 3)) & 3);
-    for (int r = j + 1; r < kC; ++r) {
+  // Tm = (I + A)^-1 in fp32, by 16 x 16 blocks.
+  // Diagonal blocks by forward substitution, one lane per (block, column):
+  //   x_j = 1, x_r = -sum_{j <= i < r} A[r][i] x_i.
+  if (wave == 0) {
+    const int bb = lg, j = 16 * bb + ls;
+    float xv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = 16 * bb + r;
       float s = 0.0f;
-      for (int i = i0; i < r; i += 4) s = fmaf(sm.a[r][i], sm.x[i][j], s);
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      if ((r & 3) == qq) sm.x[r][j] = -s;
+#pragma unroll
+      for (int i = 0; i < r; ++i) s = fmaf(sm.a[rr][16 * bb + i], xv[i], s);
+      xv[r] = rr < j ? 0.0f : (rr == j ? 1.0f : -s);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.x[16 * bb + r][j] = xv[r];
+  }
+  __syncthreads();
+  // Off-diagonal blocks by levels d = i - j: X_ij = -T_ii (sum_{j <= m < i} A_im T_mj).
+  // Step one puts the inner sum into the (j, i) block above the diagonal
+  // (scratch); step two multiplies by the diagonal block.  One element per
+  // thread per block.
+  {
+    const int er = tid >> 4, ec = tid & 15;   // element of a 16 x 16 block
+    for (int d = 1; d < 4; ++d) {
+      for (int j = 0; j + d < 4; ++j) {
+        const int i = j + d;
+        float s = 0.0f;
+        for (int m = 16 * j; m < 16 * i; ++m) s = fmaf(sm.a[16 * i + er][m], sm.x[m][16 * j + ec], s);
+        sm.x[16 * j + er][16 * i + ec] = s;   // scratch in the upper (j, i) block
+      }
+      __syncthreads();
+      for (int j = 0; j + d < 4; ++j) {
+        const int i = j + d;
+        float s = 0.0f;
+        for (int m = 0; m <= er; ++m) s = fmaf(sm.x[16 * i + er][16 * i + m], sm.x[16 * j + m][16 * i + ec], s);
+        sm.x[16 * i + er][16 * j + ec] = -s;
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
-  for (int p = tid; p < kC * kC; p += 256) {
-    const int r = p / kC, jj = p % kC;
-    if (jj <= r) sm.out[0][p] = (bf16)sm.x[r][jj];
-  }
-  __syncthreads();
-  unsigned char* dst = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
-  for (int p = tid; p < 3 * kC * kC / 8; p += 256)
-    *reinterpret_cast<bf16x8*>(dst + 16 * p) = *reinterpret_cast<const bf16x8*>(&sm.out[0][0] + 8 * p);
-  if (tid < kC) {
-    reinterpret_cast<float*>(dst + kRecG)[tid] = sm.g[tid];
-    reinterpret_cast<float*>(dst + kRecB)[tid] = sm.bt[tid];
+  // Tm to the record as bf16, zeros above the diagonal
+  for (int p = tid; p < kC * kC / 8; p += 256) {
+    const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
+    float xr[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) xr[jj] = c8 + jj <= r ? sm.x[r][c8 + jj] : 0.0f;
+    *reinterpret_cast<bf16x8*>(rtm + 8 * p) = to_bf8(xr);
   }
 }
 
