@@ -209,10 +209,15 @@ GDN_API gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v
 
 /*
  * gdn_chunk_bwd_workspace_size -- bytes of device workspace gdn_chunk_bwd needs
- * for these sizes.  Per (batch, head, backward chunk of C = min(chunk, 32)
- * tokens) it holds two float32 [V, K] states and the chunk's float32 factors
- * (three C x C matrices and three C-vectors):
+ * for these sizes, whatever the dtype: the larger of two layouts.  The float32
+ * path keeps, per (batch, head, backward chunk of C = min(chunk, 32) tokens), two
+ * float32 [V, K] states and the chunk's float32 factors (three C x C matrices and
+ * three C-vectors):
  *     B * H * ceil(T / C) * (2 * V * K + 3 * C * C + 3 * C) * 4 bytes.
+ * When chunk >= 64 and K, V are 32, 64 or 128, bfloat16 inputs take the MFMA path
+ * with 64-token chunks: per (batch, head, chunk) two float32 [V, K] states and a
+ * 25088-byte record (three bf16 64 x 64 matrices, two float32 64-vectors):
+ *     B * H * ceil(T / 64) * (2 * V * K * 4 + 25088) bytes.
  * Returns 0 when a size is not positive.
  */
 GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K,
@@ -240,8 +245,11 @@ GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int
  * "OpenGDN 0.1.0", section "Core operator reference" (backward from recomputed
  * fp32 chunk-boundary states) and "Sparse Delta Memory: layer and kernels",
  * sections "What the layer computes" and "Execution" (the backward walks the
- * chunks in reverse).  All arithmetic is float32 in a fixed order, so results
- * are bitwise reproducible; dq, dk, dv are rounded to dtype once.  No output may
+ * chunks in reverse).  Float32 inputs: all arithmetic float32.  Bfloat16 inputs
+ * with chunk >= 64 and K, V in {32, 64, 128}: 64-token chunks, matrix products
+ * on bf16 MFMA with bf16 operands and float32 accumulation, everything else
+ * float32 (other bf16 shapes: the float32 path).  Every sum has a fixed order,
+ * so results are bitwise reproducible; dq, dk, dv are rounded to dtype once.  No output may
  * overlap any other buffer (inputs, other outputs, workspace).  Errors as for
  * gdn_chunk_fwd; a workspace smaller than required is GDN_ERROR_INVALID_VALUE.
  */

@@ -408,7 +408,7 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // of dQ and dK accumulate in registers across slices.
 template <int KD, int VD>
 struct alignas(16) LocalSmem {
-  static constexpr int VSL = VD < 64 ? VD : 64;   // value slice
+  static constexpr int VSL = 32;                    // value slice
   static constexpr int LDK = KD + 8, LDW = VSL + 8;
   bf16 k[kC * LDK], q[kC * LDK];       // [token][channel]
   bf16 tm[kC * kLDC], p[kC * kLDC];    // Tm, P [row][col]
@@ -457,26 +457,110 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const unsigned char* rc = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
   const size_t ck = (((size_t)b * H + h) * NT + c) * (size_t)VD * KD;
 
-  // ---- chunk operands: keys, queries, Tm, P, gates
-  for (int p = tid; p < kC * KD / 8; p += 512) {
-    const int r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
-    bf16x8 kv = zero8(), qv = zero8();
-    if (r < n) {
-      const size_t off = ((size_t)b * T + t0 + r) * tokk + (size_t)h * KD + c8;
-      kv = *reinterpret_cast<const bf16x8*>(k + off);
-      qv = *reinterpret_cast<const bf16x8*>(q + off);
+  // ---- slice operands travel through registers, so the next slice is
+  // requested while the current one is computed: S and dS' pieces (fp32), dO
+  // pieces, and the V values of this wave's tiles
+  constexpr int SP = VSL * KD / 8, SPL = (SP + 511) / 512;
+  constexpr int OP = kC * VSL / 8, OPL = (OP + 511) / 512;
+  struct SliceRegs {
+    f32x4 s[SPL][2], d[SPL][2];
+    bf16x8 o[OPL];
+    bf16x4 v[NST];
+  };
+  auto load_slice = [&](int vs0, SliceRegs& R) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+      if (p < SP) {
+        const float* sp = ws_S + ck + (size_t)(vs0 + r) * KD + c8;
+        const float* dp = ws_dS + ck + (size_t)(vs0 + r) * KD + c8;
+        R.s[j][0] = *reinterpret_cast<const f32x4*>(sp);
+        R.s[j][1] = *reinterpret_cast<const f32x4*>(sp + 4);
+        R.d[j][0] = *reinterpret_cast<const f32x4*>(dp);
+        R.d[j][1] = *reinterpret_cast<const f32x4*>(dp + 4);
+      }
     }
-    *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv;
-    *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv;
-  }
-  for (int p = tid; p < kC * kC / 8; p += 512) {
-    const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(&sm.tm[r * kLDC + c8]) = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * p);
-    *reinterpret_cast<bf16x8*>(&sm.p[r * kLDC + c8]) = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * p);
-  }
-  if (tid < kC) {
-    sm.g[tid] = reinterpret_cast<const float*>(rc + kRecG)[tid];
-    sm.bt[tid] = reinterpret_cast<const float*>(rc + kRecB)[tid];
+#pragma unroll
+    for (int j = 0; j < OPL; ++j) {
+      const int p = tid + 512 * j, r = p / (VSL / 8), c8 = (p % (VSL / 8)) * 8;
+      R.o[j] = zero8();
+      if (p < OP && r < n)
+        R.o[j] = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)b * T + t0 + r) * tokv + (size_t)h * VD + vs0 + c8);
+    }
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int t = wave + 8 * u, vb = t % NVB, tk = 16 * (t / NVB) + ls;
+      const bf16 z = (bf16)0.0f;
+      R.v[u] = bf16x4{z, z, z, z};
+      if (tk < n)
+        R.v[u] = *reinterpret_cast<const bf16x4*>(v + ((size_t)b * T + t0 + tk) * tokv + (size_t)h * VD + vs0 + 16 * vb + 4 * lg);
+    }
+  };
+  float dot = 0.0f;   // <dS', S> partial
+  auto stage_slice = [&](const SliceRegs& R) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+      if (p < SP) {
+        const float sv[8] = {R.s[j][0][0], R.s[j][0][1], R.s[j][0][2], R.s[j][0][3],
+                             R.s[j][1][0], R.s[j][1][1], R.s[j][1][2], R.s[j][1][3]};
+        const float dvv[8] = {R.d[j][0][0], R.d[j][0][1], R.d[j][0][2], R.d[j][0][3],
+                              R.d[j][1][0], R.d[j][1][1], R.d[j][1][2], R.d[j][1][3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf(dvv[e], sv[e], dot);
+        *reinterpret_cast<bf16x8*>(&sm.u.sl.s[r * LDK + c8]) = to_bf8(sv);
+        *reinterpret_cast<bf16x8*>(&sm.u.sl.ds[r * LDK + c8]) = to_bf8(dvv);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < OPL; ++j) {
+      const int p = tid + 512 * j, r = p / (VSL / 8), c8 = (p % (VSL / 8)) * 8;
+      if (p < OP) *reinterpret_cast<bf16x8*>(&sm.u.sl.dob[r * LDW + c8]) = R.o[j];
+    }
+  };
+  SliceRegs R;
+  load_slice(0, R);
+
+  // ---- chunk operands: keys, queries, Tm, P, gates (all requested before any
+  // LDS write); M is kept in registers for the last phase
+  bf16x8 mreg;
+  {
+    constexpr int KP = kC * KD / 8, KPL = (KP + 511) / 512;
+    bf16x8 kv[KPL], qv[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+      kv[j] = qv[j] = zero8();
+      if (p < KP && r < n) {
+        const size_t off = ((size_t)b * T + t0 + r) * tokk + (size_t)h * KD + c8;
+        kv[j] = *reinterpret_cast<const bf16x8*>(k + off);
+        qv[j] = *reinterpret_cast<const bf16x8*>(q + off);
+      }
+    }
+    static_assert(kC * kC / 8 == 512, "one C x C piece per thread");
+    const bf16x8 tv = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * tid);
+    const bf16x8 pv = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * tid);
+    mreg = *reinterpret_cast<const bf16x8*>(rc + kRecM + 16 * tid);
+    float gv = 0.0f, bv = 0.0f;
+    if (tid < kC) {
+      gv = reinterpret_cast<const float*>(rc + kRecG)[tid];
+      bv = reinterpret_cast<const float*>(rc + kRecB)[tid];
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+      if (p < KP) {
+        *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv[j];
+        *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv[j];
+      }
+    }
+    const int r = tid / (kC / 8), c8 = (tid % (kC / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&sm.tm[r * kLDC + c8]) = tv;
+    *reinterpret_cast<bf16x8*>(&sm.p[r * kLDC + c8]) = pv;
+    if (tid < kC) {
+      sm.g[tid] = gv;
+      sm.bt[tid] = bv;
+    }
   }
 
   // per-wave accumulators
@@ -492,30 +576,14 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   f32x4 aq[NQT], ak1[NQT], ak2[NQT];
 #pragma unroll
   for (int u = 0; u < NQT; ++u) aq[u] = ak1[u] = ak2[u] = zero4();
-  float dot = 0.0f;
 
   for (int vs0 = 0; vs0 < VD; vs0 += VSL) {
     __syncthreads();
-    // ---- slice operands: S and dS' rows as bf16, dO slice
-    for (int p = tid; p < VSL * KD / 8; p += 512) {
-      const int r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
-      const float* sp = ws_S + ck + (size_t)(vs0 + r) * KD + c8;
-      const float* dp = ws_dS + ck + (size_t)(vs0 + r) * KD + c8;
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sp), s1 = *reinterpret_cast<const f32x4*>(sp + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dp), d1 = *reinterpret_cast<const f32x4*>(dp + 4);
-      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      const float dvv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+    stage_slice(R);
+    bf16x4 vcur[NST];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dot = fmaf(dvv[j], sv[j], dot);
-      *reinterpret_cast<bf16x8*>(&sm.u.sl.s[r * LDK + c8]) = to_bf8(sv);
-      *reinterpret_cast<bf16x8*>(&sm.u.sl.ds[r * LDK + c8]) = to_bf8(dvv);
-    }
-    for (int p = tid; p < kC * VSL / 8; p += 512) {
-      const int r = p / (VSL / 8), c8 = (p % (VSL / 8)) * 8;
-      bf16x8 x = zero8();
-      if (r < n) x = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)b * T + t0 + r) * tokv + (size_t)h * VD + vs0 + c8);
-      *reinterpret_cast<bf16x8*>(&sm.u.sl.dob[r * LDW + c8]) = x;
-    }
+    for (int u = 0; u < NST; ++u) vcur[u] = R.v[u];
+    if (vs0 + VSL < VD) load_slice(vs0 + VSL, R);
     __syncthreads();
 
     // ---- (a) Y^T = S K^T, Z^T = S Q^T, W^T = dS' K^T; R^T = beta V^T - beta gam Y^T
@@ -536,11 +604,7 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // lane: values vs0 + 16 vb + 4 lg + e, token tk = 16 tb + ls
       const int tk = 16 * tb + ls;
       const float gm = __builtin_amdgcn_exp2f(sm.g[tk]), bt = sm.bt[tk];
-      f32x4 vv = zero4();
-      if (tk < n) {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(v + ((size_t)b * T + t0 + tk) * tokv + (size_t)h * VD + vs0 + 16 * vb + 4 * lg);
-        vv = f32x4{bf2f(x[0]), bf2f(x[1]), bf2f(x[2]), bf2f(x[3])};
-      }
+      const f32x4 vv = f32x4{bf2f(vcur[u][0]), bf2f(vcur[u][1]), bf2f(vcur[u][2]), bf2f(vcur[u][3])};
       const bf16x4 ov = *reinterpret_cast<const bf16x4*>(&sm.u.sl.dob[tk * LDW + 16 * vb + 4 * lg]);
       f32x4 r;
       float oz = 0.0f;
@@ -652,10 +716,7 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __syncthreads();   // every slice array is dead from here
 
   // ---- (f) dP o E, dA o beta E to LDS (bf16, [r][i]); dP o P and dA o M (fp32)
-  for (int p = tid; p < kC * kC / 8; p += 512) {
-    const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(&sm.u.fin.m[r * kLDC + c8]) = *reinterpret_cast<const bf16x8*>(rc + kRecM + 16 * p);
-  }
+  *reinterpret_cast<bf16x8*>(&sm.u.fin.m[(tid / (kC / 8)) * kLDC + (tid % (kC / 8)) * 8]) = mreg;
   for (int p = tid; p < kC * kC / 8; p += 512) {   // zero the tiles no job writes
     const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
     *reinterpret_cast<bf16x8*>(&sm.u.fin.dpe[r * kLDC + c8]) = zero8();

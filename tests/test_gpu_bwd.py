@@ -82,6 +82,30 @@ def test_bwd_shape_sweep(case, gate):
     check(inp, C, TOL[dt], "sweep", d_sf)
 
 
+# bf16 inputs with chunk >= 64 take the MFMA backward (64-token chunks): every
+# compiled (K, V) pair, ragged tails, several chunks
+MFMA_SWEEP = [
+    # (B, T, H, K, V, chunk)
+    (2, 129, 2, 32, 32, 64),
+    (1, 200, 3, 64, 128, 64),
+    (1, 192, 2, 32, 128, 64),
+    (1, 100, 2, 128, 32, 64),
+    (2, 64, 1, 64, 32, 64),
+    (1, 77, 2, 32, 64, 64),
+    (1, 250, 2, 128, 128, 64),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_SWEEP, ids=lambda c: "B%dT%dH%dK%dV%dC%d" % c)
+@pytest.mark.parametrize("gate", ["decay", "sigmoid"])
+def test_bwd_mfma_shapes(case, gate):
+    B, T, H, K, V, C = case
+    inp = make_inputs(B, T, H, K, V, dtype=torch.bfloat16, seed=700 + T + K + V, gate=gate,
+                      s0_std=0.05, with_do=True)
+    d_sf = torch.randn(B, H, V, K, generator=torch.Generator().manual_seed(T + 1)) * 0.1
+    check(inp, C, TOL[torch.bfloat16], "mfma", d_sf)
+
+
 def test_bwd_reproducible_and_workspace_reuse():
     inp = make_inputs(2, 150, 2, 64, 64, dtype=torch.bfloat16, seed=21, s0_std=0.05, with_do=True)
     g = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
