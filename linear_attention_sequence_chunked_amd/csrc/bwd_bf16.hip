@@ -28,6 +28,7 @@
 #include "launch.h"
 #include "mfma_common.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace gdn {
@@ -197,9 +198,10 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 }
 
 // ===========================================================================
-// (3) reverse walk: one workgroup per (value block of 16 rows, head, batch).
-// Wave 0 carries dS^T (tile cb: lane (g, s) holds dS[v0 + s][16 cb + 4g + e]);
-// waves 1..3 stage the next chunk (in reverse order) into the other LDS slot.
+// (3) reverse walk: one workgroup per (32 value rows, head, batch).  Waves 0
+// and 1 carry dS^T for rows v0 + 16 w .. + 15 (tile cb: lane (g, s) holds
+// dS[v0 + 16 w + s][16 cb + 4g + e]); waves 2 and 3 stage the next chunk (in
+// reverse order) into the other LDS slot.
 // Per chunk with dS' the gradient of the chunk-end state:
 //   W = K dS'^T,  dU = diag(D) W + P^T dO,  dR = Tm^T dU,
 //   dS <- gam_n dS' + dO^T diag(gam) Q - dR^T diag(beta gam) K.
@@ -210,7 +212,7 @@ struct alignas(16) WalkSlot {
   static constexpr int LDK = KD + 8;
   bf16 k[kC * LDK], q[kC * LDK];   // [token][channel]
   bf16 tm[kC * kLDC], p[kC * kLDC];
-  bf16 dob[kC * kLDV], dog[kC * kLDV];  // dO and diag(gam) dO: [token][value]
+  bf16 dob[kC * kLDV], dog[kC * kLDV];  // dO and diag(gam) dO: [token][32 values]
   float d[kC], nbg[kC];            // D_r = gam_n / gam_r,  -beta_r gam_r
   float gamn[4];
 };
@@ -228,13 +230,14 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ls = lane & 15, lg = lane >> 4;
-  const int v0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
+  const int v0 = blockIdx.x * 32, h = blockIdx.y, b = blockIdx.z;
   const int NT = (T + kC - 1) / kC;
   const size_t tokk = (size_t)H * KD, tokv = (size_t)H * V;
-  const size_t sbase = ((size_t)b * H + h) * (size_t)V * KD + (size_t)v0 * KD;
   const unsigned char* rec_bh = rec + ((size_t)b * H + h) * NT * (size_t)kRecBytes;
 
-  if (wave == 0) {
+  if (wave < 2) {
+    const int vw = 16 * wave;   // this wave's value rows within the slot's 32
+    const size_t sbase = ((size_t)b * H + h) * (size_t)V * KD + (size_t)(v0 + vw) * KD;
     // ============================== chain wave ==============================
     f32x4 dS[NCB];
 #pragma unroll
@@ -244,7 +247,7 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int c = NT - 1; c >= 0; --c) {
       lds_barrier();
       const SL& sl = slot[c & 1];
-      float* dst = ws_dS + (((size_t)b * H + h) * NT + c) * (size_t)V * KD + (size_t)(v0 + ls) * KD + 4 * lg;
+      float* dst = ws_dS + (((size_t)b * H + h) * NT + c) * (size_t)V * KD + (size_t)(v0 + vw + ls) * KD + 4 * lg;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<f32x4*>(dst + 16 * cb) = dS[cb];
       bf16x8 sbf[KS];
@@ -261,7 +264,7 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
         for (int cs = 0; cs < 2; ++cs)
           if (32 * cs + 31 >= 16 * tb)  // P^T is upper triangular
-            pd = mma(frag_cols(sl.p, kLDC, 16 * tb, 32 * cs, lane), frag_cols(sl.dob, kLDV, 0, 32 * cs, lane), pd);
+            pd = mma(frag_cols(sl.p, kLDC, 16 * tb, 32 * cs, lane), frag_cols(sl.dob, kLDV, vw, 32 * cs, lane), pd);
         const f32x4 dd = *reinterpret_cast<const f32x4*>(&sl.d[16 * tb + 4 * lg]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dU[tb][e] = fmaf(dd[e], w[e], pd[e]);
@@ -285,7 +288,7 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
         drf[cs] = acc_pair_to_frag(dR[2 * cs], dR[2 * cs + 1]);
-        gof[cs] = frag_cols(sl.dog, kLDV, 0, 32 * cs, lane);
+        gof[cs] = frag_cols(sl.dog, kLDV, vw, 32 * cs, lane);
       }
       const float gamn = sl.gamn[0];
 #pragma unroll
@@ -306,16 +309,16 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   } else {
     // ============================= staging waves =============================
     // Chunk c is loaded into registers one iteration before it is written to
-    // LDS; 192 staging lanes.
-    constexpr int NSL = 192;
+    // LDS; 128 staging lanes.
+    constexpr int NSL = 128;
     constexpr int NKP = kC * KD / 8;              // 16-byte pieces of a key tile
     constexpr int KPL = (NKP + NSL - 1) / NSL;
     constexpr int NMP = kC * kC / 8;              // pieces of a C x C tile
     constexpr int MPL = (NMP + NSL - 1) / NSL;
-    const int sl = tid - 64;
+    const int sl = tid - 128;
     struct Regs {
-      bf16x8 k[KPL], q[KPL], tm[MPL], p[MPL], dof;
-      float g, gl, gn, bt;
+      bf16x8 k[KPL], q[KPL], tm[MPL], p[MPL], dof[2];
+      float g[2], gl, gn, bt;
     };
     auto load = [&](int c, Regs& R) {
       const int t0 = c * kC, n = min(kC, T - t0);
@@ -339,14 +342,14 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           R.p[j] = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * p);
         }
       }
-      // dO piece: token sl / 2, values 8 (sl % 2) .. + 7 (128 pieces)
-      const int dr = sl >> 1;
-      R.dof = zero8();
-      R.g = 0.0f;
-      if (sl < 128) {
+      // dO pieces: piece p = sl + 128 j is token p / 4, values 8 (p % 4) .. + 7
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int p = sl + NSL * j, dr = p >> 2;
+        R.dof[j] = zero8();
         if (dr < n)
-          R.dof = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)b * T + t0 + dr) * tokv + (size_t)h * V + v0 + 8 * (sl & 1));
-        R.g = reinterpret_cast<const float*>(rc + kRecG)[dr];
+          R.dof[j] = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)b * T + t0 + dr) * tokv + (size_t)h * V + v0 + 8 * (p & 3));
+        R.g[j] = reinterpret_cast<const float*>(rc + kRecG)[dr];
       }
       // gates of token sl (first 64 lanes)
       if (sl < kC) {
@@ -373,13 +376,14 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           *reinterpret_cast<bf16x8*>(&s.p[r * kLDC + c8]) = R.p[j];
         }
       }
-      if (sl < 128) {
-        const int dr = sl >> 1, c8 = 8 * (sl & 1);
-        const float gm = __builtin_amdgcn_exp2f(R.g);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int p = sl + NSL * j, dr = p >> 2, c8 = 8 * (p & 3);
+        const float gm = __builtin_amdgcn_exp2f(R.g[j]);
         float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = gm * bf2f(R.dof[j]);
-        *reinterpret_cast<bf16x8*>(&s.dob[dr * kLDV + c8]) = R.dof;
+        for (int e = 0; e < 8; ++e) x[e] = gm * bf2f(R.dof[j][e]);
+        *reinterpret_cast<bf16x8*>(&s.dob[dr * kLDV + c8]) = R.dof[j];
         *reinterpret_cast<bf16x8*>(&s.dog[dr * kLDV + c8]) = to_bf8(x);
       }
       if (sl < kC) {
@@ -860,6 +864,39 @@ size_t bwd_bf16_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int6
   return (size_t)(2 * B * H * NT * V * K * 4 + B * H * NT * (int64_t)kRecBytes);
 }
 
+namespace {
+
+// A second stream per device, created on first use and kept for the life of the
+// process, with the two events of a fork / join.  The chunk-start states and the
+// reverse walk are independent sequential walks of 96 workgroups each; run side
+// by side they share the chip instead of taking turns.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;   // guards creation and each fork / join enqueue sequence
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& sd = g_side[dev];
+  if (!sd.s && !sd.failed) {
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
+      sd.failed = true;   // keep going on the caller's stream alone
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  return sd.failed ? nullptr : &sd;
+}
+
+}  // namespace
+
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   if (!bwd_bf16_supported(a.K, a.V, a.chunk)) return hipErrorInvalidValue;
   const int NT = (a.T + kC - 1) / kC;
@@ -883,7 +920,17 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   f.K = a.K;
   f.V = a.V;
   f.chunk = kC;
-  if ((e = launch_fwd_states(f, true, ws_S, stream)) != hipSuccess) return e;
+  f.vs = 32;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* sd = side_stream();
+  hipStream_t st_states = stream;
+  if (sd) {
+    if ((e = hipEventRecord(sd->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return e;
+    st_states = sd->s;
+  }
+  if ((e = launch_fwd_states(f, true, ws_S, st_states)) != hipSuccess) return e;
+  if (sd && (e = hipEventRecord(sd->join, sd->s)) != hipSuccess) return e;
   const bf16* q = static_cast<const bf16*>(a.q);
   const bf16* k = static_cast<const bf16*>(a.k);
   const bf16* v = static_cast<const bf16*>(a.v);
@@ -894,9 +941,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
                        a.beta, rec, a.T, a.H);
     hipError_t r;
     if ((r = hipGetLastError()) != hipSuccess) return r;
-    hipLaunchKernelGGL((bwd16_dstate_kernel<KD>), dim3(a.V / 16, a.H, a.B), dim3(256), 0, stream, q, k,
+    hipLaunchKernelGGL((bwd16_dstate_kernel<KD>), dim3(a.V / 32, a.H, a.B), dim3(256), 0, stream, q, k,
                        d_o, a.d_sfinal, a.d_s0, rec, ws_dS, a.T, a.H, a.V);
     if ((r = hipGetLastError()) != hipSuccess) return r;
+    if (sd && (r = hipStreamWaitEvent(stream, sd->join, 0)) != hipSuccess) return r;   // states ready
     auto local = [&](auto vc) -> hipError_t {
       constexpr int VD = decltype(vc)::value;
       hipLaunchKernelGGL((bwd16_local_kernel<KD, VD>), dim3(NT, a.H, a.B), dim3(512), 0, stream, q, k, v,

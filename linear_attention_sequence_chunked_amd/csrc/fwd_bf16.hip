@@ -714,7 +714,7 @@ bool fwd_bf16_supported(int K, int V, int chunk) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (!fwd_bf16_supported(a.K, a.V, a.chunk)) return hipErrorInvalidValue;
-  const int vs = pick_vs(a.B, a.H, a.V);
+  const int vs = (a.vs == 16 || a.vs == 32) && a.vs <= a.V ? a.vs : pick_vs(a.B, a.H, a.V);
   if (a.K <= 32) return launch_vs<32>(a, vs, stream);
   if (a.K == 64) return launch_vs<64>(a, vs, stream);
   return launch_vs<128>(a, vs, stream);

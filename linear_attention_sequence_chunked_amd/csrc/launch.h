@@ -22,6 +22,8 @@ struct FwdArgs {
   // optional packed batch: B sequences, sequence b = tokens [cu[b], cu[b+1]) of
   // the [1, T, H, *] tensors; states are [B, H, V, K]
   const int* cu_seqlens = nullptr;
+  // bf16 kernel only: value rows per workgroup (16 or 32); 0 picks by grid size
+  int vs = 0;
 };
 
 // Float32 q/k/v/o: scalar fp32 kernel (exact fp32 products and sums).
