@@ -26,6 +26,7 @@ METRIC = "GDN chunk fwd tokens/s + % bf16 MFMA peak at B8·T4096·H6·d128"
 
 # Sources of the timed kernel: a traffic record measured on other sources is stale.
 KERNEL_SOURCES = ["linear_attention_sequence_chunked_amd/csrc/fwd_bf16.hip",
+                  "linear_attention_sequence_chunked_amd/csrc/mfma_common.h",
                   "linear_attention_sequence_chunked_amd/csrc/gdn_api.hip",
                   "linear_attention_sequence_chunked_amd/csrc/launch.h"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "fwd_bf16_train_B8T4096H6_hbm_traffic.md")
