@@ -430,7 +430,7 @@ struct alignas(16) LocalSmem {
   } u;
   float g[kC], bt[kC];
   float red[4][16][16];                // per-token row sums of the slice tiles
-  float dgs[kC], dbs[kC];              // per-token gate gradients
+  float dgs[kC], dbs[kC], dus[kC];     // per-token gate gradients, D_r U_r.W_r
   float dot[8];                        // <dS', S> partials per wave
 };
 
@@ -795,50 +795,61 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       store_bf4(dk + off, xk);
     }
   }
-  // ---- (h) per-token gate gradients (one lane per token, fixed order)
-  if (tid < kC) {
-    const int r = tid, tb = r / 16, s = r % 16;
-    float oz = 0.0f, uw = 0.0f, db = 0.0f, ry = 0.0f;
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      oz += sm.red[0][tb * NVB + vb][s];
-      uw += sm.red[1][tb * NVB + vb][s];
-      db += sm.red[2][tb * NVB + vb][s];
-      ry += sm.red[3][tb * NVB + vb][s];
-    }
-    const float gm = __builtin_amdgcn_exp2f(sm.g[r]), br = sm.bt[r];
-    const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[r]);
-    float sp = 0.0f, sa = 0.0f;
-    for (int i = 0; i <= r; ++i) {
+  // ---- (h) per-token gate gradients: eight lanes per token split the row and
+  // column sums of dP o P and dA o M by index mod 8 and combine them with three
+  // shuffles (fixed order)
+  {
+    const int r = tid >> 3, q8 = tid & 7;
+    float sp = 0.0f, sa = 0.0f, cp = 0.0f, ca = 0.0f;
+    for (int i = q8; i <= r; i += 8) {
       sp += sm.u.fin.xp[r][i];
       sa += sm.u.fin.xa[r][i];
     }
-    float cp = 0.0f, ca = 0.0f;
-    for (int rr = r; rr < kC; ++rr) {
+    for (int rr = r + ((q8 - r) & 7); rr < kC; rr += 8) {
       cp += sm.u.fin.xp[rr][r];
       ca += sm.bt[rr] * sm.u.fin.xa[rr][r];
     }
-    float dg = gm * oz - br * gm * ry - dd * uw + (sp - cp) + (br * sa - ca);
-    const float du = dd * uw;
-    // the chunk-end terms go to the last real token
-    float esum = du;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);  // tokens >= n add zeros
+    for (int m = 1; m < 8; m <<= 1) {
+      sp += __shfl_xor(sp, m);
+      sa += __shfl_xor(sa, m);
+      cp += __shfl_xor(cp, m);
+      ca += __shfl_xor(ca, m);
+    }
+    if (q8 == 0) {
+      const int tb = r / 16, s = r % 16;
+      float oz = 0.0f, uw = 0.0f, db = 0.0f, ry = 0.0f;
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        oz += sm.red[0][tb * NVB + vb][s];
+        uw += sm.red[1][tb * NVB + vb][s];
+        db += sm.red[2][tb * NVB + vb][s];
+        ry += sm.red[3][tb * NVB + vb][s];
+      }
+      const float gm = __builtin_amdgcn_exp2f(sm.g[r]), br = sm.bt[r];
+      const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[r]);
+      sm.dgs[r] = gm * oz - br * gm * ry - dd * uw + (sp - cp) + (br * sa - ca);
+      sm.dbs[r] = db + sa;
+      sm.dus[r] = dd * uw;   // zero past the end (U rows are zero there)
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // the chunk-end terms go to the last real token; then
+    // d ln alpha_t = sum_{t <= r < n} dg_r as a scan over the reversed tokens
+    float esum = sm.dus[lane];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);
     float dsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) dsum += sm.dot[w];
-    if (r == n - 1) dg += __builtin_amdgcn_exp2f(sm.g[kC - 1]) * dsum + esum;
-    sm.dgs[r] = dg;
-    sm.dbs[r] = db + sa;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float acc = 0.0f;  // d ln alpha_t = sum_{t <= r < n} dg_r
-    for (int r = n - 1; r >= 0; --r) {
-      acc += sm.dgs[r];
-      const size_t go = ((size_t)b * T + t0 + r) * H + h;
-      dalpha[go] = acc / alpha[go];
-      dbeta[go] = sm.dbs[r];
+    float dg = lane < n ? sm.dgs[lane] : 0.0f;
+    if (lane == n - 1) dg += __builtin_amdgcn_exp2f(sm.g[kC - 1]) * dsum + esum;
+    const float suf = __shfl(wave_scan(__shfl(dg, 63 - lane), lane), 63 - lane);
+    if (lane < n) {
+      const size_t go = ((size_t)b * T + t0 + lane) * H + h;
+      dalpha[go] = suf / alpha[go];
+      dbeta[go] = sm.dbs[lane];
     }
   }
 }
