@@ -269,7 +269,9 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
   }
 }
 
-template <int KD, int VS, int CP>
+// WO: the output o is produced.  Without it (states only: o == NULL) queries,
+// P, Z and O are skipped entirely.
+template <int KD, int VS, int CP, bool WO>
 __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -385,7 +387,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       R.q[j] = zero8();
       if (krow[j] < n) {
         R.k[j] = *reinterpret_cast<const bf16x8*>(kb + kgo[j]);
-        R.q[j] = *reinterpret_cast<const bf16x8*>(qb + kgo[j]);
+        if constexpr (WO) R.q[j] = *reinterpret_cast<const bf16x8*>(qb + kgo[j]);
       }
     }
 #pragma unroll
@@ -413,7 +415,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     for (int j = 0; j < KPL; ++j) {
       if (sl + NSL * j < KPIECES) {  // pieces past K are stored as zeros
         *reinterpret_cast<lds_bf16x8*>(kst + j * (NSL / (KD / 8)) * (KD + 8)) = R.k[j];
-        *reinterpret_cast<lds_bf16x8*>(qst + j * (NSL / (KD / 8)) * (KD + 8)) = R.q[j];
+        if constexpr (WO) *reinterpret_cast<lds_bf16x8*>(qst + j * (NSL / (KD / 8)) * (KD + 8)) = R.q[j];
       }
     }
 #pragma unroll
@@ -470,7 +472,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         ka[0][tb] = ld8(kr + 16 * tb * LDK);
-        qa[0][tb] = ld8(qr + 16 * tb * LDK);
+        if constexpr (WO) qa[0][tb] = ld8(qr + 16 * tb * LDK);
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) sbf[ks] = acc_pair_to_frag(S[2 * ks], S[2 * ks + 1]);
@@ -486,14 +488,14 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
           for (int tb = 0; tb < NTB; ++tb) {
             ka[(ks + 1) & 1][tb] = ld8(kr + 16 * tb * LDK + 32 * (ks + 1));
-            qa[(ks + 1) & 1][tb] = ld8(qr + 16 * tb * LDK + 32 * (ks + 1));
+            if constexpr (WO) qa[(ks + 1) & 1][tb] = ld8(qr + 16 * tb * LDK + 32 * (ks + 1));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
           Y[tb] = mma(ka[ks & 1][tb], sbf[ks], Y[tb]);   // Y   [token][v]
-          Z[tb] = mma(sbf[ks], qa[ks & 1][tb], Z[tb]);   // Z^T [v][token]
+          if constexpr (WO) Z[tb] = mma(sbf[ks], qa[ks & 1][tb], Z[tb]);   // Z^T [v][token]
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -507,14 +509,14 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         vt[tb] = tr4(vc + 16 * tb * SM::LDV);
         bt[tb] = *reinterpret_cast<const lf32x4*>(g4 + 16 * tb);
         bgv[tb] = *reinterpret_cast<const lf32x4*>(g4 + (SM::BG - SM::BETA) + 16 * tb);
-        gmt[tb] = g1[16 * tb];  // Z^T columns are tokens
+        if constexpr (WO) gmt[tb] = g1[16 * tb];  // Z^T columns are tokens
       }
       f32x4 R[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) R[tb][e] = bt[tb][e] * (float)vt[tb][e] - bgv[tb][e] * Y[tb][e];
-        Z[tb] = Z[tb] * gmt[tb];
+        if constexpr (WO) Z[tb] = Z[tb] * gmt[tb];
       }
       bf16x8 rb[CS];
 #pragma unroll
@@ -532,7 +534,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         for (int cs = 0; cs < CS; ++cs)
           if (32 * cs <= 16 * tb + 15) {  // Tm and P are lower triangular
             tf[tb][cs] = frag_cols_at(tc, LDC, 16 * tb, 32 * cs);
-            pf[tb][cs] = frag_cols_at(pc, LDC, 16 * tb, 32 * cs);
+            if constexpr (WO) pf[tb][cs] = frag_cols_at(pc, LDC, 16 * tb, 32 * cs);
           }
       }
       const float gam_n = sm.gt[gs].gam[CP - 1];
@@ -565,7 +567,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       const int t0 = x * C;
       const int n = min(C, Tn - t0);
       bf16* obase = o + (seq0 + t0) * tok_v + (size_t)h * V + v0 + 16 * vb + 4 * lg;
-      if (o)  // no output when only states are wanted
+      if (WO && o)  // no output when only states are wanted
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         f32x4 O = Z[tb];
@@ -642,14 +644,14 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
             switch (gw) {
               case 0: gram_rows<KD, CP, 0, 0, 3>(sm, c, lane); break;
               case 1: gram_rows<KD, CP, 0, 1, 2>(sm, c, lane); break;
-              case 2: gram_rows<KD, CP, 1, 0, 3>(sm, c, lane); break;
-              case 3: gram_rows<KD, CP, 1, 1, 2>(sm, c, lane); break;
+              case 2: if constexpr (WO) gram_rows<KD, CP, 1, 0, 3>(sm, c, lane); break;
+              case 3: if constexpr (WO) gram_rows<KD, CP, 1, 1, 2>(sm, c, lane); break;
               default: break;
             }
           } else {
             switch (gw) {
               case 0: gram_rows<KD, CP, 0, 0, 1>(sm, c, lane); break;
-              case 1: gram_rows<KD, CP, 1, 0, 1>(sm, c, lane); break;
+              case 1: if constexpr (WO) gram_rows<KD, CP, 1, 0, 1>(sm, c, lane); break;
               default: break;
             }
           }
@@ -679,11 +681,17 @@ template <int KD, int VS, int CP>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int nslice = a.V / VS;
   const int nblk = a.B * a.H * nslice;
-  hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP>), dim3(nblk), dim3(kThreads), 0, stream,
-                     static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                     static_cast<const bf16*>(a.v), a.alpha, a.beta, a.s0,
-                     static_cast<bf16*>(a.o), a.s_final, a.s_ckpt, a.cu_seqlens, a.T, a.H, a.K, a.V,
-                     a.chunk, nslice);
+  if (a.o)
+    hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP, true>), dim3(nblk), dim3(kThreads), 0, stream,
+                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                       static_cast<const bf16*>(a.v), a.alpha, a.beta, a.s0,
+                       static_cast<bf16*>(a.o), a.s_final, a.s_ckpt, a.cu_seqlens, a.T, a.H, a.K, a.V,
+                       a.chunk, nslice);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP, false>), dim3(nblk), dim3(kThreads), 0, stream,
+                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                       static_cast<const bf16*>(a.v), a.alpha, a.beta, a.s0, nullptr, a.s_final,
+                       a.s_ckpt, a.cu_seqlens, a.T, a.H, a.K, a.V, a.chunk, nslice);
   return hipGetLastError();
 }
 
