@@ -85,6 +85,53 @@ def algorithmic_bytes(B, T, H, K, V, esz=2, with_s0=False):
     return by
 
 
+def executed_mfma_flops(B, T, H, K, V, C, vs):
+    """Dense MFMA FLOPs the bf16 forward kernel issues (16x16x32 instructions x
+    16384): per (stream, chunk) and workgroup of vs value rows, the Gram tiles
+    (10 of A and 10 of P, K/32 k-steps each), the two levels of the block solve
+    (16 instructions) and, per 16 value rows, the chain (Y, Z: C/16 token blocks
+    x K/32; S: K/16 x C/32; U and O: 6 (C = 64) or 2 (C = 32) lower-triangular
+    block products each).  Gram and solve are repeated by every value slice of a
+    stream.  (A states-only call skips O; rocprofv3's SQ_INSTS_MFMA matched this
+    count per launch.)"""
+    ntb = C // 16
+    tri = ntb * (ntb + 1) // 2              # lower token-block pairs
+    gram = 2 * tri * (K // 32)
+    levels = 16 if ntb == 4 else 2
+    chain = 2 * ntb * (K // 32) + (K // 16) * (C // 32) + 2 * (6 if ntb == 4 else 2)
+    per_wg = gram + levels + (vs // 16) * chain
+    nchunks = (T + C - 1) // C
+    return B * H * (V // vs) * nchunks * per_wg * 16384.0
+
+
+def copy_bandwidth_gbs(nbytes=1 << 30, reps=5):
+    """Achievable HBM bandwidth of a plain device copy (bytes read + written per
+    second), the practical reference beside the published peak."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def algorithmic_flops(B, T, H, K, V, C):
     """Structural FLOPs per token-head of the chunk algorithm (triangular products at
     their structural size, the inverse as C^3/3 per chunk):
@@ -428,6 +475,8 @@ def main():
     per_launch = np.array([a.elapsed_time(b) for a, b in ev])
     ms_per_step = total_ms / args.steps
     kern_ms = float(per_launch.mean())
+    pcts = {"p10": float(np.percentile(per_launch, 10)), "p50": float(np.percentile(per_launch, 50)),
+            "p90": float(np.percentile(per_launch, 90))}
 
     tokens = B * T
     value = tokens / (ms_per_step / 1e3)
@@ -437,6 +486,11 @@ def main():
     achieved_gbs = abytes / (kern_ms / 1e3) / 1e9
     traffic = measured_traffic() if args.workload == "train_bf16" else None
     tflops = aflops / (kern_ms / 1e3) / 1e12
+    xflops = None
+    if w.dtype == torch.bfloat16 and args.segments == 1 and K in (32, 64, 128) and C in (32, 64):
+        vs = 32 if (V >= 32 and B * H * (V // 32) >= 192) else 16
+        xflops = executed_mfma_flops(B, T, H, K, V, C, vs)
+    copy_gbs = copy_bandwidth_gbs()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -448,9 +502,26 @@ def main():
         t0 = time.perf_counter()
         oracle.fwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["initial_state"], nthreads=used)
         dt = time.perf_counter() - t0
+        # one core on a sample of the streams, for a per-core rate
+        ns1 = min(4, B * H) if B * H >= 4 else B * H
+        sl = lambda x: None if x is None else x.reshape(1, T, B * H, *x.shape[3:])[:, :, :ns1].contiguous() \
+            if x.dim() == 4 else x.reshape(1, T, B * H)[:, :, :ns1].contiguous()
+        q1 = c["q"].permute(1, 0, 2, 3).reshape(T, B * H, K)[:, :ns1].reshape(1, T, ns1, K)
+        k1 = c["k"].permute(1, 0, 2, 3).reshape(T, B * H, K)[:, :ns1].reshape(1, T, ns1, K)
+        v1 = c["v"].permute(1, 0, 2, 3).reshape(T, B * H, V)[:, :ns1].reshape(1, T, ns1, V)
+        a1 = c["alpha"].permute(1, 0, 2).reshape(T, B * H)[:, :ns1].reshape(1, T, ns1)
+        b1 = c["beta"].permute(1, 0, 2).reshape(T, B * H)[:, :ns1].reshape(1, T, ns1)
+        t1 = time.perf_counter()
+        oracle.fwd(q1, k1, v1, a1, b1, None, nthreads=1)
+        dt1 = time.perf_counter() - t1
+        flop_tok = 8.0 * K * V     # fp64 FLOPs per token-head of the token loop
         cpu = {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
                "sample": "whole workload (all %d streams x %d tokens), fp64 token loop, %.2f s"
-                         % (B * H, T, dt)}
+                         % (B * H, T, dt),
+               "gflops_fp64": flop_tok * B * T * H / dt / 1e9,
+               "one_core": {"streams": ns1, "seconds": dt1,
+                            "token_heads_per_s": ns1 * T / dt1},
+               "cpu_model": cpu_model()}
 
     line = {
         "metric": METRIC,
@@ -473,9 +544,13 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel_ms": kern_ms, "algorithmic_bytes": abytes},
+                     "kernel_ms": kern_ms, "kernel_ms_pct": pcts, "algorithmic_bytes": abytes,
+                     "copy_gbs": copy_gbs, "frac_of_copy": achieved_gbs / copy_gbs},
         "mfma": {"tflops_algorithmic": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
-                 "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flops": aflops},
+                 "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flops": aflops,
+                 "executed_flops": xflops,
+                 "tflops_executed": xflops / (kern_ms / 1e3) / 1e12 if xflops else None,
+                 "frac_executed": xflops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS if xflops else None},
         "cpu_baseline": cpu,
         "gate": gate,
     }
