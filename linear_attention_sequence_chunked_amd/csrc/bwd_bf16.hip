@@ -115,32 +115,40 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
   __syncthreads();
 
-  // Gram tiles of row block w: A (strict) to fp32 LDS; M and P to the record
-  // (tiles above the diagonal as zeros)
+  // Gram tiles, balanced over the waves: waves 0 and 1 build A for token-block
+  // rows {0, 3} and {1, 2}, waves 2 and 3 build P for the same rows (five tiles
+  // each).  A (strict) goes to fp32 LDS and M to the record, P to the record;
+  // the tiles above the diagonal are written as zeros.
   const int ls = lane & 15, lg = lane >> 4;
   {
-    const int w = wave;
-    for (int tc = 0; tc < 4; ++tc) {
-      f32x4 accA = zero4(), accP = zero4();
-      if (tc <= w) {
+    const bool isP = wave >= 2;
+    const int ra = (wave & 1) ? 1 : 0, rb = (wave & 1) ? 2 : 3;
+    const bf16* ab = isP ? sm.q : sm.k;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 kc = frag_rows(sm.k, LDK, 16 * tc, 32 * ks, lane);
-          accA = mma(frag_rows(sm.k, LDK, 16 * w, 32 * ks, lane), kc, accA);
-          accP = mma(frag_rows(sm.q, LDK, 16 * w, 32 * ks, lane), kc, accP);
+    for (int half = 0; half < 2; ++half) {
+      const int w = half == 0 ? ra : rb;   // token-block row
+      for (int tc = 0; tc < 4; ++tc) {
+        f32x4 acc = zero4();
+        if (tc <= w) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = mma(frag_rows(ab, LDK, 16 * w, 32 * ks, lane), frag_rows(sm.k, LDK, 16 * tc, 32 * ks, lane), acc);
         }
-      }
-      // accumulator: row r = 16 w + 4 lg + e, column i = 16 tc + ls
-      const int i = 16 * tc + ls;
-      const float gi = sm.g[i];
+        // accumulator: row r = 16 w + 4 lg + e, column i = 16 tc + ls
+        const int i = 16 * tc + ls;
+        const float gi = sm.g[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * lg + e;
-        const float dec = __builtin_amdgcn_exp2f(i <= r ? sm.g[r] - gi : -INFINITY);
-        const float m = i < r ? dec * accA[e] : 0.0f;
-        sm.a[r][i] = sm.bt[r] * m;
-        rm[r * kC + i] = (bf16)m;
-        rp[r * kC + i] = (bf16)(dec * accP[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * w + 4 * lg + e;
+          const float dec = __builtin_amdgcn_exp2f(i <= r ? sm.g[r] - gi : -INFINITY);
+          if (isP) {
+            rp[r * kC + i] = (bf16)(dec * acc[e]);
+          } else {
+            const float m = i < r ? dec * acc[e] : 0.0f;
+            sm.a[r][i] = sm.bt[r] * m;
+            rm[r * kC + i] = (bf16)m;
+          }
+        }
       }
     }
   }
@@ -181,7 +189,9 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int j = 0; j + d < 4; ++j) {
         const int i = j + d;
         float s = 0.0f;
-        for (int m = 0; m <= er; ++m) s = fmaf(sm.x[16 * i + er][16 * i + m], sm.x[16 * j + m][16 * i + ec], s);
+#pragma unroll
+        for (int m = 0; m < 16; ++m)   // T_ii is lower triangular: its upper entries are zeros
+          s = fmaf(sm.x[16 * i + er][16 * i + m], sm.x[16 * j + m][16 * i + ec], s);
         sm.x[16 * i + er][16 * j + ec] = -s;
       }
       __syncthreads();

@@ -132,3 +132,19 @@ def test_fwdbwd_workload_parity():
     # the forward+backward shape: B4 T2048 H6 K=V=128 bf16, d_final_state = 0
     w = WORKLOADS["fwdbwd_bf16"]
     check(workload_inputs(w), w.chunk, TOL[w.dtype], w.name)
+
+
+def test_bwd_mfma_on_a_side_stream_matches_default_stream():
+    # the MFMA backward forks to a library stream and joins back; on a caller
+    # stream other than the default the result must be the same bits
+    inp = make_inputs(2, 200, 3, 128, 64, dtype=torch.bfloat16, seed=31, s0_std=0.05, with_do=True)
+    g = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
+    ref = chunk_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["d_o"], g["initial_state"], chunk=64)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = chunk_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["d_o"], g["initial_state"],
+                        chunk=64)
+    s.synchronize()
+    for x, y in zip(ref, got):
+        assert torch.equal(x, y)
