@@ -216,6 +216,38 @@ def bench_backward(args):
     }), flush=True)
 
 
+def oracle_timing(args):
+    """The fp64 CPU oracle timed on the host over the forward configurations
+    (mid, training shape, long context) and, in reverse mode, the forward+backward
+    one: every (batch, head) stream on all host cores, and the same on one core.
+    Prints one JSON line; the GPU is not used."""
+    import oracle
+    from linear_attention_sequence_chunked_amd.workloads import WORKLOADS, workload_inputs
+    cores = oracle.default_threads()
+    res = {"kind": "oracle", "cpu_model": cpu_model(), "cores": cores, "configs": []}
+    for name, mode in (("mid_bf16", "fwd"), ("train_bf16", "fwd"), ("fwdbwd_bf16", "bwd"),
+                       ("long_bf16", "fwd")):
+        w = WORKLOADS[name]
+        c = workload_inputs(w)
+        row = {"workload": name, "mode": mode, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V}
+        for nth in (cores, 1):
+            t0 = time.perf_counter()
+            if mode == "fwd":
+                oracle.fwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["initial_state"], nthreads=nth)
+            else:
+                oracle.bwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["d_o"], c["initial_state"],
+                           nthreads=nth)
+            dt = time.perf_counter() - t0
+            row["seconds_%d_cores" % nth] = dt
+            row["tokens_per_s_%d_cores" % nth] = w.B * w.T / dt
+        if mode == "fwd":
+            row["gflops_fp64_all_cores"] = 8.0 * w.K * w.V * w.B * w.T * w.H / row["seconds_%d_cores" % cores] / 1e9
+        res["configs"].append(row)
+        print("  %s %s: %.2f s on %d cores, %.2f s on 1" % (name, mode, row["seconds_%d_cores" % cores], cores,
+                                                           row["seconds_1_cores"]), file=sys.stderr, flush=True)
+    print(json.dumps(res), flush=True)
+
+
 def bench_decode(args):
     """One step = one gdn_decode_step call (one token for 64 streams x 16 heads,
     K = V = 128).  Five state buffers (5 x 64 MiB) rotate so the Infinity Cache
@@ -380,7 +412,12 @@ def main():
                     help="run the forward segment-parallel with this many segments per sequence")
     ap.add_argument("--varlen", action="store_true",
                     help="time gdn_chunk_fwd_varlen on a packed ragged batch instead")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="only time the fp64 CPU oracle on the configurations (no GPU)")
     args = ap.parse_args()
+    if args.oracle_timing:
+        oracle_timing(args)
+        return
     if args.copy_calibration:
         copy_calibration()
         return

@@ -249,7 +249,12 @@ GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int
  * with chunk >= 64 and K, V in {32, 64, 128}: 64-token chunks, matrix products
  * on bf16 MFMA with bf16 operands and float32 accumulation, everything else
  * float32 (other bf16 shapes: the float32 path).  Every sum has a fixed order,
- * so results are bitwise reproducible; dq, dk, dv are rounded to dtype once.  No output may
+ * so results are bitwise reproducible; dq, dk, dv are rounded to dtype once.
+ * The MFMA path runs two independent sequential walks side by side: it forks
+ * from `stream` to a second stream of the library's (one per device, created on
+ * the first call, default priority) through an event and joins back before it
+ * returns, so the work is ordered exactly as if all of it were on `stream`
+ * (host calls that enqueue on one device are serialised by a lock).  No output may
  * overlap any other buffer (inputs, other outputs, workspace).  Errors as for
  * gdn_chunk_fwd; a workspace smaller than required is GDN_ERROR_INVALID_VALUE.
  */
