@@ -128,6 +128,14 @@ def test_bwd_zero_upstream_gives_zero_gradients():
         assert torch.count_nonzero(got[n]).item() == 0, n
 
 
+def test_bwd_mfma_zero_upstream_gives_zero_gradients():
+    inp = make_inputs(2, 130, 2, 128, 64, dtype=torch.bfloat16, seed=23, s0_std=0.1, with_do=True)
+    inp["d_o"] = torch.zeros_like(inp["d_o"])
+    got = gpu_bwd(inp, 64)
+    for n in NAMES:
+        assert torch.count_nonzero(got[n]).item() == 0, n
+
+
 def test_fwdbwd_workload_parity():
     # the forward+backward shape: B4 T2048 H6 K=V=128 bf16, d_final_state = 0
     w = WORKLOADS["fwdbwd_bf16"]
