@@ -102,22 +102,11 @@ __device__ __forceinline__ bf16x8 frag_cols16(const bf16* base, int ld, int r0, 
 // per row (row stride KD + 8).  A 16-byte fragment read by 16 lanes of
 // consecutive rows then covers all 64 banks, and every fragment of a tile is a
 // constant offset from one per-lane base address (no per-read address math).
+// swz gives the element offset of (row, col) in such a tile.
 template <int KD>
 __device__ __forceinline__ int swz(int row, int col) {
   return row * (KD + 8) + col;
 }
-template <int KD>
-__device__ __forceinline__ bf16x8 frag_rows_sw(const bf16* base, int r0, int k0, int lane) {
-  return *reinterpret_cast<const bf16x8*>(base + swz<KD>(r0 + (lane & 15), k0 + 8 * (lane >> 4)));
-}
-template <int KD>
-__device__ __forceinline__ bf16x8 frag_cols_sw(const bf16* base, int c0, int k0, int lane) {
-  const int s = lane & 15, g = lane >> 4;
-  const int row = k0 + 8 * g + (s >> 2), col = c0 + 4 * (s & 3);
-  const bf16x4 lo = tr_read(base + swz<KD>(row, col)), hi = tr_read(base + swz<KD>(row + 4, col));
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 // Accumulator tile (lane holds rows 4g..4g+3 of column s) stored transposed:
 // dst[(c0 + s) * ld + r0 + 4g + e] = d[e], as bf16.
 __device__ __forceinline__ void store_tile_t(bf16* base, int ld, int c0, int r0, f32x4 d, int lane) {
