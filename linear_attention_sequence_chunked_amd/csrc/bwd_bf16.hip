@@ -10,14 +10,17 @@
 // results are bitwise reproducible.
 //
 // Launches:
-//   (1) the bf16 forward kernel writes the fp32 chunk-start states S_c;
+//   (1) the bf16 forward kernel's states-only instance writes the fp32
+//       chunk-start states S_c; it runs on a second stream, beside (2) and (3),
+//       which do not need it;
 //   (2) prep, one workgroup per chunk: gates, the Gram matrices A = diag(beta) M
-//       and P, Tm = (I + A)^-1 by fp32 substitution; record = Tm, P, M (bf16)
-//       and the gates (fp32);
-//   (3) reverse walk, one workgroup per (stream, 16 value rows): the state
+//       and P, Tm = (I + A)^-1 in fp32 by 16 x 16 blocks; record = Tm, P, M
+//       (bf16) and the gates (fp32);
+//   (3) reverse walk, one workgroup per (stream, 32 value rows): the state
 //       gradient dS^T lives in MFMA accumulator tiles across chunks (like the
 //       forward's state); stores every chunk's end-state gradient dS'_c;
-//   (4) token gradients, one workgroup per chunk, fully parallel.
+//   (4) token gradients, one workgroup per chunk, fully parallel, after the
+//       join with (1).
 //
 // Layout conventions of the products in (4): quantities with a token axis and
 // a value or channel axis are computed transposed (accumulator rows = value or
