@@ -78,7 +78,7 @@ struct alignas(16) Smem {
   // offsets (in floats) of the gate vectors from gl within one slot
   static constexpr int GAM = CP, BETA = 2 * CP, BG = 3 * CP, DN = 4 * CP;
   bf16 pt[2][CP * LDC];                // P^T: pt[i][r]
-  bf16 tt[2][CP * LDC];                // Tm^T: tt[j][i]; upper blocks zero (level scratch)
+  bf16 tt[2][CP * LDC];                // Tm^T: tt[j][i]; upper blocks zero
   bf16 ap[2][APK];                     // off-diagonal A^T blocks used by the levels
   // diagonal A blocks, fp32, transposed [c][r]; blocks ADS floats apart so the
   // four blocks read at once by the diagonal solve fall on different banks
@@ -91,51 +91,41 @@ struct alignas(16) Smem {
 //   level 1: Tm_10 = -Tm_11 (A_10 Tm_00),  Tm_32 = -Tm_33 (A_32 Tm_22)
 //   level 2: Tm_[23][01] = -Tm_[23] (A_[23][01] Tm_[01])
 // Two waves share the work: both compute level 1 (identical values, written
-// twice), then each computes one 16-column block bj = part of level 2.  Scratch
-// tiles live in Tm's upper (zero) blocks and are zeroed again afterwards.
+// twice), then each computes one 16-column block bj = part of level 2.  The
+// inner products A Tm stay in registers: their accumulator tiles become the
+// next product's operand (k = their rows) through the permlane conversion, with
+// the same bf16 rounding a trip through LDS would give.
 template <int CP>
 __device__ __forceinline__ void levels_part(bf16* tt, const bf16* ap, int lane, int part) {
   constexpr int NTB = CP / 16;
   constexpr int LDC = CP + 8, LDA = 24;
   if constexpr (NTB == 4) {
-    bf16* scr = tt + (48 - 16 * part) * LDC;  // Tm^T rows [48,64) or [32,48), columns [0,32)
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
       const int bi = 2 * pr + 1, bj = 2 * pr;
       const f32x4 X = mma(frag_cols16(ap + 16 * pr * LDA, LDA, 0, 0, lane),
                           frag_rows16(tt, LDC, 16 * bj, 16 * bj, lane), zero4());
-      store_tile_t(scr, LDC, 0, 16 * pr, X, lane);
-      const f32x4 Tij = mma(frag_cols16(tt, LDC, 16 * bi, 16 * bi, lane), frag_rows16(scr, LDC, 0, 16 * pr, lane),
+      const f32x4 Tij = mma(frag_cols16(tt, LDC, 16 * bi, 16 * bi, lane), acc_pair_to_frag(X, zero4()),
                             zero4());
       store_tile_t(tt, LDC, 16 * bj, 16 * bi, -Tij, lane);
     }
     const int bj = part;
+    f32x4 X2[2];
+#pragma unroll
+    for (int bi = 2; bi < 4; ++bi)
+      X2[bi - 2] = mma(frag_cols(ap + (bi == 2 ? 32 : 64) * LDA, LDA, 0, 0, lane),
+                       frag_rows(tt, LDC, 16 * bj, 0, lane), zero4());
+    const bf16x8 xb = acc_pair_to_frag(X2[0], X2[1]);
 #pragma unroll
     for (int bi = 2; bi < 4; ++bi) {
-      const f32x4 X2 = mma(frag_cols(ap + (bi == 2 ? 32 : 64) * LDA, LDA, 0, 0, lane),
-                           frag_rows(tt, LDC, 16 * bj, 0, lane), zero4());
-      store_tile_t(scr, LDC, 0, 16 * (bi - 2), X2, lane);
-    }
-#pragma unroll
-    for (int bi = 2; bi < 4; ++bi) {
-      const f32x4 Tij = mma(frag_cols(tt, LDC, 16 * bi, 32, lane), frag_rows(scr, LDC, 0, 0, lane), zero4());
+      const f32x4 Tij = mma(frag_cols(tt, LDC, 16 * bi, 32, lane), xb, zero4());
       store_tile_t(tt, LDC, 16 * bj, 16 * bi, -Tij, lane);
-    }
-    {
-      const int r = lane >> 2, c8 = (lane & 3) * 8;  // 16 rows x 32 columns
-      *reinterpret_cast<bf16x8*>(&scr[r * LDC + c8]) = zero8();
     }
   } else {
     if (part != 0) return;
-    bf16* scr = tt + 16 * LDC;  // Tm's upper block (0, 1)
     const f32x4 X = mma(frag_cols16(ap, LDA, 0, 0, lane), frag_rows16(tt, LDC, 0, 0, lane), zero4());
-    store_tile_t(scr, LDC, 0, 0, X, lane);
-    const f32x4 Tij = mma(frag_cols16(tt, LDC, 16, 16, lane), frag_rows16(scr, LDC, 0, 0, lane), zero4());
+    const f32x4 Tij = mma(frag_cols16(tt, LDC, 16, 16, lane), acc_pair_to_frag(X, zero4()), zero4());
     store_tile_t(tt, LDC, 0, 16, -Tij, lane);
-    if (lane < 32) {
-      const int r = lane >> 1, c8 = (lane & 1) * 8;
-      *reinterpret_cast<bf16x8*>(&scr[r * LDC + c8]) = zero8();
-    }
   }
 }
 
