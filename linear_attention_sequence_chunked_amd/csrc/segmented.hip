@@ -43,85 +43,106 @@ seg_init_kernel(int* __restrict__ cu, float* __restrict__ ident, int B, int T, i
   }
 }
 
-// start_0 = S0 (or 0); start_{s+1} = start_s A_s + N_s.  One workgroup of two
-// wavefronts per (stream, head, 8 state rows).  The rows of start stay in LDS;
-// A_s arrives in one of two LDS buffers by direct global-to-LDS loads issued a
-// step ahead, so the next transition streams in while this one is applied.
-constexpr int kCombThreads = 128;
-constexpr int kCombRows = 8;
+// start_0 = S0 (or 0); start_{s+1} = start_s A_s + N_s.  The rows of the state
+// are independent chains, so one workgroup takes 16 state rows of one (stream,
+// head) with one wavefront per 16 state columns.  The 16 x K row block of start_s
+// sits in LDS (one buffer per parity of s, one barrier per step); each wavefront
+// forms its 16 x 16 tile of start_s A_s + N_s with float32 matrix-core products
+// (16 x 16 x 4 per instruction, two accumulator chains), reading its column tile
+// of A_s and N_s from registers that were loaded during the previous step.
+//
+// Operand layout of the 16 x 16 x 4 float32 product: lane (t = lane % 16,
+// g = lane / 16) supplies the left operand's row t and the right operand's column
+// t at reduction index g, and receives rows 4g .. 4g + 3 of column t.  Reduction
+// index kk = 4m + j of the row block maps to state column k = 16m + 4g + j, so a
+// lane reads its four left operands of a group m as one 16-byte LDS read.
+typedef float comb_f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void fetch_transition(const float* A, float* dst, int K) {
-  // each wave instruction moves 64 lanes x 16 bytes = 1 KB to dst + 256 u floats
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int u = w; u < K * K / 256; u += kCombThreads / 64)
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(A + 256 * u + 4 * lane),
-        (__attribute__((address_space(3))) void*)(dst + 256 * u), 16, 0, 0);
+template <int K>
+struct CombRegs {
+  float a[K / 4];  // A_s[16m + 4g + j][col] at index 4m + j
+  float n[4];      // N_s[row r0 + 4g + i][col]
+};
+
+template <int K>
+__device__ __forceinline__ void comb_load(const float* __restrict__ A, const float* __restrict__ N,
+                                          int col, int g, CombRegs<K>& r) {
+#pragma unroll
+  for (int m = 0; m < K / 16; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.a[4 * m + j] = A[(size_t)(16 * m + 4 * g + j) * K + col];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.n[i] = N[(size_t)(4 * g + i) * K + col];
 }
 
-__global__ void __launch_bounds__(kCombThreads)
+template <int K>
+__global__ void __launch_bounds__(512)
 seg_combine_kernel(const float* __restrict__ s0, const float* __restrict__ Aseg,
-                   const float* __restrict__ Nseg, float* __restrict__ start, int H, int K, int V,
-                   int P) {
-  constexpr int R = kCombRows;
-  extern __shared__ float lds[];
-  const int LK = K + 1;
-  float* cur = lds;                // [R][LK]
-  float* nxt = cur + R * LK;       // [R][LK]
-  float* Ab = nxt + R * LK;        // [2][K][K]
-  const int tid = threadIdx.x;
-  const int r0 = blockIdx.x * R, h = blockIdx.y, b = blockIdx.z;
+                   const float* __restrict__ Nseg, float* __restrict__ start, int H, int V, int P) {
+  constexpr int NT = K * 4, LX = K + 4;
+  __shared__ __attribute__((aligned(16))) float xs[2][16 * LX];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = lane & 15, g = lane >> 4;
+  const int col = 16 * w + t;
+  const int r0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
   const size_t seg0 = (size_t)b * P * H + h;  // segment s of this stream: seg0 + s * H
-  if (P > 1) fetch_transition(Aseg + seg0 * K * K, Ab, K);
-  for (int i = tid; i < R * K; i += kCombThreads) {
-    const int r = i / K, c = i - r * K;
-    cur[r * LK + c] = s0 ? s0[(((size_t)b * H + h) * V + r0 + r) * K + c] : 0.0f;
-  }
-  // thread: rows r and r + R/2, columns c .. c + 3
-  const int r = tid / 32, c = (tid % 32) * 4;
-  for (int s = 0; s < P; ++s) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): A_s is in LDS
-    __syncthreads();
-    const size_t seg = seg0 + (size_t)s * H;
-    for (int i = tid; i < R * K; i += kCombThreads) {
-      const int rr = i / K, cc = i - rr * K;
-      start[(seg * V + r0 + rr) * K + cc] = cur[rr * LK + cc];
-    }
-    if (s + 1 == P) break;
-    if (s + 2 < P) fetch_transition(Aseg + (seg + H) * K * K, Ab + ((s + 1) & 1) * K * K, K);
-    const float* As = Ab + (s & 1) * K * K;
-    if (c < K) {
-      const float* N = Nseg + seg * V * K;
-      float a0[4], a1[4];
+  const size_t rowblk = (size_t)r0 * K;       // offset of row r0 in a [V, K] state
+
+  // start_0: every thread holds four of the 16 x K entries (NT = 4K threads)
+  float x0[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (s0) {
+    const float* src = s0 + (((size_t)b * H + h) * V + r0) * K;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a0[e] = N[(size_t)(r0 + r) * K + c + e];
-        a1[e] = N[(size_t)(r0 + r + R / 2) * K + c + e];
-      }
-      for (int j = 0; j < K; ++j) {
-        const float4 arow = *reinterpret_cast<const float4*>(&As[j * K + c]);
-        const float x0 = cur[r * LK + j], x1 = cur[(r + R / 2) * LK + j];
-        a0[0] = fmaf(x0, arow.x, a0[0]);
-        a0[1] = fmaf(x0, arow.y, a0[1]);
-        a0[2] = fmaf(x0, arow.z, a0[2]);
-        a0[3] = fmaf(x0, arow.w, a0[3]);
-        a1[0] = fmaf(x1, arow.x, a1[0]);
-        a1[1] = fmaf(x1, arow.y, a1[1]);
-        a1[2] = fmaf(x1, arow.z, a1[2]);
-        a1[3] = fmaf(x1, arow.w, a1[3]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        nxt[r * LK + c + e] = a0[e];
-        nxt[(r + R / 2) * LK + c + e] = a1[e];
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < R * K; i += kCombThreads) {
-      const int rr = i / K, cc = i - rr * K;
-      cur[rr * LK + cc] = nxt[rr * LK + cc];
-    }
+    for (int j = 0; j < 4; ++j) x0[j] = src[threadIdx.x + j * NT];
   }
+  // A_s, N_s arrive one step ahead in two register sets used in turn (segment
+  // indices are clamped to the last transition P - 2, so every load is in
+  // bounds; the spare ones go unused)
+  auto load = [&](int s, CombRegs<K>& r) {
+    const size_t sg = seg0 + (size_t)max(0, min(s, P - 2)) * H;
+    comb_load<K>(Aseg + sg * K * K, Nseg + sg * V * K + rowblk, col, g, r);
+  };
+  CombRegs<K> ra, rb;
+  load(0, ra);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = threadIdx.x + j * NT, r = i / K, cc = i - r * K;
+    xs[0][r * LX + cc] = x0[j];
+    start[seg0 * V * K + rowblk + i] = x0[j];
+  }
+  // step s applies `use` (segment s) and loads segment s + 1 into `fill`; N is
+  // added after the products so that no register of `use` is copied
+  auto step = [&](int s, const CombRegs<K>& use, CombRegs<K>& fill) {
+    load(s + 1, fill);
+    __syncthreads();  // start_s complete in xs[s & 1]
+    const float* x = xs[s & 1] + t * LX + 4 * g;
+    comb_f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f};
+    comb_f32x4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < K / 16; ++m) {
+      const float4 xv = *reinterpret_cast<const float4*>(x + 16 * m);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, use.a[4 * m + 0], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, use.a[4 * m + 1], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, use.a[4 * m + 2], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, use.a[4 * m + 3], acc1, 0, 0, 0);
+    }
+    float* xn = xs[(s + 1) & 1];
+    float* out = start + (seg0 + (size_t)(s + 1) * H) * V * K + rowblk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = (acc0[i] + acc1[i]) + use.n[i];
+      xn[(4 * g + i) * LX + col] = v;
+      out[(size_t)(4 * g + i) * K + col] = v;
+    }
+  };
+  // steps s = 0 .. P - 2: whole pairs, then the odd one (each register set a step
+  // loads is read on every path out of its block, so no load is moved later)
+  int s = 0;
+  for (; s + 2 < P; s += 2) {
+    step(s, ra, rb);
+    step(s + 1, rb, ra);
+  }
+  if (s + 1 < P) step(s, ra, rb);
 }
 
 // final_state[b] = end state of segment (b, P - 1).
@@ -208,12 +229,14 @@ hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int P, void* worksp
 
   // 2. true segment starts, in segment order per stream
   {
-    const size_t lds = sizeof(float) * (2 * kCombRows * (a.K + 1) + 2 * (size_t)a.K * a.K);
-    if ((e = hipFuncSetAttribute((const void*)seg_combine_kernel,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(seg_combine_kernel, dim3(a.V / kCombRows, a.H, a.B), dim3(kCombThreads), lds,
-                       stream, a.s0, Aseg, Nseg, start, a.H, a.K, a.V, P);
+    const dim3 grid(a.V / 16, a.H, a.B), block(4 * a.K);
+    switch (a.K) {
+      case 16: hipLaunchKernelGGL(seg_combine_kernel<16>, grid, block, 0, stream, a.s0, Aseg, Nseg, start, a.H, a.V, P); break;
+      case 32: hipLaunchKernelGGL(seg_combine_kernel<32>, grid, block, 0, stream, a.s0, Aseg, Nseg, start, a.H, a.V, P); break;
+      case 64: hipLaunchKernelGGL(seg_combine_kernel<64>, grid, block, 0, stream, a.s0, Aseg, Nseg, start, a.H, a.V, P); break;
+      case 128: hipLaunchKernelGGL(seg_combine_kernel<128>, grid, block, 0, stream, a.s0, Aseg, Nseg, start, a.H, a.V, P); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
 

@@ -33,6 +33,7 @@ CASES = [
     (3, 257, 1, 32, 32, 16, torch.bfloat16, None, 5),
     (1, 777, 2, 16, 64, 16, torch.float32, 0.3, 7),
     (2, 500, 2, 128, 128, 64, torch.float32, 0.05, 1),    # the plain path
+    (2, 300, 2, 64, 16, 32, torch.float32, 0.2, 2),       # one transition
 ]
 
 
@@ -76,17 +77,18 @@ def test_long_context_workload_segmented():
     assert rel_l2(o, ro) <= 2e-2 and rel_l2(sf, rs) <= 2e-2
 
 
-def test_segmented_weak_decay_carries_state_across_segments():
+@pytest.mark.parametrize("K,P", [(64, 6), (128, 9), (32, 2)])
+def test_segmented_weak_decay_carries_state_across_segments(K, P):
     # alpha in (0.995, 1) and small beta: the state carries across hundreds of
     # tokens, so every segment's output depends on the transition A_s of the
     # segments before it
-    inp = make_inputs(2, 900, 2, 64, 64, dtype=torch.float32, seed=620, s0_std=0.3)
+    inp = make_inputs(2, 900, 2, K, 64, dtype=torch.float32, seed=620 + K, s0_std=0.3)
     g = torch.Generator().manual_seed(621)
     inp["alpha"] = 1.0 - 0.005 * torch.rand(inp["alpha"].shape, generator=g)
     inp["beta"] = 0.1 * torch.rand(inp["beta"].shape, generator=g)
     gd = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
     o, sf = chunk_fwd_segmented(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"],
-                                gd["initial_state"], chunk=32, segments=6)
+                                gd["initial_state"], chunk=32, segments=P)
     torch.cuda.synchronize()
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
     eo, es = rel_l2(o, ro), rel_l2(sf, rs)
