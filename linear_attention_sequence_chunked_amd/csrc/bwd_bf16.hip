@@ -175,30 +175,32 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int r = 0; r < 16; ++r) sm.x[16 * bb + r][j] = xv[r];
   }
   __syncthreads();
-  // Off-diagonal blocks by levels d = i - j: X_ij = -T_ii (sum_{j <= m < i} A_im T_mj).
-  // Step one puts the inner sum into the (j, i) block above the diagonal
-  // (scratch); step two multiplies by the diagonal block.  One element per
-  // thread per block.
-  {
-    const int er = tid >> 4, ec = tid & 15;   // element of a 16 x 16 block
-    for (int d = 1; d < 4; ++d) {
-      for (int j = 0; j + d < 4; ++j) {
-        const int i = j + d;
-        float s = 0.0f;
-        for (int m = 16 * j; m < 16 * i; ++m) s = fmaf(sm.a[16 * i + er][m], sm.x[m][16 * j + ec], s);
-        sm.x[16 * j + er][16 * i + ec] = s;   // scratch in the upper (j, i) block
-      }
-      __syncthreads();
-      for (int j = 0; j + d < 4; ++j) {
-        const int i = j + d;
-        float s = 0.0f;
+  // Off-diagonal blocks by levels d = i - j: X_ij = -T_ii (sum_{j <= m < i} A_im T_mj),
+  // in fp32 on the matrix cores (16 x 16 x 4 per instruction: lane (s, g) gives
+  // the left operand's row s and the right operand's column s at reduction index
+  // g, and receives rows 4g .. 4g + 3 of column s).  Wave w takes the pair
+  // (j, i) = (w, w + d) of level d.  Step one puts the inner sum into the (j, i)
+  // block above the diagonal (scratch), which the same wave then reads back to
+  // multiply by the diagonal block; levels are separated by barriers.
+  for (int d = 1; d < 4; ++d) {
+    if (wave + d < 4) {
+      const int j = wave, i = wave + d;
+      f32x4 x = zero4();
+      for (int m0 = 16 * j; m0 < 16 * i; m0 += 4)
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.a[16 * i + ls][m0 + lg], sm.x[m0 + lg][16 * j + ls], x,
+                                                 0, 0, 0);
 #pragma unroll
-        for (int m = 0; m < 16; ++m)   // T_ii is lower triangular: its upper entries are zeros
-          s = fmaf(sm.x[16 * i + er][16 * i + m], sm.x[16 * j + m][16 * i + ec], s);
-        sm.x[16 * i + er][16 * j + ec] = -s;
-      }
-      __syncthreads();
+      for (int e = 0; e < 4; ++e) sm.x[16 * j + 4 * lg + e][16 * i + ls] = x[e];
+      // T_ii is lower triangular: its upper entries are zeros
+      f32x4 y = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.x[16 * i + ls][16 * i + k0 + lg],
+                                                 sm.x[16 * j + k0 + lg][16 * i + ls], y, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.x[16 * i + 4 * lg + e][16 * j + ls] = -y[e];
     }
+    __syncthreads();
   }
   // Tm to the record as bf16, zeros above the diagonal
   for (int p = tid; p < kC * kC / 8; p += 256) {
