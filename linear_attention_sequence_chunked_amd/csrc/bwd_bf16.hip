@@ -245,7 +245,15 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ls = lane & 15, lg = lane >> 4;
-  const int v0 = blockIdx.x * 32, h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware mapping (one-dimensional grid of B * H * V/32): consecutive
+  // workgroup ids go to different XCDs, so the value slices of one (batch, head),
+  // which read the same keys, queries and records, get ids equal modulo 8 (same
+  // XCD, shared L2)
+  int item = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int nsl = V / 32, bh = item / nsl;
+  const int v0 = (item - bh * nsl) * 32, h = bh % H, b = bh / H;
   const int NT = (T + kC - 1) / kC;
   const size_t tokk = (size_t)H * KD, tokv = (size_t)H * V;
   const unsigned char* rec_bh = rec + ((size_t)b * H + h) * NT * (size_t)kRecBytes;
@@ -967,7 +975,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
                        a.beta, rec, a.T, a.H);
     hipError_t r;
     if ((r = hipGetLastError()) != hipSuccess) return r;
-    hipLaunchKernelGGL((bwd16_dstate_kernel<KD>), dim3(a.V / 32, a.H, a.B), dim3(256), 0, stream, q, k,
+    hipLaunchKernelGGL((bwd16_dstate_kernel<KD>), dim3(a.B * a.H * (a.V / 32)), dim3(256), 0, stream, q, k,
                        d_o, a.d_sfinal, a.d_s0, rec, ws_dS, a.T, a.H, a.V);
     if ((r = hipGetLastError()) != hipSuccess) return r;
     if (sd && (r = hipStreamWaitEvent(stream, sd->join, 0)) != hipSuccess) return r;   // states ready

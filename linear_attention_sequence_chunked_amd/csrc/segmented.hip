@@ -84,7 +84,15 @@ seg_combine_kernel(const float* __restrict__ s0, const float* __restrict__ Aseg,
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = lane & 15, g = lane >> 4;
   const int col = 16 * w + t;
-  const int r0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware mapping (one-dimensional grid of B * H * V/16): consecutive
+  // workgroup ids go to different XCDs, so the row blocks of one (stream, head),
+  // which read the same transitions A_s, get ids equal modulo 8 (same XCD, shared
+  // L2)
+  int item = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int nrb = V / 16, bh = item / nrb;
+  const int r0 = (item - bh * nrb) * 16, h = bh % H, b = bh / H;
   const size_t seg0 = (size_t)b * P * H + h;  // segment s of this stream: seg0 + s * H
   const size_t rowblk = (size_t)r0 * K;       // offset of row r0 in a [V, K] state
 
@@ -229,7 +237,7 @@ hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int P, void* worksp
 
   // 2. true segment starts, in segment order per stream
   {
-    const dim3 grid(a.V / 16, a.H, a.B), block(4 * a.K);
+    const dim3 grid(a.B * a.H * (a.V / 16)), block(4 * a.K);
     switch (a.K) {
       case 16: hipLaunchKernelGGL(seg_combine_kernel<16>, grid, block, 0, stream, a.s0, Aseg, Nseg, start, a.H, a.V, P); break;
       case 32: hipLaunchKernelGGL(seg_combine_kernel<32>, grid, block, 0, stream, a.s0, Aseg, Nseg, start, a.H, a.V, P); break;
