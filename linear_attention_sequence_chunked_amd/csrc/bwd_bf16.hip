@@ -11,8 +11,8 @@
 //
 // Launches:
 //   (1) the bf16 forward kernel's states-only instance writes the fp32
-//       chunk-start states S_c; it runs on a second stream, beside (2) and (3),
-//       which do not need it;
+//       chunk-start states S_c; it runs on a second stream after (2) and beside
+//       (3), which does not need it;
 //   (2) prep, one workgroup per chunk: gates, the Gram matrices A = diag(beta) M
 //       and P, Tm = (I + A)^-1 in fp32 by 16 x 16 blocks; record = Tm, P, M
 //       (bf16) and the gates (fp32);
@@ -93,24 +93,38 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   bf16* rp = reinterpret_cast<bf16*>(dst + kRecP);
   bf16* rm = reinterpret_cast<bf16*>(dst + kRecM);
 
-  // keys and queries (zero rows past the end)
-  for (int p = tid; p < kC * KD / 8; p += 256) {
-    const int r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
-    bf16x8 kv = zero8(), qv = zero8();
+  // Every global read is issued before the first LDS write, so the chunk's
+  // loads overlap instead of waiting one after another: keys and queries (zero
+  // rows past the end; NP 16-byte pieces per thread) and, on wave 0, the gates
+  // (padding alpha = 1, beta = 0).
+  constexpr int NP = kC * KD / 8 / 256;
+  bf16x8 kv[NP], qv[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int p = tid + 256 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+    kv[j] = zero8();
+    qv[j] = zero8();
     if (r < n) {
       const size_t off = ((size_t)b * T + t0 + r) * tok + (size_t)h * KD + c8;
-      kv = *reinterpret_cast<const bf16x8*>(k + off);
-      qv = *reinterpret_cast<const bf16x8*>(q + off);
+      kv[j] = *reinterpret_cast<const bf16x8*>(k + off);
+      qv[j] = *reinterpret_cast<const bf16x8*>(q + off);
     }
-    *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv;
-    *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv;
   }
-  // gates: g = cumulative log2(alpha) by a wave scan; padding alpha = 1, beta = 0
-  if (wave == 0) {
+  float al = 1.0f, bt = 0.0f;
+  if (wave == 0 && lane < n) {
     const size_t go = ((size_t)b * T + t0 + lane) * H + h;
-    const float la = lane < n ? __builtin_amdgcn_logf(alpha[go]) : 0.0f;
-    const float g = wave_scan(la, lane);
-    const float bt = lane < n ? beta[go] : 0.0f;
+    al = alpha[go];
+    bt = beta[go];
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int p = tid + 256 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv[j];
+    *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv[j];
+  }
+  // gates: g = cumulative log2(alpha) by a wave scan
+  if (wave == 0) {
+    const float g = wave_scan(__builtin_amdgcn_logf(al), lane);
     sm.g[lane] = g;
     sm.bt[lane] = bt;
     reinterpret_cast<float*>(dst + kRecG)[lane] = g;
@@ -937,8 +951,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   float* ws_S = a.workspace;
   float* ws_dS = ws_S + (size_t)a.B * a.H * NT * a.V * a.K;
   unsigned char* rec = reinterpret_cast<unsigned char*>(ws_dS + (size_t)a.B * a.H * NT * a.V * a.K);
-  hipError_t e;
-  // (1) chunk-start states
+  // (1) chunk-start states (launched after prep, below)
   FwdArgs f;
   f.q = a.q;
   f.k = a.k;
@@ -957,24 +970,26 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   f.vs = 32;
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream* sd = side_stream();
-  hipStream_t st_states = stream;
-  if (sd) {
-    if ((e = hipEventRecord(sd->fork, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return e;
-    st_states = sd->s;
-  }
-  if ((e = launch_fwd_states(f, true, ws_S, st_states)) != hipSuccess) return e;
-  if (sd && (e = hipEventRecord(sd->join, sd->s)) != hipSuccess) return e;
   const bf16* q = static_cast<const bf16*>(a.q);
   const bf16* k = static_cast<const bf16*>(a.k);
   const bf16* v = static_cast<const bf16*>(a.v);
   const bf16* d_o = static_cast<const bf16*>(a.d_o);
   auto run = [&](auto kc) -> hipError_t {
     constexpr int KD = decltype(kc)::value;
+    // (2) prep first, with the whole GPU; then (1) on the side stream beside (3):
+    // the two long walks have one workgroup per CU each and fit side by side
     hipLaunchKernelGGL((bwd16_prep_kernel<KD>), dim3(NT, a.H, a.B), dim3(256), 0, stream, q, k, a.alpha,
                        a.beta, rec, a.T, a.H);
     hipError_t r;
     if ((r = hipGetLastError()) != hipSuccess) return r;
+    hipStream_t st_states = stream;
+    if (sd) {
+      if ((r = hipEventRecord(sd->fork, stream)) != hipSuccess) return r;
+      if ((r = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return r;
+      st_states = sd->s;
+    }
+    if ((r = launch_fwd_states(f, true, ws_S, st_states)) != hipSuccess) return r;
+    if (sd && (r = hipEventRecord(sd->join, sd->s)) != hipSuccess) return r;
     hipLaunchKernelGGL((bwd16_dstate_kernel<KD>), dim3(a.B * a.H * (a.V / 32)), dim3(256), 0, stream, q, k,
                        d_o, a.d_sfinal, a.d_s0, rec, ws_dS, a.T, a.H, a.V);
     if ((r = hipGetLastError()) != hipSuccess) return r;
