@@ -55,6 +55,8 @@ using namespace mfma;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+// Ragged batches of up to this many sequences start their longest sequences first.
+constexpr int kLongestFirstMax = 128;
 
 template <int KD, int VS, int CP>
 struct alignas(16) Smem {
@@ -84,6 +86,8 @@ struct alignas(16) Smem {
   // four blocks read at once by the diagonal solve fall on different banks
   static constexpr int ADS = 256 + 4;
   float ad[NTB * ADS];
+  int lens[kLongestFirstMax];          // ragged batch: sequence lengths (start order)
+  int pick;
 };
 
 // Off-diagonal blocks of Tm = (I + A)^-1 from its diagonal blocks (already in
@@ -290,14 +294,49 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ls = lane & 15, lg = lane >> 4;
 
-  // XCD-aware mapping: consecutive workgroup ids go to different XCDs, so give
-  // the slices of one stream ids that are equal modulo 8 (same XCD, shared L2).
+  // XCD-aware mapping: consecutive workgroup ids go to different XCDs (id mod 8),
+  // so give the slices of one stream ids that are equal modulo 8 (same XCD,
+  // shared L2).  A dense batch gives each XCD a contiguous run of slices (the
+  // heads of one sequence then share the lines of the [B, T, H] gates).  In a
+  // ragged batch, when the (stream, head) pairs divide evenly, pair p goes to
+  // XCD p mod 8 instead, which spreads long and short sequences over all XCDs.
   int item = blockIdx.x;
   const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const bool spread = cu && (nblk / nslice) % 8 == 0;
+  if (spread) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    item = ((slot / nslice) * 8 + xcd) * nslice + slot % nslice;
+  } else if ((nblk & 7) == 0) {
+    item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  }
+  const bool pair_order = spread || (nblk & 7) != 0;  // ids start in pair order
   const int slice = item % nslice;
   const int bh = item / nslice;
-  const int h = bh % H, b = bh / H;
+  const int h = bh % H;
+  int b = bh / H;
+  // Ragged batch: the pair started r-th takes a sequence of length rank r / H
+  // (longest first, equal lengths in table order), so that the longest chains
+  // are not left to start after the short ones.  The ranks come from the
+  // clamped table below and form a permutation, so exactly one thread picks.
+  const int nseq = nblk / (H * nslice);
+  if (cu && pair_order && nseq <= kLongestFirstMax) {
+    for (int j = tid; j < nseq; j += kThreads) {
+      const int s = min(max(cu[j], 0), T), e = min(max(cu[j + 1], s), T);
+      sm.lens[j] = e - s;
+    }
+    __syncthreads();
+    if (tid < nseq) {
+      const int lc = sm.lens[tid];
+      int rank = 0;
+      for (int j = 0; j < nseq; ++j) {
+        const int lj = sm.lens[j];
+        rank += (lj > lc || (lj == lc && j < tid)) ? 1 : 0;
+      }
+      if (rank == b) sm.pick = tid;
+    }
+    __syncthreads();
+    b = sm.pick;
+  }
   const int v0 = slice * VS;
   const size_t tok_k = (size_t)H * K;
   const size_t tok_v = (size_t)H * V;
