@@ -75,3 +75,35 @@ def test_equal_lengths_reproduce_dense_call_bitwise(dt):
     torch.cuda.synchronize()
     assert torch.equal(ov.reshape(od.shape), od)
     assert torch.equal(sv, sd)
+
+
+# Workgroup scheduling of the bf16 kernel depends on the batch shape: (sequence,
+# head) pairs spread over the XCDs when they divide by 8, a plain id order when the
+# workgroups do not, a contiguous run per XCD otherwise; sequences start longest
+# first for up to 128 of them.  Every path must give each sequence its own result.
+SCHEDULE_CASES = [
+    # (lengths, H, K, V)
+    ([70, 5, 300, 64, 129], 1, 64, 32),                   # 10 workgroups: id order, longest first
+    ([90, 90, 7, 250, 250, 33], 2, 64, 128),               # 96 workgroups, 12 pairs: contiguous runs
+    ([40, 40, 40, 3, 3, 160, 160, 1], 1, 32, 32),          # equal lengths: ties in table order
+    ([(7 * i) % 61 + 1 for i in range(136)], 1, 32, 32),   # 136 sequences: spread, table order
+]
+
+
+@pytest.mark.parametrize("case", SCHEDULE_CASES, ids=lambda c: "n%dH%dK%dV%d" % (len(c[0]), c[1], c[2], c[3]))
+def test_ragged_schedule_paths(case):
+    lengths, H, K, V = case
+    print("case varlen schedule n=%d H=%d K=%d V=%d" % (len(lengths), H, K, V), flush=True)
+    parts, cat, cu = packed(lengths, H, K, V, torch.bfloat16, seed=900 + len(lengths))
+    g = {n: t.to(DEV) for n, t in cat.items()}
+    o, sf = chunk_fwd_varlen(g["q"], g["k"], g["v"], g["alpha"], g["beta"], cu.to(DEV),
+                             g["initial_state"], chunk=64)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, (p, L) in enumerate(zip(parts, lengths)):
+        ro, rs = oracle.fwd(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["initial_state"])
+        a, b = int(cu[i]), int(cu[i + 1])
+        eo, es = rel_l2(o[:, a:b], ro), rel_l2(sf[i:i + 1], rs)
+        worst = max(worst, eo, es)
+        assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16], (i, L, eo, es)
+    print("  worst rel L2 %.2e" % worst, flush=True)
