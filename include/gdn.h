@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -138,6 +138,25 @@ GDN_API gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const vo
                                   void *o, float *final_state,
                                   int64_t T, int64_t H, int64_t K, int64_t V,
                                   int64_t chunk, gdn_dtype_t dtype, void *stream);
+
+/*
+ * gdn_chunk_fwd_segments_hint -- a `segments` value for gdn_chunk_fwd_segmented:
+ * the count with the lowest modelled time for these sizes, 1 when the plain call
+ * (gdn_chunk_fwd) is expected to be fastest.  The model: each of the three passes
+ * walks every segment's chunks with one workgroup per compute unit at a time
+ * (about 2.2 us per chunk with 32 value rows per workgroup, 1.86 us with 16, for
+ * bf16 with 64-token chunks on MI355X), and the combine adds about 1.8 us per
+ * segment.  Segments keep at least four chunks each; at most 256.
+ *
+ *   num_cus   compute units to plan for; 0 = those of the current device
+ *             (the only case that makes a runtime call)
+ *
+ * Returns 0 when a size is not positive or the device cannot be queried.  Host
+ * only: nothing is enqueued.  The value is advice; any 1 <= segments <= T is
+ * accepted by gdn_chunk_fwd_segmented.
+ */
+GDN_API int64_t gdn_chunk_fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K,
+                                            int64_t V, int64_t chunk, int64_t num_cus);
 
 /*
  * gdn_chunk_fwd_segmented_workspace_size -- bytes of device workspace that

@@ -744,6 +744,8 @@ int pick_vs(int B, int H, int V) {
 
 }  // namespace
 
+int fwd_bf16_value_slice(int B, int H, int V) { return pick_vs(B, H, V); }
+
 bool fwd_bf16_supported(int K, int V, int chunk) {
   return (K == 16 || K == 32 || K == 64 || K == 128) && (V == 16 || V == 32 || V == 64 || V == 128) &&
          (chunk == 16 || chunk == 32 || chunk == 64);

@@ -148,6 +148,18 @@ gdn_status_t gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
                         H, K, V, chunk, dtype, stream);
 }
 
+int64_t gdn_chunk_fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                    int64_t chunk, int64_t num_cus) {
+  if (num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return 0;
+    num_cus = n;
+  }
+  return gdn::fwd_segments_hint(B, T, H, K, V, chunk, num_cus);
+}
+
 size_t gdn_chunk_fwd_segmented_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K,
                                               int64_t V, int64_t chunk, int64_t segments) {
   if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0 || segments <= 0) return 0;

@@ -63,9 +63,16 @@ bool bwd_bf16_supported(int K, int V, int chunk);
 size_t bwd_bf16_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
+// Value rows per workgroup (16 or 32) that the bf16 forward picks for a dense call.
+int fwd_bf16_value_slice(int B, int H, int V);
+
 // Segment-parallel forward (P segments per sequence) with a caller workspace.
 size_t fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                      int64_t chunk, int64_t segments);
+// Segment count with the lowest modelled time on `cus` compute units (1 = the
+// plain call is expected to be fastest).
+int64_t fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk,
+                          int64_t cus);
 hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int segments, void* workspace,
                                 hipStream_t stream);
 

@@ -197,6 +197,40 @@ SegLayout seg_layout(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int6
 
 }  // namespace
 
+// Modelled time of the plain call (P = 1) and of the segmented one.  A forward
+// pass over streams of n chunks takes rounds * n * t_chunk: one workgroup per CU
+// (the bf16 kernel fills a CU's LDS), rounds = ceil(workgroups / CUs), and
+// t_chunk = 2.2 us with 32 value rows per workgroup or 1.86 us with 16 (bf16,
+// K = 128, 64-token chunks, measured on MI355X; scaled by chunk / 64 here).  The
+// segmented call is three such passes over the segments (the A pass with K state
+// rows) plus P - 1 combine steps of about 1.8 us.
+int64_t fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk,
+                          int64_t cus) {
+  if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0 || cus <= 0) return 0;
+  if (B * H > (INT64_C(1) << 24)) return 1;  // that many streams fill the GPU by themselves
+  const double scale = (double)chunk / 64.0;
+  auto pass = [&](int64_t streams, int64_t rows, int64_t nchunks) {
+    if (streams > (INT64_C(1) << 24)) return 1e30;  // beyond any useful segment count
+    const int vs = fwd_bf16_value_slice((int)streams, (int)H, (int)rows);
+    const int64_t wgs = streams * H * ((rows + vs - 1) / vs);
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    return (double)rounds * (double)nchunks * (vs == 32 ? 2.2 : 1.86) * scale;
+  };
+  const int64_t nch = (T + chunk - 1) / chunk;
+  double best = pass(B, V, nch);
+  int64_t best_p = 1;
+  // at least four chunks per segment, at most 256 segments
+  for (int64_t P = 2; P <= 256 && 4 * P <= nch; ++P) {
+    const int64_t L = ((T + P - 1) / P + chunk - 1) / chunk;  // chunks per segment
+    const double t = pass(B * P, V, L) + pass(B * P, K, L) + pass(B * P, V, L) + 1.8 * (double)(P - 1);
+    if (t < best) {
+      best = t;
+      best_p = P;
+    }
+  }
+  return best_p;
+}
+
 size_t fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                      int64_t chunk, int64_t segments) {
   return seg_layout(B, T, H, K, V, chunk, segments).bytes;

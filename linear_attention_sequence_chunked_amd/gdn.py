@@ -38,6 +38,7 @@ SIGNATURES = {
     "gdn_chunk_fwd": (ctypes.c_int, [_VP] * 8 + [_I64] * 6 + [ctypes.c_int, _VP]),
     "gdn_chunk_fwd_varlen": (ctypes.c_int, [_VP] * 6 + [_I64] + [_VP] * 3 + [_I64] * 5 +
                              [ctypes.c_int, _VP]),
+    "gdn_chunk_fwd_segments_hint": (ctypes.c_int64, [_I64] * 7),
     "gdn_chunk_fwd_segmented_workspace_size": (ctypes.c_size_t, [_I64] * 7),
     "gdn_chunk_fwd_segmented": (ctypes.c_int, [_VP] * 8 + [_I64] * 7 + [_VP, ctypes.c_size_t] +
                                 [ctypes.c_int, _VP]),
@@ -290,17 +291,24 @@ def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, chunk
     return out, final_state
 
 
+def segments_hint(B: int, T: int, H: int, K: int, V: int, chunk: int = 64, num_cus: int = 0) -> int:
+    """Segment count ``gdn_chunk_fwd_segments_hint`` suggests (1: the plain call);
+    ``num_cus`` = 0 plans for the current device.  0 when a size is not positive."""
+    return int(load_library().gdn_chunk_fwd_segments_hint(B, T, H, K, V, chunk, num_cus))
+
+
 def segmented_workspace_size(B: int, T: int, H: int, K: int, V: int, chunk: int, segments: int) -> int:
     """Bytes of device workspace ``gdn_chunk_fwd_segmented`` needs."""
     return int(load_library().gdn_chunk_fwd_segmented_workspace_size(B, T, H, K, V, chunk, segments))
 
 
 def chunk_fwd_segmented(q, k, v, alpha, beta, initial_state=None, chunk: int = 64,
-                        segments: int = 2, *, out=None, final_state=None,
+                        segments=None, *, out=None, final_state=None,
                         want_final_state: bool = True, workspace=None, stream=None):
     """:func:`chunk_fwd` computed segment-parallel (``gdn_chunk_fwd_segmented``):
     each sequence is split into ``segments`` pieces processed in parallel, joined by
-    their affine state maps.  Returns ``(o, final_state)``."""
+    their affine state maps (``None``: the count :func:`segments_hint` gives for the
+    tensors' device).  Returns ``(o, final_state)``."""
     lib = load_library()
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a 4-D tensor [B,T,H,K]")
@@ -327,6 +335,9 @@ def chunk_fwd_segmented(q, k, v, alpha, beta, initial_state=None, chunk: int = 6
         final_state = torch.empty((B, H, V, K), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check(final_state, "final_state", (B, H, V, K), torch.float32, dev)
+    if segments is None:
+        with torch.cuda.device(dev):
+            segments = max(1, int(lib.gdn_chunk_fwd_segments_hint(B, T, H, K, V, int(chunk), 0)))
     need = int(lib.gdn_chunk_fwd_segmented_workspace_size(B, T, H, K, V, int(chunk), int(segments)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = gdn.load_library()
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
     for code in range(4):
         assert len(gdn.status_string(code)) > 0
     assert gdn.status_string(99) == "unknown status"
@@ -212,3 +212,19 @@ def test_segmented_rejects_bad_arguments():
     assert scall(null="q") == gdn.GDN_ERROR_INVALID_VALUE
     assert scall(K=48) == gdn.GDN_ERROR_NOT_SUPPORTED
     assert scall(segments=2000) == gdn.GDN_ERROR_NOT_SUPPORTED                             # more than T
+
+
+def test_segments_hint_follows_the_cost_model():
+    # host only (num_cus given): the counts the cost model picks for the measured
+    # shapes, 1 for a batch that fills the GPU by itself, 0 for invalid sizes
+    hint = gdn.segments_hint
+    assert hint(1, 32768, 2, 128, 128, 64, num_cus=256) == 32    # B1 T32768 H2: 0.19 vs 0.97 ms
+    assert hint(1, 32768, 16, 128, 128, 64, num_cus=256) == 4    # B1 T32768 H16: 0.79 vs 0.99 ms
+    assert hint(8, 4096, 6, 128, 128, 64, num_cus=256) == 1      # the training shape
+    assert hint(1, 100, 2, 128, 128, 64, num_cus=256) == 1       # too short to split
+    assert hint(1, 32768, 2, 128, 128, 64, num_cus=512) >= 32    # more CUs, no fewer segments
+    assert hint(0, 32768, 2, 128, 128, 64, num_cus=256) == 0
+    assert hint(1, 32768, 2, 128, 128, -1, num_cus=256) == 0
+    for args in [(1, 5000, 3, 64, 32, 32), (2, 70000, 1, 16, 16, 16), (1, 8192, 4, 128, 64, 64)]:
+        P = hint(*args, num_cus=256)
+        assert 1 <= P <= 256 and (P == 1 or 4 * P <= -(-args[1] // args[5]))

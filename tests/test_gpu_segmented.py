@@ -94,3 +94,19 @@ def test_segmented_weak_decay_carries_state_across_segments(K, P):
     eo, es = rel_l2(o, ro), rel_l2(sf, rs)
     print("  weak decay rel L2 o=%.2e final_state=%.2e" % (eo, es), flush=True)
     assert eo <= 1e-5 and es <= 1e-5
+
+
+def test_segment_count_from_the_hint():
+    # segments=None takes gdn_chunk_fwd_segments_hint for the device; on a
+    # few-stream sequence it splits, and the result still matches the oracle
+    inp = make_inputs(1, 4096, 2, 128, 128, dtype=torch.bfloat16, seed=630, s0_std=0.05)
+    from linear_attention_sequence_chunked_amd import segments_hint
+    P = segments_hint(1, 4096, 2, 128, 128, 64)
+    print("hint for B1 T4096 H2: %d segments" % P, flush=True)
+    assert P > 1
+    g = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
+    o, sf = chunk_fwd_segmented(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["initial_state"],
+                                chunk=64)
+    torch.cuda.synchronize()
+    ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
+    assert rel_l2(o, ro) <= TOL[torch.bfloat16] and rel_l2(sf, rs) <= TOL[torch.bfloat16]
