@@ -193,9 +193,9 @@ def bench_backward(args):
         b.record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    # bf16 inputs with chunk >= 64 take the MFMA path (64-token chunks, bf16
+    # bf16 inputs with K, V >= 32 take the MFMA path (64-token chunks, bf16
     # operands, fp32 accumulation); otherwise the fp32 path with 32-token chunks
-    mfma = w.dtype == torch.bfloat16 and C >= 64
+    mfma = w.dtype == torch.bfloat16 and K >= 32 and V >= 32
     bwd_c = 64 if mfma else min(C, 32)
     flops = backward_flops(B, T, H, K, V, bwd_c)
     peak = 2500.0 if mfma else 157.3

@@ -233,8 +233,8 @@ GDN_API gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v
  * float32 [V, K] states and the chunk's float32 factors (three C x C matrices and
  * three C-vectors):
  *     B * H * ceil(T / C) * (2 * V * K + 3 * C * C + 3 * C) * 4 bytes.
- * When chunk >= 64 and K, V are 32, 64 or 128, bfloat16 inputs take the MFMA path
- * with 64-token chunks: per (batch, head, chunk) two float32 [V, K] states and a
+ * When K and V are 32, 64 or 128, bfloat16 inputs take the MFMA path with
+ * 64-token chunks: per (batch, head, chunk) two float32 [V, K] states and a
  * 25088-byte record (three bf16 64 x 64 matrices, two float32 64-vectors):
  *     B * H * ceil(T / 64) * (2 * V * K * 4 + 25088) bytes.
  * Returns 0 when a size is not positive.
@@ -265,9 +265,10 @@ GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int
  * fp32 chunk-boundary states) and "Sparse Delta Memory: layer and kernels",
  * sections "What the layer computes" and "Execution" (the backward walks the
  * chunks in reverse).  Float32 inputs: all arithmetic float32.  Bfloat16 inputs
- * with chunk >= 64 and K, V in {32, 64, 128}: 64-token chunks, matrix products
- * on bf16 MFMA with bf16 operands and float32 accumulation, everything else
- * float32 (other bf16 shapes: the float32 path).  Every sum has a fixed order,
+ * with K, V in {32, 64, 128}: 64-token chunks whatever `chunk` is (the chunk size
+ * changes results only by rounding), matrix products on bf16 MFMA with bf16
+ * operands and float32 accumulation, everything else float32 (K or V = 16: the
+ * float32 path).  Every sum has a fixed order,
  * so results are bitwise reproducible; dq, dk, dv are rounded to dtype once.
  * The MFMA path runs two independent sequential walks side by side: it forks
  * from `stream` to a second stream of the library's (one per device, created on

@@ -707,13 +707,13 @@ size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V
   const int64_t C = chunk < kBwdC ? chunk : kBwdC;
   const int64_t NT = (T + C - 1) / C;
   const size_t scalar = (size_t)(2 * B * H * NT * V * K + B * H * NT * factor_floats((int)C)) * sizeof(float);
-  if (!bwd_bf16_supported((int)K, (int)V, (int)chunk)) return scalar;
+  if (!bwd_bf16_supported((int)K, (int)V)) return scalar;
   const size_t mfma = bwd_bf16_workspace_bytes(B, T, H, K, V);
   return scalar > mfma ? scalar : mfma;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
-  if (bf16 && bwd_bf16_supported(a.K, a.V, a.chunk)) return launch_bwd_bf16(a, stream);
+  if (bf16 && bwd_bf16_supported(a.K, a.V)) return launch_bwd_bf16(a, stream);
   return bf16 ? launch_bwd_t<__hip_bfloat16>(a, stream) : launch_bwd_t<float>(a, stream);
 }
 

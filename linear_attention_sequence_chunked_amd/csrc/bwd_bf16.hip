@@ -903,8 +903,8 @@ hipError_t with_kd(int K, F&& f) {
 
 }  // namespace
 
-bool bwd_bf16_supported(int K, int V, int chunk) {
-  return chunk >= kC && (K == 32 || K == 64 || K == 128) && (V == 32 || V == 64 || V == 128);
+bool bwd_bf16_supported(int K, int V) {
+  return (K == 32 || K == 64 || K == 128) && (V == 32 || V == 64 || V == 128);
 }
 
 size_t bwd_bf16_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
@@ -946,7 +946,7 @@ SideStream* side_stream() {
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
-  if (!bwd_bf16_supported(a.K, a.V, a.chunk)) return hipErrorInvalidValue;
+  if (!bwd_bf16_supported(a.K, a.V)) return hipErrorInvalidValue;
   const int NT = (a.T + kC - 1) / kC;
   float* ws_S = a.workspace;
   float* ws_dS = ws_S + (size_t)a.B * a.H * NT * a.V * a.K;

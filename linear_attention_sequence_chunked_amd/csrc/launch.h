@@ -56,10 +56,10 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 
-// Bfloat16 backward on MFMA with 64-token chunks (chunk >= 64; K and V 32, 64 or
-// 128).  Workspace: chunk-start states, chunk-end state gradients, per-chunk
-// records.
-bool bwd_bf16_supported(int K, int V, int chunk);
+// Bfloat16 backward on MFMA with 64-token chunks, whatever chunk the caller gave
+// (K and V 32, 64 or 128).  Workspace: chunk-start states, chunk-end state
+// gradients, per-chunk records.
+bool bwd_bf16_supported(int K, int V);
 size_t bwd_bf16_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 

@@ -125,12 +125,15 @@ def test_bwd_workspace_size():
     assert lib.gdn_chunk_bwd_workspace_size(1, 17, 1, 16, 16, 16) == \
         2 * (2 * 16 * 16 + 3 * 16 * 16 + 3 * 16) * 4
     assert lib.gdn_chunk_bwd_workspace_size(0, 17, 1, 16, 16, 16) == 0
-    # chunk >= 64 with supported K, V: the larger of that layout and the bf16
-    # MFMA layout (per 64-token chunk two fp32 [V,K] states and a 25088-byte
-    # record: Tm, P, M as bf16 C x C, gates as fp32)
-    assert lib.gdn_chunk_bwd_workspace_size(1, 1, 1, 128, 128, 64) == 2 * 128 * 128 * 4 + 25088
+    # K, V in {32, 64, 128}: the larger of that layout and the bf16 MFMA layout
+    # (per 64-token chunk two fp32 [V,K] states and a 25088-byte record: Tm, P, M
+    # as bf16 C x C, gates as fp32), whatever the chunk
+    mfma = 2 * 128 * 128 * 4 + 25088
+    assert lib.gdn_chunk_bwd_workspace_size(1, 1, 1, 128, 128, 64) == mfma
     assert lib.gdn_chunk_bwd_workspace_size(1, 1, 1, 128, 128, 32) == \
-        (2 * 128 * 128 + 3 * 32 * 32 + 3 * 32) * 4
+        max(mfma, (2 * 128 * 128 + 3 * 32 * 32 + 3 * 32) * 4)
+    assert lib.gdn_chunk_bwd_workspace_size(1, 256, 1, 128, 128, 16) == \
+        max(4 * mfma, 16 * (2 * 128 * 128 + 3 * 16 * 16 + 3 * 16) * 4)
 
 
 def test_bwd_rejects_bad_arguments():

@@ -82,7 +82,7 @@ def test_bwd_shape_sweep(case, gate):
     check(inp, C, TOL[dt], "sweep", d_sf)
 
 
-# bf16 inputs with chunk >= 64 take the MFMA backward (64-token chunks): every
+# bf16 inputs with K, V >= 32 take the MFMA backward (64-token chunks): every
 # compiled (K, V) pair, ragged tails, several chunks
 MFMA_SWEEP = [
     # (B, T, H, K, V, chunk)
@@ -156,3 +156,14 @@ def test_bwd_mfma_on_a_side_stream_matches_default_stream():
     s.synchronize()
     for x, y in zip(ref, got):
         assert torch.equal(x, y)
+
+
+def test_bwd_bf16_chunk_argument_keeps_the_mfma_path():
+    # bf16 inputs with K, V >= 32 run the MFMA backward with 64-token chunks
+    # whatever chunk is asked for, so every chunk gives the same bits
+    inp = make_inputs(2, 150, 2, 64, 32, dtype=torch.bfloat16, seed=640, s0_std=0.05, with_do=True)
+    outs = {C: gpu_bwd(inp, C) for C in (16, 32, 64)}
+    for C in (16, 32):
+        for n in NAMES:
+            assert torch.equal(outs[C][n], outs[64][n]), (C, n)
+    check(inp, 16, TOL[torch.bfloat16], "chunk16 on the MFMA path")
