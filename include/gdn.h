@@ -128,8 +128,13 @@ GDN_API gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v,
  *                                       every sequence start)
  *
  * Equal (bitwise) to N separate gdn_chunk_fwd calls with B = 1.  "OpenGDN 0.1.0",
- * section "Scope", lists packed variable-length batches as outside its operator;
- * this entry point adds them with the same per-sequence contract.
+ * section "Scope", lists packed variable-length batches and reset masks as outside
+ * its operator; this entry point adds the first with the same per-sequence
+ * contract and covers the second: a reset before token t (the state set to zero,
+ * then the token applied) is a sequence boundary at t whose piece starts from a
+ * zero initial state, so a batch with resets is one call with a boundary at every
+ * row start and every reset (initial states: the row's own for its first piece,
+ * zeros for the others; its final state is that of its last piece).
  */
 GDN_API gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v,
                                   const float *alpha, const float *beta,

@@ -107,3 +107,38 @@ def test_ragged_schedule_paths(case):
         worst = max(worst, eo, es)
         assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16], (i, L, eo, es)
     print("  worst rel L2 %.2e" % worst, flush=True)
+
+
+def test_reset_mask_as_packed_sequences():
+    # rows of a [B, T] batch with resets (state set to zero before the token):
+    # boundaries at every row start and reset, the row's own initial state for
+    # its first piece and zeros for the others; each row's final state is its
+    # last piece's.  The oracle runs every piece on its own.
+    B, T, H, K, V = 3, 400, 2, 64, 64
+    inp = make_inputs(B, T, H, K, V, dtype=torch.bfloat16, seed=650, s0_std=0.05)
+    r = np.random.default_rng(651)
+    reset = r.random((B, T)) < 0.01
+    reset[:, 0] = False
+    starts, s0, last = [], [], []
+    for b in range(B):
+        cuts = [0] + [int(t) for t in np.nonzero(reset[b])[0]]
+        for j, c in enumerate(cuts):
+            starts.append(b * T + c)
+            s0.append(inp["initial_state"][b] if j == 0 else torch.zeros(H, V, K))
+        last.append(len(starts) - 1)
+    cu = torch.tensor(starts + [B * T], dtype=torch.int32)
+    flat = {n: inp[n].reshape((1, B * T) + tuple(inp[n].shape[2:])).contiguous()
+            for n in ("q", "k", "v", "alpha", "beta")}
+    print("case reset mask: %d pieces from %d resets" % (len(starts), int(reset.sum())), flush=True)
+    g = {n: t.to(DEV) for n, t in flat.items()}
+    o, sf = chunk_fwd_varlen(g["q"], g["k"], g["v"], g["alpha"], g["beta"], cu.to(DEV),
+                             torch.stack(s0).to(DEV), chunk=64)
+    torch.cuda.synchronize()
+    for i in range(len(starts)):
+        a, e = int(cu[i]), int(cu[i + 1])
+        piece = {n: flat[n][:, a:e] for n in flat}
+        ro, rs = oracle.fwd(piece["q"], piece["k"], piece["v"], piece["alpha"], piece["beta"],
+                            s0[i].unsqueeze(0))
+        assert rel_l2(o[:, a:e], ro) <= TOL[torch.bfloat16], i
+        if i in last:
+            assert rel_l2(sf[i:i + 1], rs) <= TOL[torch.bfloat16], i
