@@ -132,6 +132,19 @@ def cpu_model():
     return None
 
 
+def oracle_baseline(call, tokens, streams, sample, repeats=1):
+    """The fp64 CPU oracle timed on the host: call(nthreads) runs it once over the
+    sample (threads over the streams); tokens/s over `repeats` calls."""
+    import oracle
+    used = max(1, min(oracle.default_threads(), streams))
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        call(used)
+    dt = (time.perf_counter() - t0) / repeats
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": sample % dt, "cpu_model": cpu_model()}
+
+
 def algorithmic_flops(B, T, H, K, V, C):
     """Structural FLOPs per token-head of the chunk algorithm (triangular products at
     their structural size, the inverse as C^3/3 per chunk):
@@ -201,6 +214,14 @@ def bench_backward(args):
     peak = 2500.0 if mfma else 157.3
     tok = B * T * H
     abytes = tok * (4 * K * 2 + 3 * K * 2 + 2 * 4 + 2 * 4) + B * H * V * K * 4  # q,k,v,dO,gates in; dq,dk,dv,dgates out; dS0
+    cpub = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cpub = oracle_baseline(
+            lambda n: oracle.bwd(cpu["q"], cpu["k"], cpu["v"], cpu["alpha"], cpu["beta"], cpu["d_o"],
+                                 cpu["initial_state"], nthreads=n),
+            B * T, B * H, "whole workload (%d streams x %d tokens), fp64 reverse mode with fp64 "
+                          "checkpoints every 64 tokens, %%.2f s" % (B * H, T))
     print(json.dumps({
         "metric": "GDN chunk bwd tokens/s at B4\u00b7T2048\u00b7H6\u00b7d128",
         "value": B * T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -212,6 +233,7 @@ def bench_backward(args):
                      "peak": peak, "unit": "TFLOP/s", "frac": flops / (ms / 1e3) / 1e12 / peak,
                      "traffic": None, "algorithmic_flops": flops,
                      "hbm_gbs_algorithmic": abytes / (ms / 1e3) / 1e9},
+        "cpu_baseline": cpub,
         "gate": gate,
     }), flush=True)
 
@@ -304,6 +326,15 @@ def bench_decode(args):
     ms = t0.elapsed_time(t1) / args.steps
     abytes = B * H * (2 * V * K * 4 + (2 * K + 2 * V) * 2 + 8)
     gbs = abytes / (kern_ms / 1e3) / 1e9
+    cpub = None
+    if not args.no_cpu_baseline:
+        import oracle
+        reps = 5
+        cpub = oracle_baseline(
+            lambda n: oracle.fwd(cpu["q"], cpu["k"], cpu["v"], cpu["alpha"], cpu["beta"],
+                                 cpu["initial_state"], nthreads=n),
+            B, B * H, "one token for all %d streams (the same step), fp64, %d calls of %%.4f s" % (B * H, reps),
+            repeats=reps)
     print(json.dumps({
         "metric": "GDN decode step tokens/s at B64\u00b7H16\u00b7d128",
         "value": B / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -314,6 +345,7 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel_ms": kern_ms,
                      "algorithmic_bytes": abytes},
+        "cpu_baseline": cpub,
         "gate": gate,
     }), flush=True)
 
@@ -378,6 +410,19 @@ def bench_varlen(args):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     abytes = T * H * 1032 + N * H * V * K * 4
     longest_chunks = -(-max(lengths) // C)
+    cpub = None
+    if not args.no_cpu_baseline:
+        import oracle
+        bounds = np.concatenate([[0], np.cumsum(lengths)])
+
+        def every_sequence(n):
+            for i in range(N):
+                a, b = int(bounds[i]), int(bounds[i + 1])
+                oracle.fwd(*(inp[nm][:, a:b].contiguous() for nm in ("q", "k", "v", "alpha", "beta")),
+                           nthreads=n)
+        cpub = oracle_baseline(every_sequence, T, H,
+                               "whole workload (%d sequences one after another, threads over the %d "
+                               "heads), fp64 token loop, %%.2f s" % (N, H))
     print(json.dumps({
         "metric": "GDN chunk fwd (packed ragged batch) tokens/s",
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -390,6 +435,7 @@ def bench_varlen(args):
                      "unit": "GB/s", "frac": abytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes": abytes},
         "us_per_chunk_of_longest": ms * 1e3 / longest_chunks,
+        "cpu_baseline": cpub,
         "gate": gate,
     }), flush=True)
 
