@@ -667,14 +667,17 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       {
         const int c = x + 1;  // chunk whose Gram is built now
         // plan: (type, rows) per Gram wave.  type 0: A = K K^T, type 1: P = Q K^T.
-        // Four token blocks are split as rows {0, 3} and {1, 2} for balance.
+        // Four token blocks are split as rows {0, 3} and {1, 2} for balance.  P
+        // goes to the Gram waves that share a SIMD with the chain waves and A,
+        // whose epilogue is the longer one, to those beside the levels and
+        // diagonal waves (2-3% faster than the other way round).
         if (c >= 0 && c < NT) {
           if constexpr (NTB == 4) {
             switch (gw) {
-              case 0: gram_rows<KD, CP, 0, 0, 3>(sm, c, lane); break;
-              case 1: gram_rows<KD, CP, 0, 1, 2>(sm, c, lane); break;
-              case 2: if constexpr (WO) gram_rows<KD, CP, 1, 0, 3>(sm, c, lane); break;
-              case 3: if constexpr (WO) gram_rows<KD, CP, 1, 1, 2>(sm, c, lane); break;
+              case 0: if constexpr (WO) gram_rows<KD, CP, 1, 0, 3>(sm, c, lane); break;
+              case 1: if constexpr (WO) gram_rows<KD, CP, 1, 1, 2>(sm, c, lane); break;
+              case 2: gram_rows<KD, CP, 0, 0, 3>(sm, c, lane); break;
+              case 3: gram_rows<KD, CP, 0, 1, 2>(sm, c, lane); break;
               default: break;
             }
           } else {
