@@ -287,6 +287,11 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // while chunks are staged
   constexpr int W_GATE = W_G0 + (NG >= 3 ? 2 : 0);
   static_assert(NG >= 2, "need at least two Gram waves");
+  // Issue priority with outputs, 64-token chunks and two chain waves: the Gram
+  // waves that build A first, then the chain waves, then the rest (6% faster
+  // than equal priorities on the training shape).  Equal priorities are faster
+  // for the states-only instance, one chain wave and 32-token chunks.
+  constexpr bool kPrio = WO && NTB == 4 && NCH == 2;
   __shared__ SM sm;
 
   const int tid = threadIdx.x;
@@ -474,6 +479,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     // Everything that depends on the state stays in registers: the state (as
     // S^T tiles), R and U become MFMA operands through permlane swaps.  Only
     // the chunk's K, Q, V, gates, Tm and P come from LDS.
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
     // the two pipeline-fill iterations (x = -2, -1) have no chain work
     for (int i = 0; i < 4; ++i) lds_barrier();
     for (int x = 0; x < NT; ++x) {
@@ -662,6 +668,8 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     StageRegs R;
     load_chunk(0, R);
     const int gw = wave - W_G0;
+    if constexpr (kPrio)
+      if (gw >= 2 && gw <= 3) __builtin_amdgcn_s_setprio(2);  // the A waves
     for (int x = -2; x < NT; ++x) {
       lds_barrier();
       {
