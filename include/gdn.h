@@ -98,7 +98,8 @@ GDN_API const char *gdn_status_string(gdn_status_t status);
  * the next call's initial_state continues the stream ("OpenGDN 0.1.0", section
  * "Core operator reference").  The result is bitwise reproducible run to run:
  * every output element has one writer and every sum runs in a fixed order.
- * Sizes: B*T*H*max(K,V) must stay below 2^31 elements.
+ * Sizes: B*T*H*max(K,V) must stay below 2^31 elements and the state B*H*V*K
+ * at or below 2^31; larger calls return GDN_ERROR_NOT_SUPPORTED.
  */
 GDN_API gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *alpha, const float *beta,

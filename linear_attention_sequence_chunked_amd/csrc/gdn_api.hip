@@ -54,7 +54,7 @@ const char* gdn_status_string(gdn_status_t status) {
              "not 16-byte aligned, or an output overlaps another buffer";
     case GDN_ERROR_NOT_SUPPORTED:
       return "not supported: K and V must be 16, 32, 64 or 128, chunk 16, 32 or 64, dtype F32 "
-             "or BF16, and B*T*H*max(K,V) below 2^31";
+             "or BF16, B*T*H*max(K,V) below 2^31 and B*H*V*K at most 2^31";
     case GDN_ERROR_LAUNCH:
       return "kernel launch failed";
   }

@@ -115,3 +115,37 @@ def workload_inputs(w: Workload | str, **overrides) -> dict:
              s0_std=w.s0_std, with_do=w.with_do)
     p.update(overrides)
     return make_inputs(**p)
+
+
+def make_inputs_on_device(B: int, T: int, H: int, K: int, V: int, device, dtype=torch.bfloat16,
+                          seed: int = 0, gate: str = "decay", slab_tokens: int = 1 << 16) -> dict:
+    """Draw a seeded input set directly in device memory, for sizes whose float32
+    draws would not fit the host comfortably (gigabytes per token tensor).
+
+    The same distributions as make_inputs (unit-norm q and k normalised in
+    float32, decay or sigmoid alpha, sigmoid beta, no initial state), drawn with a
+    device generator slab by slab along the token axis, so the float32 scratch
+    stays at one slab.  The values differ from make_inputs' for the same seed;
+    whoever checks them copies the tensors it needs back to the host.
+    """
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    q = torch.empty(B, T, H, K, dtype=dtype, device=device)
+    k = torch.empty(B, T, H, K, dtype=dtype, device=device)
+    v = torch.empty(B, T, H, V, dtype=dtype, device=device)
+    for t0 in range(0, T, slab_tokens):
+        t1 = min(T, t0 + slab_tokens)
+        for dst, d in ((q, K), (k, K)):
+            x = torch.randn(B, t1 - t0, H, d, generator=g, dtype=torch.float32, device=device)
+            dst[:, t0:t1] = (x / x.norm(dim=-1, keepdim=True)).to(dtype)
+        v[:, t0:t1] = torch.randn(B, t1 - t0, H, V, generator=g, dtype=torch.float32,
+                                  device=device).to(dtype)
+    a_logit = torch.randn(B, T, H, generator=g, dtype=torch.float32, device=device)
+    b_logit = torch.randn(B, T, H, generator=g, dtype=torch.float32, device=device)
+    if gate == "sigmoid":
+        alpha = torch.sigmoid(a_logit)
+    elif gate == "decay":
+        alpha = torch.exp(-0.1 * torch.nn.functional.softplus(a_logit))
+    else:
+        raise ValueError("gate must be 'sigmoid' or 'decay'")
+    return {"q": q, "k": k, "v": v, "alpha": alpha.contiguous(),
+            "beta": torch.sigmoid(b_logit).contiguous(), "initial_state": None, "d_o": None}

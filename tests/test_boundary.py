@@ -77,7 +77,9 @@ def test_misaligned_pointer_is_invalid():
 
 
 @pytest.mark.parametrize("kw", [{"K": 48}, {"V": 256}, {"K": 8}, {"chunk": 128}, {"chunk": 24},
-                                {"dtype": 7}, {"B": 1 << 20, "T": 1 << 12, "H": 8}])
+                                {"dtype": 7}, {"B": 1 << 20, "T": 1 << 12, "H": 8},
+                                # state [B, H, V, K] above 2^31 elements (tokens well below)
+                                {"B": 8193, "T": 1, "H": 16, "K": 128, "V": 128}])
 def test_unsupported_configurations(kw):
     assert call(**kw) == gdn.GDN_ERROR_NOT_SUPPORTED
 
