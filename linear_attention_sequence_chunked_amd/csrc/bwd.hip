@@ -155,8 +155,9 @@ bwd_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   float* sgam = sg + C;
   float* sb = sgam + C;
   const int tid = threadIdx.x;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int NT = (T + C - 1) / C;
+  // one-dimensional grid over (chunk, head, batch), chunk fastest
+  const int c = blockIdx.x % NT, h = (blockIdx.x / NT) % H, b = blockIdx.x / NT / H;
   const int t0 = c * C;
   const int n = min(C, T - t0);
   for (int i = tid; i < n * K; i += kThreads) {
@@ -223,9 +224,11 @@ bwd_dstate_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
   float* sb = sgam + C;
 
   const int tid = threadIdx.x;
-  const int v0 = blockIdx.x * VS;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // one-dimensional grid over (value slice, head, batch), value slice fastest
+  const int nvs = V / VS;
+  const int v0 = (blockIdx.x % nvs) * VS;
+  const int h = (blockIdx.x / nvs) % H;
+  const int b = blockIdx.x / nvs / H;
   const int NT = (T + C - 1) / C;
   const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
 
@@ -406,10 +409,11 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   float* sred = sdg + C;           // [kThreads] reduction scratch
 
   const int tid = threadIdx.x;
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
   const int NT = (T + C - 1) / C;
+  // one-dimensional grid over (chunk, head, batch), chunk fastest
+  const int c = blockIdx.x % NT;
+  const int h = (blockIdx.x / NT) % H;
+  const int b = blockIdx.x / NT / H;
   const int t0 = c * C;
   const int n = min(C, T - t0);
   const size_t ck = (((size_t)b * H + h) * NT + c) * (size_t)V * K;
@@ -658,7 +662,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     const size_t LK = a.K + 1;
     const size_t lds = sizeof(float) * (2 * C * LK + 3 * C * C + 3 * C);
     if ((e = set_lds_limit<TIn>((const void*)bwd_prep_kernel<TIn>)) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_prep_kernel<TIn>, dim3(NT, a.H, a.B), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL(bwd_prep_kernel<TIn>, dim3(NT * a.H * a.B), dim3(kThreads), lds, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), a.alpha, a.beta,
                        ws_F, a.T, a.H, a.K, C);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -672,7 +676,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
       constexpr int KK = decltype(kc)::value;
       hipError_t r;
       if ((r = set_lds_limit<TIn>((const void*)bwd_dstate_kernel<TIn, KK>)) != hipSuccess) return r;
-      hipLaunchKernelGGL((bwd_dstate_kernel<TIn, KK>), dim3(a.V / VS, a.H, a.B), dim3(kThreads), lds,
+      hipLaunchKernelGGL((bwd_dstate_kernel<TIn, KK>), dim3(a.V / VS * a.H * a.B), dim3(kThreads), lds,
                          stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                          static_cast<const TIn*>(a.d_o), a.d_sfinal, a.d_s0, ws_F, ws_dS, a.T, a.H,
                          a.V, C, VS);
@@ -688,7 +692,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
       constexpr int KK = decltype(kc)::value;
       hipError_t r;
       if ((r = set_lds_limit<TIn>((const void*)bwd_local_kernel<TIn, KK>)) != hipSuccess) return r;
-      hipLaunchKernelGGL((bwd_local_kernel<TIn, KK>), dim3(NT, a.H, a.B), dim3(kThreads), lds, stream,
+      hipLaunchKernelGGL((bwd_local_kernel<TIn, KK>), dim3(NT * a.H * a.B), dim3(kThreads), lds, stream,
                          static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                          static_cast<const TIn*>(a.v), static_cast<const TIn*>(a.d_o), a.alpha,
                          a.beta, ws_S, ws_dS, ws_F, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),

@@ -84,8 +84,9 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int NT = (T + kC - 1) / kC;
+  // one-dimensional grid over (chunk, head, batch), chunk fastest
+  const int c = blockIdx.x % NT, h = (blockIdx.x / NT) % H, b = blockIdx.x / NT / H;
   const int t0 = c * kC, n = min(kC, T - t0);
   const size_t tok = (size_t)H * KD;
   unsigned char* dst = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
@@ -491,8 +492,9 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ls = lane & 15, lg = lane >> 4;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int NT = (T + kC - 1) / kC;
+  // one-dimensional grid over (chunk, head, batch), chunk fastest
+  const int c = blockIdx.x % NT, h = (blockIdx.x / NT) % H, b = blockIdx.x / NT / H;
   const int t0 = c * kC, n = min(kC, T - t0);
   const size_t tokk = (size_t)H * KD, tokv = (size_t)H * VD;
   const unsigned char* rc = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
@@ -978,7 +980,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     constexpr int KD = decltype(kc)::value;
     // (2) prep first, with the whole GPU; then (1) on the side stream beside (3):
     // the two long walks have one workgroup per CU each and fit side by side
-    hipLaunchKernelGGL((bwd16_prep_kernel<KD>), dim3(NT, a.H, a.B), dim3(256), 0, stream, q, k, a.alpha,
+    hipLaunchKernelGGL((bwd16_prep_kernel<KD>), dim3(NT * a.H * a.B), dim3(256), 0, stream, q, k, a.alpha,
                        a.beta, rec, a.T, a.H);
     hipError_t r;
     if ((r = hipGetLastError()) != hipSuccess) return r;
@@ -996,7 +998,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     if (sd && (r = hipStreamWaitEvent(stream, sd->join, 0)) != hipSuccess) return r;   // states ready
     auto local = [&](auto vc) -> hipError_t {
       constexpr int VD = decltype(vc)::value;
-      hipLaunchKernelGGL((bwd16_local_kernel<KD, VD>), dim3(NT, a.H, a.B), dim3(512), 0, stream, q, k, v,
+      hipLaunchKernelGGL((bwd16_local_kernel<KD, VD>), dim3(NT * a.H * a.B), dim3(512), 0, stream, q, k, v,
                          d_o, a.alpha, ws_S, ws_dS, rec, static_cast<bf16*>(a.dq), static_cast<bf16*>(a.dk),
                          static_cast<bf16*>(a.dv), a.dalpha, a.dbeta, a.T, a.H);
       return hipGetLastError();

@@ -53,9 +53,11 @@ fwd_f32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* 
   float* sb = sgam + C;            // [C] beta
 
   const int tid = threadIdx.x;
-  const int v0 = blockIdx.x * VS;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // one-dimensional grid over (value slice, head, sequence), value slice fastest
+  const int nvs = V / VS;
+  const int v0 = (blockIdx.x % nvs) * VS;
+  const int h = (blockIdx.x / nvs) % H;
+  const int b = blockIdx.x / nvs / H;
   const size_t state_base = ((size_t)b * H + h) * (size_t)V * K + (size_t)v0 * K;
 
   for (int i = tid; i < VS * K; i += kThreads) sS[(i / K) * LK + i % K] = s0 ? s0[state_base + i] : 0.0f;
@@ -191,7 +193,7 @@ hipError_t launch_scalar(const FwdArgs& a, float* s_ckpt, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid(a.V / VS, a.H, a.B);
+  dim3 grid(a.V / VS * a.H * a.B);
   hipLaunchKernelGGL(fwd_f32_kernel<TIn>, grid, dim3(kThreads), lds, stream,
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                      static_cast<const TIn*>(a.v), a.alpha, a.beta, a.s0,

@@ -125,3 +125,48 @@ def test_packed_batch_at_the_size_limit():
         assert np.isfinite(eo) and eo <= TOL and es <= TOL
     del g, o, sf
     release()
+
+
+# More than 65,536 (batch, head) pairs: every kernel takes a one-dimensional grid,
+# since the y and z grid dimensions stop at 65,536 on this GPU.
+MANY = 70_000
+
+
+def test_fp32_forward_and_backward_with_more_than_65536_sequences():
+    from linear_attention_sequence_chunked_amd import chunk_bwd
+    from linear_attention_sequence_chunked_amd.workloads import make_inputs
+    print("case limits: fp32, B=%d T=20 H=1 K=V=16 chunk 16" % MANY, flush=True)
+    inp = make_inputs(MANY, 20, 1, 16, 16, dtype=torch.float32, seed=44, gate="decay",
+                      s0_std=0.1, with_do=True)
+    g = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
+    o, sf = chunk_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["initial_state"], chunk=16)
+    got = chunk_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["d_o"], g["initial_state"],
+                    chunk=16)
+    torch.cuda.synchronize()
+    ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
+    ref = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["d_o"],
+                     inp["initial_state"])
+    errs = {"o": rel_l2(o, ro), "final_state": rel_l2(sf, rs)}
+    for n, x in zip(("dq", "dk", "dv", "dalpha", "dbeta", "d_initial_state"), got):
+        errs[n] = rel_l2(x, ref[n])
+    print("  " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert np.isfinite(e) and e <= 1e-5, (n, e)
+    release()
+
+
+def test_bf16_backward_with_more_than_65536_heads():
+    from linear_attention_sequence_chunked_amd import chunk_bwd
+    from linear_attention_sequence_chunked_amd.workloads import make_inputs
+    print("case limits: bf16 matrix-core backward, B=1 T=64 H=%d K=V=32" % MANY, flush=True)
+    inp = make_inputs(1, 64, MANY, 32, 32, dtype=torch.bfloat16, seed=45, gate="decay",
+                      with_do=True)
+    g = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
+    got = chunk_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["d_o"], None, chunk=64)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["d_o"])
+    errs = {n: rel_l2(x, ref[n]) for n, x in zip(("dq", "dk", "dv", "dalpha", "dbeta"), got)}
+    print("  " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert np.isfinite(e) and e <= TOL, (n, e)
+    release()
