@@ -573,7 +573,8 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
           }
       }
       const float gam_n = sm.gt[gs].gam[CP - 1];
-      __builtin_amdgcn_sched_barrier(0);
+      // (no scheduling barrier here: letting the U products start while the later
+      // Tm and P fragments arrive measured 0.7% faster)
       f32x4 U[NTB], Up[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
