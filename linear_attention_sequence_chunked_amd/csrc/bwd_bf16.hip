@@ -64,12 +64,18 @@ __device__ __forceinline__ void store_bf4(bf16* p, f32x4 d) {
 
 // ===========================================================================
 // (2) prep: one workgroup (4 waves) per (chunk, head, batch).
+// The key and query tiles are dead once the Gram is built, so Tm takes their
+// place: 53 KB at K = 128, three workgroups per CU.
 template <int KD>
 struct alignas(16) PrepSmem {
   static constexpr int LDK = KD + 8;
-  bf16 k[kC * LDK], q[kC * LDK];   // [token][channel]
+  union {
+    struct {
+      bf16 k[kC * LDK], q[kC * LDK];   // [token][channel], read by the Gram only
+    } in;
+    float x[kC][kC + 4];             // Tm (lower); upper blocks hold level scratch
+  } u;
   float a[kC][kC + 4];             // A = diag(beta) M, strictly lower
-  float x[kC][kC + 4];             // Tm (lower); upper blocks hold level scratch
   float g[kC], bt[kC];
 };
 
@@ -120,8 +126,8 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int p = tid + 256 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv[j];
-    *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv[j];
+    *reinterpret_cast<bf16x8*>(&sm.u.in.k[r * LDK + c8]) = kv[j];
+    *reinterpret_cast<bf16x8*>(&sm.u.in.q[r * LDK + c8]) = qv[j];
   }
   // gates: g = cumulative log2(alpha) by a wave scan
   if (wave == 0) {
@@ -141,7 +147,7 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   {
     const bool isP = wave >= 2;
     const int ra = (wave & 1) ? 1 : 0, rb = (wave & 1) ? 2 : 3;
-    const bf16* ab = isP ? sm.q : sm.k;
+    const bf16* ab = isP ? sm.u.in.q : sm.u.in.k;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int w = half == 0 ? ra : rb;   // token-block row
@@ -150,7 +156,7 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         if (tc <= w) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            acc = mma(frag_rows(ab, LDK, 16 * w, 32 * ks, lane), frag_rows(sm.k, LDK, 16 * tc, 32 * ks, lane), acc);
+            acc = mma(frag_rows(ab, LDK, 16 * w, 32 * ks, lane), frag_rows(sm.u.in.k, LDK, 16 * tc, 32 * ks, lane), acc);
         }
         // accumulator: row r = 16 w + 4 lg + e, column i = 16 tc + ls
         const int i = 16 * tc + ls;
@@ -187,7 +193,7 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       xv[r] = rr < j ? 0.0f : (rr == j ? 1.0f : -s);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sm.x[16 * bb + r][j] = xv[r];
+    for (int r = 0; r < 16; ++r) sm.u.x[16 * bb + r][j] = xv[r];
   }
   __syncthreads();
   // Off-diagonal blocks by levels d = i - j: X_ij = -T_ii (sum_{j <= m < i} A_im T_mj),
@@ -202,18 +208,18 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const int j = wave, i = wave + d;
       f32x4 x = zero4();
       for (int m0 = 16 * j; m0 < 16 * i; m0 += 4)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.a[16 * i + ls][m0 + lg], sm.x[m0 + lg][16 * j + ls], x,
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.a[16 * i + ls][m0 + lg], sm.u.x[m0 + lg][16 * j + ls], x,
                                                  0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.x[16 * j + 4 * lg + e][16 * i + ls] = x[e];
+      for (int e = 0; e < 4; ++e) sm.u.x[16 * j + 4 * lg + e][16 * i + ls] = x[e];
       // T_ii is lower triangular: its upper entries are zeros
       f32x4 y = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < 16; k0 += 4)
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.x[16 * i + ls][16 * i + k0 + lg],
-                                                 sm.x[16 * j + k0 + lg][16 * i + ls], y, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.x[16 * i + ls][16 * i + k0 + lg],
+                                                 sm.u.x[16 * j + k0 + lg][16 * i + ls], y, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.x[16 * i + 4 * lg + e][16 * j + ls] = -y[e];
+      for (int e = 0; e < 4; ++e) sm.u.x[16 * i + 4 * lg + e][16 * j + ls] = -y[e];
     }
     __syncthreads();
   }
@@ -222,7 +228,7 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
     float xr[8];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) xr[jj] = c8 + jj <= r ? sm.x[r][c8 + jj] : 0.0f;
+    for (int jj = 0; jj < 8; ++jj) xr[jj] = c8 + jj <= r ? sm.u.x[r][c8 + jj] : 0.0f;
     *reinterpret_cast<bf16x8*>(rtm + 8 * p) = to_bf8(xr);
   }
 }
