@@ -32,7 +32,7 @@
 //
 //   chain waves (one per 16 value rows): Y, Z, R of chunk x      | U, O, S of chunk x
 //   levels wave:                         off-diagonal Tm of x     |
-//   diag wave:                                                    | diagonal Tm of x+1
+//   diag wave:                           (the other half of it)   | diagonal Tm of x+1
 //   Gram waves:                          A, P of chunk x+1        | stage chunk x+2 in LDS,
 //                                                                 | load chunk x+3
 //
