@@ -233,3 +233,16 @@ def test_segments_hint_follows_the_cost_model():
     for args in [(1, 5000, 3, 64, 32, 32), (2, 70000, 1, 16, 16, 16), (1, 8192, 4, 128, 64, 64)]:
         P = hint(*args, num_cus=256)
         assert 1 <= P <= 256 and (P == 1 or 4 * P <= -(-args[1] // args[5]))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the bench measures one GPU; a request for more exits with a message before any
+    # device work (so this runs on the host)
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
