@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -234,19 +234,20 @@ GDN_API gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v
 
 /*
  * gdn_chunk_bwd_workspace_size -- bytes of device workspace gdn_chunk_bwd needs
- * for these sizes, whatever the dtype: the larger of two layouts.  The float32
- * path keeps, per (batch, head, backward chunk of C = min(chunk, 32) tokens), two
- * float32 [V, K] states and the chunk's float32 factors (three C x C matrices and
- * three C-vectors):
- *     B * H * ceil(T / C) * (2 * V * K + 3 * C * C + 3 * C) * 4 bytes.
- * When K and V are 32, 64 or 128, bfloat16 inputs take the MFMA path with
- * 64-token chunks: per (batch, head, chunk) two float32 [V, K] states and a
- * 25088-byte record (three bf16 64 x 64 matrices, two float32 64-vectors):
- *     B * H * ceil(T / 64) * (2 * V * K * 4 + 25088) bytes.
- * Returns 0 when a size is not positive.
+ * for these sizes and this dtype (the layout of the path the call takes).
+ *  - bfloat16 with K and V in {32, 64, 128}: the MFMA path with 64-token chunks,
+ *    whatever `chunk` is; per (batch, head, chunk) two float32 [V, K] states and
+ *    a 16896-byte record (two bf16 64 x 64 matrices, two float32 64-vectors):
+ *        B * H * ceil(T / 64) * (2 * V * K * 4 + 16896) bytes.
+ *  - otherwise (float32, or bfloat16 with K or V = 16): the float32 path, per
+ *    (batch, head, backward chunk of C = min(chunk, 32) tokens) two float32
+ *    [V, K] states and the chunk's float32 factors (three C x C matrices and
+ *    three C-vectors):
+ *        B * H * ceil(T / C) * (2 * V * K + 3 * C * C + 3 * C) * 4 bytes.
+ * Returns 0 when a size is not positive or the dtype is not F32 or BF16.
  */
 GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K,
-                                            int64_t V, int64_t chunk);
+                                            int64_t V, int64_t chunk, gdn_dtype_t dtype);
 
 /*
  * gdn_chunk_bwd -- reverse mode of gdn_chunk_fwd for the loss
@@ -260,7 +261,8 @@ GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int
  *   dalpha, dbeta  [B,T,H]   float32      dL/dalpha, dL/dbeta with respect to the
  *                                         gates themselves (written)
  *   d_initial_state [B,H,V,K] float32     dL/dinitial_state, or NULL to skip
- *   workspace      device scratch of workspace_bytes >= gdn_chunk_bwd_workspace_size(...);
+ *   workspace      device scratch of workspace_bytes >=
+ *                  gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk, dtype);
  *                  owned by the caller, contents undefined after the call
  *   B .. dtype, stream                    as for gdn_chunk_fwd
  *

@@ -20,10 +20,20 @@
 //   dK = diag(D) U dS' - diag(beta gam) dR S + (dP o E)^T Q + (dA o bE) K + (dA o bE)^T K
 //   dV = diag(beta) dR
 //   dbeta_r = dR_r.(v_r - gam_r Y_r) + sum_i dA_ri M_ri
-//   dg_r = gam_r dO_r.Z_r - beta_r gam_r dR_r.Y_r - D_r U_r.W_r
+//   dg_r = gam_r dO_r.Z_r - beta_r gam_r dR_r.Y_r
 //          + sum_i (dP o P)_ri - sum_i (dP o P)_ir + sum_i (dA o A)_ri - sum_i (dA o A)_ir
 //   dg_last += gam_last <dS', S> + sum_r D_r U_r.W_r
 //   d ln alpha_t = sum_{r >= t} dg_r,   dalpha_t = d ln alpha_t / alpha_t
+//
+// which is summed here in an equal form without cancellation:
+//   d ln alpha_t = sum_{r >= t} (gam_r dO_r.Z_r - beta_r gam_r dR_r.Y_r)
+//                + sum_{r >= t} sum_{i < t} ((dP o P)_ri + (dA o A)_ri)
+//                + sum_{r < t} D_r U_r.W_r + gam_last <dS', S>
+// (every (dP o P + dA o A)_ri with i and r both >= t enters the suffix twice
+// with opposite signs, and the U.W terms, the derivative through
+// D_r = e^(g_last - g_r), reach token t only for r < t; with small gates
+// d ln alpha_t is tiny next to those terms, and the chunk total minus a suffix
+// would lose it to rounding).
 //
 // Four launches: (1) the forward kernel of the input dtype recomputes the
 // chunk-start states into the workspace; (2a) every chunk builds its
@@ -406,7 +416,9 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   float* sb = sgam + C;
   float* sdb = sb + C;             // dbeta accumulator
   float* sdg = sdb + C;            // dg accumulator
-  float* sred = sdg + C;           // [kThreads] reduction scratch
+  float* sdu = sdg + C;            // D_r U_r.W_r accumulator
+  float* sxr = sdu + C;            // cross sums of dP o P + dA o A per token
+  float* sred = sxr + C;           // [kThreads] reduction scratch
 
   const int tid = threadIdx.x;
   const int NT = (T + C - 1) / C;
@@ -427,6 +439,7 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   if (tid < C) {
     sdb[tid] = 0.0f;
     sdg[tid] = 0.0f;
+    sdu[tid] = 0.0f;
   }
   for (int i = tid; i < C * C; i += kThreads) {
     sdP[i] = 0.0f;
@@ -440,7 +453,7 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   float aq[kQPT], ak[kQPT];
 #pragma unroll
   for (int j = 0; j < kQPT; ++j) aq[j] = ak[j] = 0.0f;
-  float sdot = 0.0f, esum = 0.0f;  // <dS', S> and sum_r D_r U_r.W_r, per-thread partials
+  float sdot = 0.0f;  // <dS', S>, per-thread partial
 
   for (int v0 = 0; v0 < V; v0 += VS) {
     const int vs = min(VS, V - v0);
@@ -548,29 +561,30 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
         ry = fmaf(dr, y, ry);
         uw = fmaf(sU[r * LV + e], sW[r * LV + e], uw);
       }
-      const float du = expf(glast - sg[r]) * uw;
       sdb[r] += db;
-      sdg[r] += sgam[r] * oz - sb[r] * sgam[r] * ry - du;
-      esum += du;
+      sdg[r] += sgam[r] * oz - sb[r] * sgam[r] * ry;
+      sdu[r] = fmaf(expf(glast - sg[r]), uw, sdu[r]);
     }
   }
   __syncthreads();
-  // (dP o E) and beta (dA o E) in place, dg and dbeta terms of P and A
+  // (dP o E) and beta (dA o E) in place, dg and dbeta terms of P and A: token t
+  // sums the pairs i < t <= r (rows r >= t, columns i < t) in a fixed order
   if (tid < n) {
-    const int r = tid;
+    const int t = tid;
     float s = 0.0f, db = 0.0f;
-    for (int i = 0; i <= r; ++i) s = fmaf(sdP[r * C + i], sP[r * C + i], s);
-    for (int rr = r; rr < n; ++rr) s = fmaf(-sdP[rr * C + r], sP[rr * C + r], s);
-    for (int i = 0; i < r; ++i) {
-      s = fmaf(sdA[r * C + i], sb[r] * sM[r * C + i], s);
-      db = fmaf(sdA[r * C + i], sM[r * C + i], db);
+    for (int r = t; r < n; ++r) {
+      const float br = sb[r];
+      for (int i = 0; i < t; ++i) {
+        s = fmaf(sdP[r * C + i], sP[r * C + i], s);
+        s = fmaf(sdA[r * C + i], br * sM[r * C + i], s);
+      }
     }
-    for (int rr = r + 1; rr < n; ++rr) s = fmaf(-sdA[rr * C + r], sb[rr] * sM[rr * C + r], s);
-    sdg[r] += s;
-    sdb[r] += db;
+    for (int i = 0; i < t; ++i) db = fmaf(sdA[t * C + i], sM[t * C + i], db);
+    sxr[t] = s;
+    sdb[t] += db;
   }
-  // reduction of the <dS', S> and esum partials (fixed order)
-  sred[tid] = fmaf(gam_last, sdot, esum);
+  // reduction of the <dS', S> partials (fixed order)
+  sred[tid] = gam_last * sdot;
   __syncthreads();
   for (int i = tid; i < C * C; i += kThreads) {
     const int r = i / C, j = i - r * C;
@@ -602,11 +616,18 @@ bwd_local_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn
   }
   if (tid == 0) {
     sdg[n - 1] += sred[0];
-    float acc = 0.0f;  // d ln alpha_t = sum_{r >= t} dg_r
+    // prefix sums of the U.W terms (sdg's slots hold the results in place)
+    float pre = 0.0f;
+    for (int r = 0; r < n; ++r) {
+      const float du = sdu[r];
+      sdu[r] = pre;  // sum_{r' < r}
+      pre += du;
+    }
+    float acc = 0.0f;  // suffix sums of the per-token terms (gam_last <dS', S> on the last)
     for (int r = n - 1; r >= 0; --r) {
       acc += sdg[r];
       const size_t go = ((size_t)b * T + t0 + r) * H + h;
-      dalpha[go] = acc / alpha[go];
+      dalpha[go] = (acc + sxr[r] + sdu[r]) / alpha[go];
       dbeta[go] = sdb[r];
     }
   }
@@ -687,7 +708,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   // (3) token gradients
   {
     const size_t LK = a.K + 1, LV = kBwdVS + 1;
-    const size_t lds = sizeof(float) * (2 * C * LK + 5 * C * C + 8 * C * LV + 2 * kBwdVS * LK + 5 * C + kThreads);
+    const size_t lds = sizeof(float) * (2 * C * LK + 5 * C * C + 8 * C * LV + 2 * kBwdVS * LK + 7 * C + kThreads);
     auto run = [&](auto kc) -> hipError_t {
       constexpr int KK = decltype(kc)::value;
       hipError_t r;
@@ -706,14 +727,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// The larger of the two layouts: the caller's buffer serves either path.
-size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk) {
+// The layout of the path the call takes: the matrix-core path for bf16 inputs
+// with K and V in {32, 64, 128}, the float32 path otherwise.
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk,
+                           bool bf16) {
+  if (bf16 && bwd_bf16_supported((int)K, (int)V)) return bwd_bf16_workspace_bytes(B, T, H, K, V);
   const int64_t C = chunk < kBwdC ? chunk : kBwdC;
   const int64_t NT = (T + C - 1) / C;
-  const size_t scalar = (size_t)(2 * B * H * NT * V * K + B * H * NT * factor_floats((int)C)) * sizeof(float);
-  if (!bwd_bf16_supported((int)K, (int)V)) return scalar;
-  const size_t mfma = bwd_bf16_workspace_bytes(B, T, H, K, V);
-  return scalar > mfma ? scalar : mfma;
+  return (size_t)(2 * B * H * NT * V * K + B * H * NT * factor_floats((int)C)) * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {

@@ -14,13 +14,17 @@
 //       chunk-start states S_c; it runs on a second stream after (2) and beside
 //       (3), which does not need it;
 //   (2) prep, one workgroup per chunk: gates, the Gram matrices A = diag(beta) M
-//       and P, Tm = (I + A)^-1 in fp32 by 16 x 16 blocks; record = Tm, P, M
+//       and P, Tm = (I + A)^-1 in fp32 by 16 x 16 blocks; record = Tm, P
 //       (bf16) and the gates (fp32);
 //   (3) reverse walk, one workgroup per (stream, 32 value rows): the state
 //       gradient dS^T lives in MFMA accumulator tiles across chunks (like the
 //       forward's state); stores every chunk's end-state gradient dS'_c;
 //   (4) token gradients, one workgroup per chunk, fully parallel, after the
-//       join with (1).
+//       join with (1).  The gate gradients are sums of dP o P and dA o M whose
+//       terms cancel (strongly so for correlated keys); their P and M are
+//       recomputed here in fp32 (exact bf16 products summed in fp32, as prep
+//       forms them before rounding) rather than read back as bf16, which halves
+//       the error of dalpha in that regime.
 //
 // Layout conventions of the products in (4): quantities with a token axis and
 // a value or channel axis are computed transposed (accumulator rows = value or
@@ -41,11 +45,11 @@ using namespace mfma;
 
 constexpr int kC = 64;          // backward chunk (tokens)
 constexpr int kLDC = kC + 8;    // row stride of C x C bf16 tiles in LDS
-// Per-chunk record: Tm, P, M as bf16 [C][C] row-major (M strictly lower, P
-// lower, Tm unit lower), then g (cumulative log2 gate) and beta as fp32 [C].
-// Padding tokens past a sequence's end have alpha = 1 and beta = 0.
-constexpr int kRecTm = 0, kRecP = kC * kC * 2, kRecM = 2 * kC * kC * 2;
-constexpr int kRecG = 3 * kC * kC * 2, kRecB = kRecG + kC * 4;
+// Per-chunk record: Tm, P as bf16 [C][C] row-major (P lower, Tm unit lower),
+// then g (cumulative log2 gate) and beta as fp32 [C].  Padding tokens past a
+// sequence's end have alpha = 1 and beta = 0.
+constexpr int kRecTm = 0, kRecP = kC * kC * 2;
+constexpr int kRecG = 2 * kC * kC * 2, kRecB = kRecG + kC * 4;
 constexpr int kRecBytes = kRecB + kC * 4;
 
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
@@ -98,7 +102,6 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   unsigned char* dst = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
   bf16* rtm = reinterpret_cast<bf16*>(dst + kRecTm);
   bf16* rp = reinterpret_cast<bf16*>(dst + kRecP);
-  bf16* rm = reinterpret_cast<bf16*>(dst + kRecM);
 
   // Every global read is issued before the first LDS write, so the chunk's
   // loads overlap instead of waiting one after another: keys and queries (zero
@@ -141,7 +144,7 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // Gram tiles, balanced over the waves: waves 0 and 1 build A for token-block
   // rows {0, 3} and {1, 2}, waves 2 and 3 build P for the same rows (five tiles
-  // each).  A (strict) goes to fp32 LDS and M to the record, P to the record;
+  // each).  A (strict) goes to fp32 LDS, P to the record;
   // the tiles above the diagonal are written as zeros.
   const int ls = lane & 15, lg = lane >> 4;
   {
@@ -170,7 +173,6 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           } else {
             const float m = i < r ? dec * acc[e] : 0.0f;
             sm.a[r][i] = sm.bt[r] * m;
-            rm[r * kC + i] = (bf16)m;
           }
         }
       }
@@ -468,7 +470,6 @@ struct alignas(16) LocalSmem {
     } sl;
     struct {
       bf16 dpe[kC * kLDC], dae[kC * kLDC];  // (dP o E), (dA o beta E) [row][col]
-      bf16 m[kC * kLDC];                    // M [row][col]
       float xp[kC][kC + 4], xa[kC][kC + 4]; // dP o P and dA o M, [row][col]
     } fin;
   } u;
@@ -571,8 +572,7 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   load_slice(0, R);
 
   // ---- chunk operands: keys, queries, Tm, P, gates (all requested before any
-  // LDS write); M is kept in registers for the last phase
-  bf16x8 mreg;
+  // LDS write)
   {
     constexpr int KP = kC * KD / 8, KPL = (KP + 511) / 512;
     bf16x8 kv[KPL], qv[KPL];
@@ -589,7 +589,6 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     static_assert(kC * kC / 8 == 512, "one C x C piece per thread");
     const bf16x8 tv = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * tid);
     const bf16x8 pv = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * tid);
-    mreg = *reinterpret_cast<const bf16x8*>(rc + kRecM + 16 * tid);
     float gv = 0.0f, bv = 0.0f;
     if (tid < kC) {
       gv = reinterpret_cast<const float*>(rc + kRecG)[tid];
@@ -764,8 +763,8 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   if (lane == 0) sm.dot[wave] = dot;
   __syncthreads();   // every slice array is dead from here
 
-  // ---- (f) dP o E, dA o beta E to LDS (bf16, [r][i]); dP o P and dA o M (fp32)
-  *reinterpret_cast<bf16x8*>(&sm.u.fin.m[(tid / (kC / 8)) * kLDC + (tid % (kC / 8)) * 8]) = mreg;
+  // ---- (f) dP o E, dA o beta E to LDS (bf16, [r][i]); dP o P and dA o M (fp32,
+  // with P and M recomputed in fp32 from the key and query tiles)
   for (int p = tid; p < kC * kC / 8; p += 512) {   // zero the tiles no job writes
     const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
     *reinterpret_cast<bf16x8*>(&sm.u.fin.dpe[r * kLDC + c8]) = zero8();
@@ -782,28 +781,33 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // lane: i = 16 ibk + 4 lg + e, r = 16 rbk + ls
       const int r = 16 * rbk + ls;
       const float gr = sm.g[r], br = sm.bt[r];
+      // Gram tile in the same layout: G[i][r] = k_i . q_r (dP jobs) or
+      // k_i . k_r (dA jobs), exact bf16 products summed in fp32
+      const bf16* gsrc = j < 10 ? sm.q : sm.k;
+      f32x4 gram = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        gram = mma(frag_rows(sm.k, LDK, 16 * ibk, 32 * ks, lane), frag_rows(gsrc, LDK, 16 * rbk, 32 * ks, lane), gram);
       f32x4 val, prod;
       if (j < 10) {
-        const bf16x4 pv = *reinterpret_cast<const bf16x4*>(&sm.p[r * kLDC + 16 * ibk + 4 * lg]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * ibk + 4 * lg + e;
           const float ee = __builtin_amdgcn_exp2f(i <= r ? gr - sm.g[i] : -INFINITY);
           const float dp = i <= r ? pa[u][e] : 0.0f;
           val[e] = dp * ee;
-          prod[e] = dp * bf2f(pv[e]);
+          prod[e] = dp * (ee * gram[e]);   // dP o P, P = E o (Q K^T)
         }
         store_tile_t(sm.u.fin.dpe, kLDC, 16 * rbk, 16 * ibk, val, lane);
         *reinterpret_cast<f32x4*>(&sm.u.fin.xp[r][16 * ibk + 4 * lg]) = prod;
       } else {
-        const bf16x4 mv = *reinterpret_cast<const bf16x4*>(&sm.u.fin.m[r * kLDC + 16 * ibk + 4 * lg]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * ibk + 4 * lg + e;
           const float ee = __builtin_amdgcn_exp2f(i < r ? gr - sm.g[i] : -INFINITY);
           const float da = i < r ? -pa[u][e] : 0.0f;
           val[e] = da * br * ee;
-          prod[e] = da * bf2f(mv[e]);
+          prod[e] = da * (ee * gram[e]);   // dA o M, M = E o (K K^T), strictly lower
         }
         store_tile_t(sm.u.fin.dae, kLDC, 16 * rbk, 16 * ibk, val, lane);
         *reinterpret_cast<f32x4*>(&sm.u.fin.xa[r][16 * ibk + 4 * lg]) = prod;
@@ -842,15 +846,16 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
   // ---- (h) per-token gate gradients: eight lanes per token split the row and
   // column sums of dP o P and dA o M by index mod 8 and combine them with three
-  // shuffles (fixed order)
+  // shuffles (fixed order).  The sums skip the diagonal (dP o P's diagonal term
+  // would enter both and cancel; dA o M's diagonal is zero).
   {
     const int r = tid >> 3, q8 = tid & 7;
     float sp = 0.0f, sa = 0.0f, cp = 0.0f, ca = 0.0f;
-    for (int i = q8; i <= r; i += 8) {
+    for (int i = q8; i < r; i += 8) {
       sp += sm.u.fin.xp[r][i];
       sa += sm.u.fin.xa[r][i];
     }
-    for (int rr = r + ((q8 - r) & 7); rr < kC; rr += 8) {
+    for (int rr = r + 1 + ((q8 - r - 1) & 7); rr < kC; rr += 8) {
       cp += sm.u.fin.xp[rr][r];
       ca += sm.bt[rr] * sm.u.fin.xa[rr][r];
     }
@@ -873,27 +878,29 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
       const float gm = __builtin_amdgcn_exp2f(sm.g[r]), br = sm.bt[r];
       const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[r]);
-      sm.dgs[r] = gm * oz - br * gm * ry - dd * uw + (sp - cp) + (br * sa - ca);
+      sm.dgs[r] = gm * oz - br * gm * ry + (sp - cp) + (br * sa - ca);
       sm.dbs[r] = db + sa;
       sm.dus[r] = dd * uw;   // zero past the end (U rows are zero there)
     }
   }
   __syncthreads();
   if (wave == 0) {
-    // the chunk-end terms go to the last real token; then
-    // d ln alpha_t = sum_{t <= r < n} dg_r as a scan over the reversed tokens
-    float esum = sm.dus[lane];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);
+    // d ln alpha_t = sum_{t <= r < n} dg_r (a scan over the reversed tokens, with
+    // gam_last <dS', S> on the last real token) + sum_{r < t} D_r U_r.W_r (an
+    // exclusive scan): the U.W terms reach token t only through the gates of
+    // tokens before it, and summing them so, rather than as the chunk total minus
+    // a suffix, keeps small gates free of cancellation
     float dsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) dsum += sm.dot[w];
     float dg = lane < n ? sm.dgs[lane] : 0.0f;
-    if (lane == n - 1) dg += __builtin_amdgcn_exp2f(sm.g[kC - 1]) * dsum + esum;
+    if (lane == n - 1) dg += __builtin_amdgcn_exp2f(sm.g[kC - 1]) * dsum;
     const float suf = __shfl(wave_scan(__shfl(dg, 63 - lane), lane), 63 - lane);
+    // exclusive scan: shift by one token first (inclusive minus own would cancel)
+    const float pre = wave_scan(lane > 0 ? sm.dus[lane - 1] : 0.0f, lane);
     if (lane < n) {
       const size_t go = ((size_t)b * T + t0 + lane) * H + h;
-      dalpha[go] = suf / alpha[go];
+      dalpha[go] = (suf + pre) / alpha[go];
       dbeta[go] = sm.dbs[lane];
     }
   }
@@ -925,24 +932,44 @@ namespace {
 // A second stream per device, created on first use and kept for the life of the
 // process, with the two events of a fork / join.  The chunk-start states and the
 // reverse walk are independent sequential walks of 96 workgroups each; run side
-// by side they share the chip instead of taking turns.
+// by side they share the chip instead of taking turns.  The device is the one
+// the caller's stream belongs to; each device has its own lock, held while a call
+// creates its side stream or enqueues its fork / join sequence (the events are
+// reused by every call on that device).
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   bool failed = false;
+  std::mutex mu;
 };
 constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
-std::mutex g_side_mu;   // guards creation and each fork / join enqueue sequence
 
-SideStream* side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+int stream_device(hipStream_t stream) {
+  int dev = -1;
+  if (stream) {
+    hipDevice_t d;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return -1;
+    dev = static_cast<int>(d);
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return -1;
+  }
+  return dev >= 0 && dev < kMaxDevices ? dev : -1;
+}
+
+// Called with g_side[dev].mu held.  The stream and events are created on `dev`
+// (made current for the creation, the caller's current device restored after).
+SideStream* side_stream(int dev) {
+  if (dev < 0) return nullptr;
   SideStream& sd = g_side[dev];
   if (!sd.s && !sd.failed) {
-    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
+    int cur = -1;
+    bool ok = hipGetDevice(&cur) == hipSuccess && (cur == dev || hipSetDevice(dev) == hipSuccess);
+    ok = ok && hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) == hipSuccess;
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+    if (!ok) {
       sd.failed = true;   // keep going on the caller's stream alone
       (void)hipGetLastError();
       return nullptr;
@@ -976,8 +1003,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   f.V = a.V;
   f.chunk = kC;
   f.vs = 32;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream* sd = side_stream();
+  const int dev = stream_device(stream);
+  std::unique_lock<std::mutex> lock;
+  if (dev >= 0) lock = std::unique_lock<std::mutex>(g_side[dev].mu);
+  SideStream* sd = side_stream(dev);
   const bf16* q = static_cast<const bf16*>(a.q);
   const bf16* k = static_cast<const bf16*>(a.k);
   const bf16* v = static_cast<const bf16*>(a.v);

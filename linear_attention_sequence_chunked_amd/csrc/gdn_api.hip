@@ -263,9 +263,10 @@ gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const 
 }
 
 size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
-                                    int64_t chunk) {
+                                    int64_t chunk, gdn_dtype_t dtype) {
   if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0) return 0;
-  return gdn::bwd_workspace_bytes(B, T, H, K, V, chunk);
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return 0;
+  return gdn::bwd_workspace_bytes(B, T, H, K, V, chunk, dtype == GDN_DTYPE_BF16);
 }
 
 gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
@@ -283,7 +284,8 @@ gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const fl
     if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
   const gdn_status_t st = check_shape(B, T, H, K, V, chunk, dtype);
   if (st != GDN_SUCCESS) return st;
-  if (workspace_bytes < gdn::bwd_workspace_bytes(B, T, H, K, V, chunk)) return GDN_ERROR_INVALID_VALUE;
+  if (workspace_bytes < gdn::bwd_workspace_bytes(B, T, H, K, V, chunk, dtype == GDN_DTYPE_BF16))
+    return GDN_ERROR_INVALID_VALUE;
 
   const int64_t esz = dtype == GDN_DTYPE_F32 ? 4 : 2;
   const int64_t nk = B * T * H * K, nv = B * T * H * V, ng = B * T * H, ns = B * H * V * K;

@@ -53,7 +53,9 @@ struct BwdArgs {
   float* workspace;       // bwd_workspace_bytes(...) bytes
   int B, T, H, K, V, chunk;
 };
-size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk);
+// Workspace of the path a call with these sizes and dtype takes.
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk,
+                           bool bf16);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 
 // Bfloat16 backward on MFMA with 64-token chunks, whatever chunk the caller gave

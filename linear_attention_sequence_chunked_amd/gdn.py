@@ -3,7 +3,9 @@
 Every step of the computation runs in the HIP kernels behind the C ABI declared
 in ``include/gdn.h``; this module checks tensors, allocates outputs with torch
 (device memory and streams are all torch is used for), and forwards raw device
-pointers plus the current HIP stream.  If the built library is missing it raises
+pointers plus the HIP stream (torch's current one unless ``stream=`` is given;
+memory the binding allocates for a call on another stream is recorded on that
+stream, so the caching allocator does not reuse it while the call still runs).  If the built library is missing it raises
 at load time: there is no CPU or PyTorch fallback.
 
 Operator contract ("OpenGDN 0.1.0", section "Core operator reference"): q, k
@@ -43,7 +45,7 @@ SIGNATURES = {
     "gdn_chunk_fwd_segmented": (ctypes.c_int, [_VP] * 8 + [_I64] * 7 + [_VP, ctypes.c_size_t] +
                                 [ctypes.c_int, _VP]),
     "gdn_decode_step": (ctypes.c_int, [_VP] * 7 + [_I64] * 4 + [ctypes.c_int, _VP]),
-    "gdn_chunk_bwd_workspace_size": (ctypes.c_size_t, [_I64] * 6),
+    "gdn_chunk_bwd_workspace_size": (ctypes.c_size_t, [_I64] * 6 + [ctypes.c_int]),
     "gdn_chunk_bwd": (ctypes.c_int, [_VP] * 15 + [ctypes.c_size_t] + [_I64] * 6 + [ctypes.c_int, _VP]),
 }
 
@@ -90,6 +92,25 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _launch_stream(dev, stream):
+    """The stream a call enqueues on (``stream``, else torch's current stream of
+    ``dev``) and whether it differs from torch's current stream."""
+    cur = torch.cuda.current_stream(dev)
+    s = stream if stream is not None else cur
+    return s, s.cuda_stream != cur.cuda_stream
+
+
+def _keep_for(s, other, tensors):
+    """Tensors this binding allocated on torch's current stream but handed to work
+    on another stream ``s``: tell the caching allocator, so that none of their
+    memory is given to new work on the current stream before ``s`` is done with
+    it (a scratch buffer is freed as soon as the call returns)."""
+    if other:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
+
+
 def _check(t, name, shape, dtype, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -131,27 +152,34 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk: int = 64, *,
     _check(q, "q", (B, T, H, K), q.dtype, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (B, H, V, K), torch.float32, dev)
+    made = []
     if out is None:
         out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+        made.append(out)
     else:
         _check(out, "out", (B, T, H, V), q.dtype, dev)
     if final_state is None and want_final_state:
         final_state = torch.empty((B, H, V, K), dtype=torch.float32, device=dev)
+        made.append(final_state)
     elif final_state is not None:
         _check(final_state, "final_state", (B, H, V, K), torch.float32, dev)
     with torch.cuda.device(dev):
-        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        s, other = _launch_stream(dev, stream)
         rc = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(initial_state), _ptr(out), _ptr(final_state),
                                B, T, H, K, V, int(chunk), _DTYPES[q.dtype],
                                ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_chunk_fwd")
+    _keep_for(s, other, made)
     return out, final_state
 
 
-def bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, chunk: int = 64) -> int:
-    """Bytes of device workspace ``gdn_chunk_bwd`` needs for these sizes."""
-    return int(load_library().gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk))
+def bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, chunk: int = 64,
+                       dtype=torch.bfloat16) -> int:
+    """Bytes of device workspace ``gdn_chunk_bwd`` needs for these sizes and dtype."""
+    if dtype not in _DTYPES:
+        raise NotImplementedError("dtype %s is not supported (float32 or bfloat16)" % dtype)
+    return int(load_library().gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk, _DTYPES[dtype]))
 
 
 def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
@@ -186,9 +214,11 @@ def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
         _check(initial_state, "initial_state", (B, H, V, K), torch.float32, dev)
     if d_final_state is not None:
         _check(d_final_state, "d_final_state", (B, H, V, K), torch.float32, dev)
-    need = lib.gdn_chunk_bwd_workspace_size(B, T, H, K, V, int(chunk))
+    need = lib.gdn_chunk_bwd_workspace_size(B, T, H, K, V, int(chunk), _DTYPES[q.dtype])
+    made = []
     if workspace is None:
         workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+        made.append(workspace)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
     dq = torch.empty_like(q)
@@ -197,14 +227,16 @@ def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
     dalpha = torch.empty_like(alpha)
     dbeta = torch.empty_like(beta)
     d_s0 = torch.empty((B, H, V, K), dtype=torch.float32, device=dev) if want_d_initial_state else None
+    made += [dq, dk, dv, dalpha, dbeta, d_s0]
     with torch.cuda.device(dev):
-        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        s, other = _launch_stream(dev, stream)
         rc = lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq),
                                _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(dbeta), _ptr(d_s0),
                                _ptr(workspace), workspace.numel(), B, T, H, K, V, int(chunk),
                                _DTYPES[q.dtype], ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_chunk_bwd")
+    _keep_for(s, other, made)
     return dq, dk, dv, dalpha, dbeta, d_s0
 
 
@@ -230,15 +262,18 @@ def decode_step(q, k, v, alpha, beta, state, *, out=None, stream=None):
     _check(beta, "beta", (B, H), torch.float32, dev)
     _check(state, "state", (B, H, V, K), torch.float32, dev)
     _check(q, "q", (B, H, K), q.dtype, dev)
+    made = []
     if out is None:
         out = torch.empty((B, H, V), dtype=q.dtype, device=dev)
+        made.append(out)
     else:
         _check(out, "out", (B, H, V), q.dtype, dev)
     with torch.cuda.device(dev):
-        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        s, other = _launch_stream(dev, stream)
         rc = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
                                  _ptr(out), B, H, K, V, _DTYPES[q.dtype], ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_decode_step")
+    _keep_for(s, other, made)
     return out
 
 
@@ -273,21 +308,25 @@ def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, chunk
     _check(q, "q", (1, T, H, K), q.dtype, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (N, H, V, K), torch.float32, dev)
+    made = []
     if out is None:
         out = torch.empty((1, T, H, V), dtype=q.dtype, device=dev)
+        made.append(out)
     else:
         _check(out, "out", (1, T, H, V), q.dtype, dev)
     if final_state is None and want_final_state:
         final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=dev)
+        made.append(final_state)
     elif final_state is not None:
         _check(final_state, "final_state", (N, H, V, K), torch.float32, dev)
     with torch.cuda.device(dev):
-        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        s, other = _launch_stream(dev, stream)
         rc = lib.gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                       _ptr(cu_seqlens), N, _ptr(initial_state), _ptr(out),
                                       _ptr(final_state), T, H, K, V, int(chunk), _DTYPES[q.dtype],
                                       ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_chunk_fwd_varlen")
+    _keep_for(s, other, made)
     return out, final_state
 
 
@@ -327,12 +366,15 @@ def chunk_fwd_segmented(q, k, v, alpha, beta, initial_state=None, chunk: int = 6
     _check(beta, "beta", (B, T, H), torch.float32, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (B, H, V, K), torch.float32, dev)
+    made = []
     if out is None:
         out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+        made.append(out)
     else:
         _check(out, "out", (B, T, H, V), q.dtype, dev)
     if final_state is None and want_final_state:
         final_state = torch.empty((B, H, V, K), dtype=torch.float32, device=dev)
+        made.append(final_state)
     elif final_state is not None:
         _check(final_state, "final_state", (B, H, V, K), torch.float32, dev)
     if segments is None:
@@ -341,14 +383,16 @@ def chunk_fwd_segmented(q, k, v, alpha, beta, initial_state=None, chunk: int = 6
     need = int(lib.gdn_chunk_fwd_segmented_workspace_size(B, T, H, K, V, int(chunk), int(segments)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        made.append(workspace)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
     with torch.cuda.device(dev):
-        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        s, other = _launch_stream(dev, stream)
         rc = lib.gdn_chunk_fwd_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                          _ptr(initial_state), _ptr(out), _ptr(final_state), B, T,
                                          H, K, V, int(chunk), int(segments), _ptr(workspace),
                                          workspace.numel(), _DTYPES[q.dtype],
                                          ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_chunk_fwd_segmented")
+    _keep_for(s, other, made)
     return out, final_state

@@ -71,11 +71,22 @@ WORKLOADS = {
 
 def make_inputs(B: int, T: int, H: int, K: int, V: int, dtype=torch.bfloat16,
                 seed: int = 0, gate: str = "decay", s0_std: float | None = None,
-                with_do: bool = False) -> dict:
+                with_do: bool = False, keys: str = "unit", beta_range=None) -> dict:
     """Draw one seeded input set on the CPU.
 
     Returns a dict with q, k, v (``dtype``), alpha, beta (float32 [B,T,H]),
     initial_state (float32 [B,H,V,K] or None) and d_o (``dtype`` or None).
+
+    Edge-case options (drawn after every standard draw, so the standard inputs of
+    a seed do not change):
+      gate="strong"          alpha in (0.005, 0.2): the decay over a 64-token
+                             chunk reaches about 2^-210, far below float32's range;
+      gate="extreme"         alpha in (2^-16, 2^-4): the same for 16-token chunks;
+      keys="correlated"      k_t = normalise(kbar + 0.1 n_t / sqrt(K)) with one
+                             unit kbar per (batch, head): k_r . k_i ~ 0.99, so
+                             I + tril(beta A, -1) is far from the identity;
+      keys="repeated"        runs of 8 identical keys;
+      beta_range=(lo, hi)    beta = lo + (hi - lo) sigmoid(x) instead of sigmoid(x).
     """
     g = torch.Generator().manual_seed(int(seed))
     q = torch.randn(B, T, H, K, generator=g, dtype=torch.float32)
@@ -92,13 +103,31 @@ def make_inputs(B: int, T: int, H: int, K: int, V: int, dtype=torch.bfloat16,
     # unit-norm queries and keys along the key axis, normalised in float32
     q = q / q.norm(dim=-1, keepdim=True)
     k = k / k.norm(dim=-1, keepdim=True)
+    if keys == "correlated":
+        kbar = torch.randn(B, 1, H, K, generator=g, dtype=torch.float32)
+        kbar = kbar / kbar.norm(dim=-1, keepdim=True)
+        noise = torch.randn(B, T, H, K, generator=g, dtype=torch.float32)
+        k = kbar + (0.1 / K ** 0.5) * noise
+        k = k / k.norm(dim=-1, keepdim=True)
+    elif keys == "repeated":
+        idx = (torch.arange(T) // 8) * 8
+        k = k[:, idx].contiguous()
+    elif keys != "unit":
+        raise ValueError("keys must be 'unit', 'correlated' or 'repeated'")
     if gate == "sigmoid":
         alpha = torch.sigmoid(a_logit)
     elif gate == "decay":
         alpha = torch.exp(-0.1 * torch.nn.functional.softplus(a_logit))
+    elif gate == "strong":
+        alpha = 0.005 + 0.195 * torch.sigmoid(a_logit)
+    elif gate == "extreme":
+        alpha = torch.exp2(-(4.0 + 12.0 * torch.sigmoid(a_logit)))
     else:
-        raise ValueError("gate must be 'sigmoid' or 'decay'")
+        raise ValueError("gate must be 'sigmoid', 'decay', 'strong' or 'extreme'")
     beta = torch.sigmoid(b_logit)
+    if beta_range is not None:
+        lo, hi = beta_range
+        beta = lo + (hi - lo) * beta
     return {
         "q": q.to(dtype).contiguous(), "k": k.to(dtype).contiguous(), "v": v.to(dtype).contiguous(),
         "alpha": alpha.contiguous(), "beta": beta.contiguous(),

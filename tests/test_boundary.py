@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = gdn.load_library()
-    assert lib.gdn_abi_version() == 6
+    assert lib.gdn_abi_version() == 7
     for code in range(4):
         assert len(gdn.status_string(code)) > 0
     assert gdn.status_string(99) == "unknown status"
@@ -114,28 +114,44 @@ def call_bwd(B=2, T=100, H=3, K=64, V=64, chunk=64, dtype=gdn.GDN_DTYPE_BF16, ws
             args.append(ptr[name])
         else:
             args.append(addr(i, 2 if misalign == name else 0))
-    need = lib.gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk)
+    need = lib.gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk,
+                                            dtype if dtype in (0, 1) else gdn.GDN_DTYPE_BF16)
     return lib.gdn_chunk_bwd(*args, need if ws_bytes is None else ws_bytes, B, T, H, K, V, chunk,
                              dtype, None)
 
 
 def test_bwd_workspace_size():
     lib = gdn.load_library()
-    # per (b, h, chunk of min(chunk, 32) tokens): two fp32 [V,K] states, 3 CxC + 3 C factors
-    assert lib.gdn_chunk_bwd_workspace_size(2, 100, 3, 64, 32, 64) == \
-        2 * 3 * 4 * (2 * 32 * 64 + 3 * 32 * 32 + 3 * 32) * 4
-    assert lib.gdn_chunk_bwd_workspace_size(1, 17, 1, 16, 16, 16) == \
-        2 * (2 * 16 * 16 + 3 * 16 * 16 + 3 * 16) * 4
-    assert lib.gdn_chunk_bwd_workspace_size(0, 17, 1, 16, 16, 16) == 0
-    # K, V in {32, 64, 128}: the larger of that layout and the bf16 MFMA layout
-    # (per 64-token chunk two fp32 [V,K] states and a 25088-byte record: Tm, P, M
-    # as bf16 C x C, gates as fp32), whatever the chunk
-    mfma = 2 * 128 * 128 * 4 + 25088
-    assert lib.gdn_chunk_bwd_workspace_size(1, 1, 1, 128, 128, 64) == mfma
-    assert lib.gdn_chunk_bwd_workspace_size(1, 1, 1, 128, 128, 32) == \
-        max(mfma, (2 * 128 * 128 + 3 * 32 * 32 + 3 * 32) * 4)
-    assert lib.gdn_chunk_bwd_workspace_size(1, 256, 1, 128, 128, 16) == \
-        max(4 * mfma, 16 * (2 * 128 * 128 + 3 * 16 * 16 + 3 * 16) * 4)
+    F32, BF16 = gdn.GDN_DTYPE_F32, gdn.GDN_DTYPE_BF16
+
+    def scalar(B, T, H, K, V, chunk):
+        # float32 path: per (b, h, chunk of min(chunk, 32) tokens) two fp32 [V,K]
+        # states and 3 C x C + 3 C float32 factors
+        C = min(chunk, 32)
+        return B * H * -(-T // C) * (2 * V * K + 3 * C * C + 3 * C) * 4
+
+    def mfma(B, T, H, K, V):
+        # matrix-core path: per 64-token chunk two fp32 [V,K] states and a 16896-byte
+        # record (Tm, P as bf16 64 x 64, gates as fp32), whatever the chunk
+        return B * H * -(-T // 64) * (2 * V * K * 4 + 16896)
+
+    assert lib.gdn_chunk_bwd_workspace_size(2, 100, 3, 64, 32, 64, F32) == scalar(2, 100, 3, 64, 32, 64)
+    assert lib.gdn_chunk_bwd_workspace_size(1, 17, 1, 16, 16, 16, F32) == scalar(1, 17, 1, 16, 16, 16)
+    assert lib.gdn_chunk_bwd_workspace_size(0, 17, 1, 16, 16, 16, F32) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(1, 17, 1, 16, 16, 16, 7) == 0
+    # bf16 with K or V = 16 takes the float32 path
+    assert lib.gdn_chunk_bwd_workspace_size(1, 100, 2, 16, 64, 32, BF16) == scalar(1, 100, 2, 16, 64, 32)
+    # bf16 with K, V in {32, 64, 128}: the matrix-core layout alone, whatever the chunk
+    for chunk in (16, 32, 64):
+        assert lib.gdn_chunk_bwd_workspace_size(1, 256, 1, 128, 128, chunk, BF16) == \
+            mfma(1, 256, 1, 128, 128)
+        assert lib.gdn_chunk_bwd_workspace_size(1, 256, 1, 128, 128, chunk, F32) == \
+            scalar(1, 256, 1, 128, 128, chunk)
+    # the forward+backward workload (B4 T2048 H6 d128 bf16): about 114 MB, not the
+    # 220 MB float32 layout
+    ws = lib.gdn_chunk_bwd_workspace_size(4, 2048, 6, 128, 128, 64, BF16)
+    assert ws == mfma(4, 2048, 6, 128, 128) == 113_639_424
+    assert ws < scalar(4, 2048, 6, 128, 128, 64)
 
 
 def test_bwd_rejects_bad_arguments():

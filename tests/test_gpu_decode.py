@@ -14,6 +14,8 @@ import oracle
 from linear_attention_sequence_chunked_amd import chunk_fwd, decode_step
 from linear_attention_sequence_chunked_amd.workloads import WORKLOADS, make_inputs, workload_inputs
 
+from tests.parity import assert_parity
+
 pytestmark = pytest.mark.gpu
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
@@ -47,9 +49,8 @@ def test_decode_steps_match_oracle(dt, K, V):
     state = inp["initial_state"].to(DEV).clone()
     o = run_decode(inp, state)
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
-    eo, es = rel_l2(o, ro), rel_l2(state, rs)
-    print("  rel L2 o=%.2e state=%.2e" % (eo, es), flush=True)
-    assert eo <= TOL[dt] and es <= 1e-5
+    assert_parity("decode o", {"o": (o, ro)}, TOL[dt])
+    assert_parity("decode state", {"final_state": (state, rs)}, 1e-5)
 
 
 def test_decode_continues_a_prefill():
@@ -63,9 +64,8 @@ def test_decode_continues_a_prefill():
     o1, state = chunk_fwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["initial_state"], chunk=64)
     o2 = run_decode(dec, state)
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
-    assert rel_l2(torch.cat([o1, o2], 1), ro) <= 2e-2
+    assert_parity("prefill+decode", {"o": (torch.cat([o1, o2], 1), ro), "final_state": (state, rs)}, 2e-2)
     assert rel_l2(o2, ro[:, 300:]) <= 2e-2
-    assert rel_l2(state, rs) <= 2e-2
 
 
 def test_decode_workload_one_step():
@@ -74,7 +74,8 @@ def test_decode_workload_one_step():
     state = inp["initial_state"].to(DEV).clone()
     o = run_decode(inp, state)
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
-    assert rel_l2(o, ro) <= 2e-2 and rel_l2(state, rs) <= 1e-5
+    assert_parity("decode workload o", {"o": (o, ro)}, 2e-2)
+    assert_parity("decode workload state", {"final_state": (state, rs)}, 1e-5)
 
 
 def test_decode_identity_gates_keep_state_and_read_it():

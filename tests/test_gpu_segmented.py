@@ -13,6 +13,8 @@ import oracle
 from linear_attention_sequence_chunked_amd import chunk_fwd, chunk_fwd_segmented
 from linear_attention_sequence_chunked_amd.workloads import WORKLOADS, make_inputs, workload_inputs
 
+from tests.parity import assert_parity
+
 pytestmark = pytest.mark.gpu
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
@@ -48,9 +50,7 @@ def test_segmented_matches_oracle(case):
                                 chunk=C, segments=P)
     torch.cuda.synchronize()
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
-    eo, es = rel_l2(o, ro), rel_l2(sf, rs)
-    print("  rel L2 o=%.2e final_state=%.2e" % (eo, es), flush=True)
-    assert eo <= TOL[dt] and es <= TOL[dt]
+    assert_parity("segmented", {"o": (o, ro), "final_state": (sf, rs)}, TOL[dt])
 
 
 def test_segmented_state_in_place_and_close_to_plain():
@@ -74,7 +74,7 @@ def test_long_context_workload_segmented():
                                 chunk=w.chunk, segments=4)
     torch.cuda.synchronize()
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
-    assert rel_l2(o, ro) <= 2e-2 and rel_l2(sf, rs) <= 2e-2
+    assert_parity("long segmented", {"o": (o, ro), "final_state": (sf, rs)}, 2e-2)
 
 
 @pytest.mark.parametrize("K,P", [(64, 6), (128, 9), (32, 2)])
@@ -91,9 +91,7 @@ def test_segmented_weak_decay_carries_state_across_segments(K, P):
                                 gd["initial_state"], chunk=32, segments=P)
     torch.cuda.synchronize()
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
-    eo, es = rel_l2(o, ro), rel_l2(sf, rs)
-    print("  weak decay rel L2 o=%.2e final_state=%.2e" % (eo, es), flush=True)
-    assert eo <= 1e-5 and es <= 1e-5
+    assert_parity("weak decay", {"o": (o, ro), "final_state": (sf, rs)}, 1e-5)
 
 
 def test_segment_count_from_the_hint():
@@ -109,4 +107,4 @@ def test_segment_count_from_the_hint():
                                 chunk=64)
     torch.cuda.synchronize()
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
-    assert rel_l2(o, ro) <= TOL[torch.bfloat16] and rel_l2(sf, rs) <= TOL[torch.bfloat16]
+    assert_parity("hinted", {"o": (o, ro), "final_state": (sf, rs)}, TOL[torch.bfloat16])
