@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -62,7 +62,9 @@ typedef enum gdn_status {
     GDN_ERROR_INVALID_VALUE = 1, /* NULL required pointer, non-positive size, misaligned pointer,
                                     or overlapping input/output buffers */
     GDN_ERROR_NOT_SUPPORTED = 2, /* valid, but outside the compiled kernel set (see below) */
-    GDN_ERROR_LAUNCH = 3         /* the HIP runtime refused the launch */
+    GDN_ERROR_LAUNCH = 3,        /* the HIP runtime refused the launch */
+    GDN_ERROR_SCRATCH_LIMIT = 4  /* gdn_chunk_fwd_segmented_noalloc only: the call needs more
+                                    than the static scratch (GDN_SEGMENTED_NOALLOC_MAX_BYTES) */
 } gdn_status_t;
 
 typedef enum gdn_dtype {
@@ -207,6 +209,39 @@ GDN_API gdn_status_t gdn_chunk_fwd_segmented(const void *q, const void *k, const
                                      int64_t chunk, int64_t segments,
                                      void *workspace, size_t workspace_bytes,
                                      gdn_dtype_t dtype, void *stream);
+
+/* Size of the static per-device scratch of gdn_chunk_fwd_segmented_noalloc. */
+#define GDN_SEGMENTED_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
+/*
+ * gdn_chunk_fwd_segmented_noalloc -- gdn_chunk_fwd_segmented without a
+ * workspace argument and without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * The scratch lives in a static device array of GDN_SEGMENTED_NOALLOC_MAX_BYTES
+ * (64 MiB) that every GPU the library runs on holds until the process ends (its
+ * address is looked up once per device, on the first call there).  A call whose
+ * gdn_chunk_fwd_segmented_workspace_size(...) exceeds it returns
+ * GDN_ERROR_SCRATCH_LIMIT before any device work (B1 T32768 H16 with 4 segments
+ * needs 21 MB; so does H2 with 32).  The call itself allocates nothing (no
+ * hipMalloc, no allocating library routine); nothing in the scratch needs to
+ * start at zero, and every pass overwrites what the next one reads.
+ *
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one
+ * device (different streams, or several host threads without ordering) RACE on
+ * it and give wrong results.  Calls in one stream's order are safe.
+ *
+ *   arguments      as for gdn_chunk_fwd_segmented, without workspace and
+ *                  workspace_bytes; results identical (bitwise) to it
+ */
+GDN_API gdn_status_t gdn_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
+                                             const float *alpha, const float *beta,
+                                             const float *initial_state,
+                                             void *o, float *final_state,
+                                             int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                             int64_t chunk, int64_t segments,
+                                             gdn_dtype_t dtype, void *stream);
 
 /*
  * gdn_decode_step -- one token of the recurrence for every (batch, head), the

@@ -7,6 +7,9 @@
 #include "../../include/gdn.h"
 #include "launch.h"
 
+static_assert(GDN_SEGMENTED_NOALLOC_MAX_BYTES == gdn::kSegmentedScratchBytes,
+              "header and library disagree on the static scratch size");
+
 namespace {
 
 struct Range {
@@ -57,6 +60,11 @@ const char* gdn_status_string(gdn_status_t status) {
              "or BF16, B*T*H*max(K,V) below 2^31 and B*H*V*K at most 2^31";
     case GDN_ERROR_LAUNCH:
       return "kernel launch failed";
+    case GDN_ERROR_SCRATCH_LIMIT:
+      return "the call needs more scratch than the allocation-free entry point's static buffer "
+             "holds (GDN_SEGMENTED_NOALLOC_MAX_BYTES = 64 MiB per device; "
+             "gdn_chunk_fwd_segmented_workspace_size gives the need): use gdn_chunk_fwd_segmented "
+             "with a workspace, or fewer segments";
   }
   return "unknown status";
 }
@@ -166,33 +174,41 @@ size_t gdn_chunk_fwd_segmented_workspace_size(int64_t B, int64_t T, int64_t H, i
   return gdn::fwd_segmented_workspace_bytes(B, T, H, K, V, chunk, segments);
 }
 
-gdn_status_t gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
-                                     const float* alpha, const float* beta,
-                                     const float* initial_state, void* o, float* final_state,
-                                     int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
-                                     int64_t chunk, int64_t segments, void* workspace,
-                                     size_t workspace_bytes, gdn_dtype_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the segmented entry points: the caller's workspace, or (noalloc)
+// the library's static per-device scratch.
+gdn_status_t segmented_impl(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* beta, const float* initial_state, void* o,
+                            float* final_state, int64_t B, int64_t T, int64_t H, int64_t K,
+                            int64_t V, int64_t chunk, int64_t segments, void* workspace,
+                            size_t workspace_bytes, bool noalloc, gdn_dtype_t dtype, void* stream) {
   if (segments <= 0) return GDN_ERROR_INVALID_VALUE;
   if (segments == 1)
     return chunk_fwd_impl(q, k, v, alpha, beta, nullptr, initial_state, o, final_state, B, B, T,
                           H, K, V, chunk, dtype, stream);
-  if (!workspace || !aligned16(workspace)) return GDN_ERROR_INVALID_VALUE;
+  if (!noalloc && (!workspace || !aligned16(workspace))) return GDN_ERROR_INVALID_VALUE;
   // shape checks of the dense call, plus the B * segments packed states
   const gdn_status_t st = check_shape(B, T, H, K, V, chunk, dtype);
   if (st != GDN_SUCCESS) return st;
   if (segments > T || B * segments > (INT64_C(1) << 31) / (H * K * (K > V ? K : V)))
     return GDN_ERROR_NOT_SUPPORTED;
-  if (workspace_bytes < gdn::fwd_segmented_workspace_bytes(B, T, H, K, V, chunk, segments))
-    return GDN_ERROR_INVALID_VALUE;
+  const size_t need = gdn::fwd_segmented_workspace_bytes(B, T, H, K, V, chunk, segments);
+  if (noalloc && need > gdn::kSegmentedScratchBytes) return GDN_ERROR_SCRATCH_LIMIT;
+  if (!noalloc && workspace_bytes < need) return GDN_ERROR_INVALID_VALUE;
   const int64_t esz = dtype == GDN_DTYPE_F32 ? 4 : 2;
-  const Range rw = range_of(workspace, (int64_t)workspace_bytes);
   const Range others[] = {range_of(q, B * T * H * K * esz), range_of(k, B * T * H * K * esz),
                           range_of(v, B * T * H * V * esz), range_of(alpha, B * T * H * 4),
                           range_of(beta, B * T * H * 4), range_of(o, B * T * H * V * esz),
                           initial_state ? range_of(initial_state, B * H * V * K * 4) : Range{0, 0},
                           final_state ? range_of(final_state, B * H * V * K * 4) : Range{0, 0}};
-  for (const Range& r : others)
-    if (r.hi != r.lo && overlaps(rw, r)) return GDN_ERROR_INVALID_VALUE;
+  if (!noalloc) {
+    const Range rw = range_of(workspace, (int64_t)workspace_bytes);
+    for (const Range& r : others)
+      if (r.hi != r.lo && overlaps(rw, r)) return GDN_ERROR_INVALID_VALUE;
+  }
   // the pointer, alignment and overlap checks of the dense call
   if (!q || !k || !v || !alpha || !beta || !o) return GDN_ERROR_INVALID_VALUE;
   const void* ptrs[] = {q, k, v, alpha, beta, initial_state, o, final_state};
@@ -223,9 +239,36 @@ gdn_status_t gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v
   a.K = static_cast<int>(K);
   a.V = static_cast<int>(V);
   a.chunk = static_cast<int>(chunk);
-  hipError_t err = gdn::launch_fwd_segmented(a, dtype == GDN_DTYPE_BF16, static_cast<int>(segments),
-                                             workspace, static_cast<hipStream_t>(stream));
+  const bool bf16 = dtype == GDN_DTYPE_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err =
+      noalloc ? gdn::launch_fwd_segmented_noalloc(a, bf16, static_cast<int>(segments), s)
+              : gdn::launch_fwd_segmented(a, bf16, static_cast<int>(segments), workspace, s);
   return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                     const float* alpha, const float* beta,
+                                     const float* initial_state, void* o, float* final_state,
+                                     int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                     int64_t chunk, int64_t segments, void* workspace,
+                                     size_t workspace_bytes, gdn_dtype_t dtype, void* stream) {
+  return segmented_impl(q, k, v, alpha, beta, initial_state, o, final_state, B, T, H, K, V, chunk,
+                        segments, workspace, workspace_bytes, false, dtype, stream);
+}
+
+gdn_status_t gdn_chunk_fwd_segmented_noalloc(const void* q, const void* k, const void* v,
+                                             const float* alpha, const float* beta,
+                                             const float* initial_state, void* o,
+                                             float* final_state, int64_t B, int64_t T, int64_t H,
+                                             int64_t K, int64_t V, int64_t chunk, int64_t segments,
+                                             gdn_dtype_t dtype, void* stream) {
+  return segmented_impl(q, k, v, alpha, beta, initial_state, o, final_state, B, T, H, K, V, chunk,
+                        segments, nullptr, 0, true, dtype, stream);
 }
 
 gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,

@@ -77,6 +77,12 @@ int64_t fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                           int64_t cus);
 hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int segments, void* workspace,
                                 hipStream_t stream);
+// The same with the library's per-device static scratch of kSegmentedScratchBytes
+// instead of a caller workspace (no allocation; calls that overlap on one device
+// race on it).  hipErrorInvalidValue when the call needs more than that.
+constexpr size_t kSegmentedScratchBytes = size_t(64) << 20;
+hipError_t launch_fwd_segmented_noalloc(const FwdArgs& a, bool bf16, int segments,
+                                        hipStream_t stream);
 
 // One decode step (T = 1), already validated by the C-ABI layer.
 struct DecodeArgs {

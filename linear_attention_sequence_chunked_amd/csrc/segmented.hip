@@ -19,6 +19,14 @@
 // most of the GPU idle.
 #include "launch.h"
 
+#include <mutex>
+
+// Scratch of the allocation-free segmented forward (gdn_chunk_fwd_segmented_noalloc):
+// every GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device (segmented_scratch below).
+static __device__ __align__(256) unsigned char scratch[gdn::kSegmentedScratchBytes];
+
 namespace gdn {
 namespace {
 
@@ -234,6 +242,53 @@ int64_t fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
 size_t fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                      int64_t chunk, int64_t segments) {
   return seg_layout(B, T, H, K, V, chunk, segments).bytes;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev`, looked up on the first call there
+// with `dev` current (the caller's current device is restored after).
+hipError_t segmented_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_segmented_noalloc(const FwdArgs& a, bool bf16, int P, hipStream_t stream) {
+  if (fwd_segmented_workspace_bytes(a.B, a.T, a.H, a.K, a.V, a.chunk, P) > kSegmentedScratchBytes)
+    return hipErrorInvalidValue;
+  int dev = -1;
+  if (stream) {
+    hipDevice_t d;
+    const hipError_t e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return e;
+    dev = static_cast<int>(d);
+  } else {
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+  }
+  void* ws = nullptr;
+  const hipError_t e = segmented_scratch(dev, &ws);
+  if (e != hipSuccess) return e;
+  return launch_fwd_segmented(a, bf16, P, ws, stream);
 }
 
 hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int P, void* workspace,

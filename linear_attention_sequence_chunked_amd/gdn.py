@@ -26,6 +26,8 @@ GDN_SUCCESS = 0
 GDN_ERROR_INVALID_VALUE = 1
 GDN_ERROR_NOT_SUPPORTED = 2
 GDN_ERROR_LAUNCH = 3
+GDN_ERROR_SCRATCH_LIMIT = 4
+SEGMENTED_NOALLOC_MAX_BYTES = 64 << 20
 GDN_DTYPE_F32 = 0
 GDN_DTYPE_BF16 = 1
 
@@ -44,6 +46,7 @@ SIGNATURES = {
     "gdn_chunk_fwd_segmented_workspace_size": (ctypes.c_size_t, [_I64] * 7),
     "gdn_chunk_fwd_segmented": (ctypes.c_int, [_VP] * 8 + [_I64] * 7 + [_VP, ctypes.c_size_t] +
                                 [ctypes.c_int, _VP]),
+    "gdn_chunk_fwd_segmented_noalloc": (ctypes.c_int, [_VP] * 8 + [_I64] * 7 + [ctypes.c_int, _VP]),
     "gdn_decode_step": (ctypes.c_int, [_VP] * 7 + [_I64] * 4 + [ctypes.c_int, _VP]),
     "gdn_chunk_bwd_workspace_size": (ctypes.c_size_t, [_I64] * 6 + [ctypes.c_int]),
     "gdn_chunk_bwd": (ctypes.c_int, [_VP] * 15 + [ctypes.c_size_t] + [_I64] * 6 + [ctypes.c_int, _VP]),
@@ -394,5 +397,57 @@ def chunk_fwd_segmented(q, k, v, alpha, beta, initial_state=None, chunk: int = 6
                                          workspace.numel(), _DTYPES[q.dtype],
                                          ctypes.c_void_p(s.cuda_stream))
     _raise_for(rc, "gdn_chunk_fwd_segmented")
+    _keep_for(s, other, made)
+    return out, final_state
+
+
+def chunk_fwd_segmented_noalloc(q, k, v, alpha, beta, initial_state=None, chunk: int = 64,
+                                segments: int = 4, *, out=None, final_state=None,
+                                want_final_state: bool = True, stream=None):
+    """:func:`chunk_fwd_segmented` through ``gdn_chunk_fwd_segmented_noalloc``: the
+    library's static per-device scratch (``SEGMENTED_NOALLOC_MAX_BYTES``) replaces
+    the workspace, so the library allocates nothing; calls that overlap in time on
+    one device race on that scratch.  ``out`` and ``final_state`` may be passed in
+    so that the call allocates nothing on the torch side either.  Returns
+    ``(o, final_state)``; raises ``MemoryError`` when the call needs more scratch
+    than the static buffer holds."""
+    lib = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B,T,H,K]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    if q.dtype not in _DTYPES:
+        raise NotImplementedError("dtype %s is not supported (float32 or bfloat16)" % q.dtype)
+    B, T, H, K = q.shape
+    if v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B,T,H,V]")
+    V = v.shape[-1]
+    _check(k, "k", (B, T, H, K), q.dtype, dev)
+    _check(v, "v", (B, T, H, V), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, V, K), torch.float32, dev)
+    made = []
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+        made.append(out)
+    else:
+        _check(out, "out", (B, T, H, V), q.dtype, dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, H, V, K), dtype=torch.float32, device=dev)
+        made.append(final_state)
+    elif final_state is not None:
+        _check(final_state, "final_state", (B, H, V, K), torch.float32, dev)
+    with torch.cuda.device(dev):
+        s, other = _launch_stream(dev, stream)
+        rc = lib.gdn_chunk_fwd_segmented_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out),
+            _ptr(final_state), B, T, H, K, V, int(chunk), int(segments), _DTYPES[q.dtype],
+            ctypes.c_void_p(s.cuda_stream))
+    if rc == GDN_ERROR_SCRATCH_LIMIT:
+        raise MemoryError("gdn_chunk_fwd_segmented_noalloc: %s" % status_string(rc))
+    _raise_for(rc, "gdn_chunk_fwd_segmented_noalloc")
     _keep_for(s, other, made)
     return out, final_state

@@ -38,8 +38,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = gdn.load_library()
-    assert lib.gdn_abi_version() == 7
-    for code in range(4):
+    assert lib.gdn_abi_version() == 8
+    for code in range(5):
         assert len(gdn.status_string(code)) > 0
     assert gdn.status_string(99) == "unknown status"
 
@@ -262,3 +262,28 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_noalloc_segmented_rejects_calls_beyond_its_static_scratch():
+    # host checks only (fake addresses): a call that needs more than the 64 MiB
+    # static scratch is refused with its own status before any device work
+    lib = gdn.load_library()
+    assert gdn.SEGMENTED_NOALLOC_MAX_BYTES == 64 << 20
+    text = open(HEADER).read()
+    assert "#define GDN_SEGMENTED_NOALLOC_MAX_BYTES ((size_t)64 << 20)" in text
+
+    def ncall(B=1, T=32768, H=16, K=128, V=128, segments=4, null=None, dtype=gdn.GDN_DTYPE_BF16):
+        names = ["q", "k", "v", "a", "b", "s0", "o", "sf"]
+        args = [None if (n == null or n in ("s0", "sf")) else addr(i) for i, n in enumerate(names)]
+        return lib.gdn_chunk_fwd_segmented_noalloc(*args, B, T, H, K, V, 64, segments, dtype, None)
+
+    need = lib.gdn_chunk_fwd_segmented_workspace_size
+    assert need(1, 32768, 16, 128, 128, 64, 4) <= gdn.SEGMENTED_NOALLOC_MAX_BYTES
+    assert need(1, 32768, 16, 128, 128, 64, 16) > gdn.SEGMENTED_NOALLOC_MAX_BYTES
+    assert ncall(segments=16) == gdn.GDN_ERROR_SCRATCH_LIMIT
+    assert ncall(B=4, segments=4) == gdn.GDN_ERROR_SCRATCH_LIMIT
+    assert "64 MiB" in gdn.status_string(gdn.GDN_ERROR_SCRATCH_LIMIT)
+    # the other checks of the segmented call still apply, before the size check
+    assert ncall(segments=0) == gdn.GDN_ERROR_INVALID_VALUE
+    assert ncall(K=48) == gdn.GDN_ERROR_NOT_SUPPORTED
+    assert ncall(segments=4, null="q") == gdn.GDN_ERROR_INVALID_VALUE
