@@ -44,7 +44,7 @@
 // array (one 16-byte read per lane) or from a [k][row] array with two gfx950
 // transpose reads (ds_read_b64_tr_b16).  Accumulator tiles are written
 // transposed ([col][row], 8 bytes per lane).  Key and query tiles are row-major
-// [token][channel] with padded rows.
+// [token][channel] with rows padded to a stride of 32 bytes modulo 64.
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -61,11 +61,15 @@ constexpr int kLongestFirstMax = 128;
 template <int KD, int VS, int CP>
 struct alignas(16) Smem {
   static constexpr int NTB = CP / 16;
+  // key and query rows: KD + 16 elements, a stride of 32 bytes modulo 64, which
+  // keeps the 16-byte fragment reads (lanes 0-7 and 16-23 served together, rows
+  // s and pieces g) on distinct banks: 2x the read rate of an 8-element pad
+  static constexpr int LDK = KD + 16;
   static constexpr int LDC = CP + 8;   // CP x CP tiles
   static constexpr int LDA = 24;       // packed 16-wide A^T blocks
   static constexpr int APK = (NTB == 4 ? 96 : 16) * LDA;
-  bf16 k[3][CP * (KD + 8)];            // keys [token][channel], padded rows
-  bf16 q[2][CP * (KD + 8)];            // queries, padded rows
+  bf16 k[3][CP * LDK];                 // keys [token][channel], padded rows
+  bf16 q[2][CP * LDK];                 // queries, padded rows
   // value slice [token][v]; rows of 96 bytes keep the transpose reads of 8
   // consecutive token rows on distinct banks
   static constexpr int LDV = (VS == 16 || VS == 32) ? 48 : VS + 16;
@@ -146,7 +150,7 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
   constexpr int LDC = SM::LDC, LDA = SM::LDA;
   const int ls = lane & 15, lg = lane >> 4;
   const int gs = c % 3;
-  constexpr int LDK = KD + 8;
+  constexpr int LDK = SM::LDK;
   const lbf16* kr = pin(lds(sm.k[gs]) + rows_lane(LDK, lane));
   const lbf16* qr = pin(lds(sm.q[c % 2]) + rows_lane(LDK, lane));
   const lf32* gl = lds(sm.gt[gs].gl);
@@ -398,7 +402,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     const int r = p / (KD / 8), ch = (p % (KD / 8)) * 8;
     krow[j] = (p < KPIECES && ch < K) ? r : CP;  // CP: never loaded or stored
     kgo[j] = r * (int)tok_k + ch;
-    klo[j] = swz<KD>(r, ch);
+    klo[j] = r * SM::LDK + ch;
   }
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
@@ -448,8 +452,8 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       if (sl + NSL * j < KPIECES) {  // pieces past K are stored as zeros
-        *reinterpret_cast<lds_bf16x8*>(kst + j * (NSL / (KD / 8)) * (KD + 8)) = R.k[j];
-        if constexpr (WO) *reinterpret_cast<lds_bf16x8*>(qst + j * (NSL / (KD / 8)) * (KD + 8)) = R.q[j];
+        *reinterpret_cast<lds_bf16x8*>(kst + j * (NSL / (KD / 8)) * SM::LDK) = R.k[j];
+        if constexpr (WO) *reinterpret_cast<lds_bf16x8*>(qst + j * (NSL / (KD / 8)) * SM::LDK) = R.q[j];
       }
     }
 #pragma unroll
@@ -491,7 +495,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
           if (16 * cb < K) *reinterpret_cast<f32x4*>(dst + 16 * cb) = S[cb];
       }
       const int gs = x % 3;
-      constexpr int LDK = KD + 8;
+      constexpr int LDK = SM::LDK;
       const lbf16* kr = pin(lds(sm.k[gs]) + rows_lane(LDK, lane));      // K rows
       const lbf16* qr = pin(lds(sm.q[x % 2]) + rows_lane(LDK, lane));   // Q rows
       const lbf16* kc = pin(lds(sm.k[gs]) + cols_lane(LDK, lane));      // K^T by transpose reads
