@@ -72,7 +72,7 @@ __device__ __forceinline__ void store_bf4(bf16* p, f32x4 d) {
 // place: 53 KB at K = 128, three workgroups per CU.
 template <int KD>
 struct alignas(16) PrepSmem {
-  static constexpr int LDK = KD + 8;
+  static constexpr int LDK = KD + 16;   // 32 bytes modulo 64: conflict-free fragment reads
   union {
     struct {
       bf16 k[kC * LDK], q[kC * LDK];   // [token][channel], read by the Gram only
@@ -247,7 +247,7 @@ constexpr int kLDV = 48;  // [token][16 values] rows of 96 bytes (transpose read
 
 template <int KD>
 struct alignas(16) WalkSlot {
-  static constexpr int LDK = KD + 8;
+  static constexpr int LDK = KD + 16;   // 32 bytes modulo 64: conflict-free fragment reads
   bf16 k[kC * LDK], q[kC * LDK];   // [token][channel]
   bf16 tm[kC * kLDC], p[kC * kLDC];
   bf16 dob[kC * kLDV], dog[kC * kLDV];  // dO and diag(gam) dO: [token][32 values]
@@ -459,7 +459,9 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 template <int KD, int VD>
 struct alignas(16) LocalSmem {
   static constexpr int VSL = 32;                    // value slice
-  static constexpr int LDK = KD + 8, LDW = VSL + 8;
+  // rows of 32 bytes modulo 64 for the 16-byte fragment reads (lanes 0-7 and
+  // 16-23 are served together): keys, queries, S, dS' and the slice tiles
+  static constexpr int LDK = KD + 16, LDW = VSL + 16;
   bf16 k[kC * LDK], q[kC * LDK];       // [token][channel]
   bf16 tm[kC * kLDC], p[kC * kLDC];    // Tm, P [row][col]
   union {

@@ -368,16 +368,22 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     (&sm.tt[0][0])[i] = (bf16)0.0f;
   }
 
-  // ---- chain waves: the state slice as S^T accumulator tiles: tile cb holds
-  // S^T[16 cb + 4g + e][16 vb + s] = S[16 vb + s][16 cb + 4g + e] in lane (g, s)
+  // ---- chain waves: the state slice as S^T accumulator tiles.  Tile cb, lane
+  // (g, s), element e holds S[16 vb + s][ch(cb, g) + e] with the key channels in
+  // the order ch(cb, g) = 32 (cb / 2) + 8 g + 4 (cb % 2): the pair of tiles
+  // (2 ks, 2 ks + 1) then gives lane group g channels 32 ks + 8 g .. + 7 in order,
+  // which is the k order of a key-row fragment, so the state packs into the
+  // operand of Y = K S^T and Z^T = S Q^T with no data moved between lanes.  The
+  // state update's K^T reads fetch the channels in the same order.
   f32x4 S[NCB];
   const int vb = wave;  // value block of a chain wave
+  auto chan = [&](int cb) { return 32 * (cb >> 1) + 4 * (cb & 1) + 8 * lg; };
   if (wave < NCH) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       S[cb] = zero4();
-      if (s0 && 16 * cb < K)
-        S[cb] = *reinterpret_cast<const f32x4*>(&s0[state_base + (size_t)(16 * vb + ls) * K + 16 * cb + 4 * lg]);
+      if (s0 && chan(cb) < K)
+        S[cb] = *reinterpret_cast<const f32x4*>(&s0[state_base + (size_t)(16 * vb + ls) * K + chan(cb)]);
     }
   }
 
@@ -489,16 +495,16 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     for (int x = 0; x < NT; ++x) {
       lds_barrier();
       if (s_ckpt) {  // chunk-start state [B, H, NT, V, K] (for the backward)
-        float* dst = s_ckpt + ((((size_t)b * H + h) * NT + x) * V + v0 + 16 * vb + ls) * (size_t)K + 4 * lg;
+        float* dst = s_ckpt + ((((size_t)b * H + h) * NT + x) * V + v0 + 16 * vb + ls) * (size_t)K;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          if (16 * cb < K) *reinterpret_cast<f32x4*>(dst + 16 * cb) = S[cb];
+          if (chan(cb) < K) *reinterpret_cast<f32x4*>(dst + chan(cb)) = S[cb];
       }
       const int gs = x % 3;
       constexpr int LDK = SM::LDK;
       const lbf16* kr = pin(lds(sm.k[gs]) + rows_lane(LDK, lane));      // K rows
       const lbf16* qr = pin(lds(sm.q[x % 2]) + rows_lane(LDK, lane));   // Q rows
-      const lbf16* kc = pin(lds(sm.k[gs]) + cols_lane(LDK, lane));      // K^T by transpose reads
+      const lbf16* kc = pin(lds(sm.k[gs]) + cols_lane_tau(LDK, lane, 8));  // K^T by transpose reads
       const lbf16* vc = pin(lds(sm.v[x % 2]) + (4 * lg + (ls >> 2)) * SM::LDV + 16 * vb + 4 * (ls & 3));
       const lf32* g4 = pin(lds(&sm.gt[gs].beta[0]) + 4 * lg);             // per-row gate vectors
       const lf32* g1 = pin(lds(&sm.gt[gs].gam[0]) + ls);                  // per-column gates
@@ -514,7 +520,7 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         if constexpr (WO) qa[0][tb] = ld8(qr + 16 * tb * LDK);
       }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sbf[ks] = acc_pair_to_frag(S[2 * ks], S[2 * ks + 1]);
+      for (int ks = 0; ks < KS; ++ks) sbf[ks] = acc_pair_pack(S[2 * ks], S[2 * ks + 1]);
       f32x4 Y[NTB], Z[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
@@ -557,12 +563,14 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         for (int e = 0; e < 4; ++e) R[tb][e] = bt[tb][e] * (float)vt[tb][e] - bgv[tb][e] * Y[tb][e];
         if constexpr (WO) Z[tb] = Z[tb] * gmt[tb];
       }
+      // R, U and Up become operands with the tokens (their k) in tau order; Tm, P
+      // and K^T are read in the same order
       bf16x8 rb[CS];
 #pragma unroll
-      for (int cs = 0; cs < CS; ++cs) rb[cs] = acc_pair_to_frag(R[2 * cs], R[2 * cs + 1]);
+      for (int cs = 0; cs < CS; ++cs) rb[cs] = acc_pair_pack(R[2 * cs], R[2 * cs + 1]);
       lds_barrier();  // Tm_x is complete after this barrier
       // ---- phase B: U = Tm R, O = diag(gam) Z + P U, S^T <- gam_n S^T + K^T Up
-      const lbf16* tc = pin(lds(sm.tt[x % 2]) + cols_lane(LDC, lane));
+      const lbf16* tc = pin(lds(sm.tt[x % 2]) + cols_lane_tau(LDC, lane, 4));
       const lbf16* pc = tc + (&sm.pt[0][0] - &sm.tt[0][0]);
       bf16x8 tf[NTB][CS], pf[NTB][CS];
       f32x4 dnv[NTB];
@@ -572,8 +580,8 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs)
           if (32 * cs <= 16 * tb + 15) {  // Tm and P are lower triangular
-            tf[tb][cs] = frag_cols_at(tc, LDC, 16 * tb, 32 * cs);
-            if constexpr (WO) pf[tb][cs] = frag_cols_at(pc, LDC, 16 * tb, 32 * cs);
+            tf[tb][cs] = frag_cols_tau_at(tc, LDC, 16 * tb, 32 * cs);
+            if constexpr (WO) pf[tb][cs] = frag_cols_tau_at(pc, LDC, 16 * tb, 32 * cs);
           }
       }
       const float gam_n = sm.gt[gs].gam[CP - 1];
@@ -591,15 +599,16 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       bf16x8 ub[CS], upb[CS];
 #pragma unroll
       for (int cs = 0; cs < CS; ++cs) {
-        ub[cs] = acc_pair_to_frag(U[2 * cs], U[2 * cs + 1]);
-        upb[cs] = acc_pair_to_frag(Up[2 * cs], Up[2 * cs + 1]);
+        ub[cs] = acc_pair_pack(U[2 * cs], U[2 * cs + 1]);
+        upb[cs] = acc_pair_pack(Up[2 * cs], Up[2 * cs + 1]);
       }
       // S^T <- gam_n S^T + K^T Up  (A operand: K^T by transpose reads, k = token)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = S[cb] * gam_n;
 #pragma unroll
-        for (int cs = 0; cs < CS; ++cs) acc = mma(frag_cols_at(kc, LDK, 16 * cb, 32 * cs), upb[cs], acc);
+        for (int cs = 0; cs < CS; ++cs)
+          acc = mma(frag_cols_tau_at(kc, LDK, 32 * (cb >> 1) + 4 * (cb & 1), 32 * cs), upb[cs], acc);
         S[cb] = acc;
       }
       // O^T = Z^T diag(gam) + U^T P^T: lane (g, s) ends with O[token 16 tb + s]
@@ -713,12 +722,12 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     }
   }
 
-  // ---- final state
+  // ---- final state (channel order as above)
   if (wave < NCH && s_final) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-      if (16 * cb < K)
-        *reinterpret_cast<f32x4*>(&s_final[state_base + (size_t)(16 * vb + ls) * K + 16 * cb + 4 * lg]) = S[cb];
+      if (chan(cb) < K)
+        *reinterpret_cast<f32x4*>(&s_final[state_base + (size_t)(16 * vb + ls) * K + chan(cb)]) = S[cb];
   }
 }
 

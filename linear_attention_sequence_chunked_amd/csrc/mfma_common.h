@@ -146,6 +146,27 @@ __device__ __forceinline__ bf16x8 acc_pair_to_frag(f32x4 a, f32x4 b) {
   return __builtin_bit_cast(bf16x8, i32x4{t_lo[0], t_hi[0], t_lo[1], t_hi[1]});
 }
 
+// The same two tiles as an operand without moving data between lanes: lane
+// group g keeps rows 4g..4g+3 of a, then of b, as its eight k values, so the
+// operand's k order is {4g..4g+3, 16+4g..16+4g+3} ("tau order").  The other
+// operand of that product must take its k in the same order: frag_cols_tau_at
+// below, or, for the key channels of the state, the channel order the state
+// rows are kept in.
+__device__ __forceinline__ bf16x8 acc_pair_pack(f32x4 a, f32x4 b) {
+  return __builtin_bit_cast(bf16x8, i32x4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3])});
+}
+// Lane part of a tau-order operand read from a [k][row] array: row 4g + s/4,
+// column cstep * (s % 4) (cstep 4 for consecutive rows of the operand).
+__device__ __forceinline__ int cols_lane_tau(int ld, int lane, int cstep) {
+  return (4 * (lane >> 4) + ((lane & 15) >> 2)) * ld + cstep * (lane & 3);
+}
+// Operand from a [k][row] array with k in tau order: transpose reads of rows
+// k0 + 4g + s/4 and k0 + 16 + 4g + s/4 (base from cols_lane_tau).
+__device__ __forceinline__ bf16x8 frag_cols_tau_at(const lbf16* cb, int ld, int r0, int k0) {
+  const bf16x4 lo = tr4(cb + k0 * ld + r0), hi = tr4(cb + (k0 + 16) * ld + r0);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 __device__ __forceinline__ float bits_f(int x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ int f_bits(float x) { return __builtin_bit_cast(int, x); }
 
