@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32 (matrix and vector), published
 METRIC = "GDN chunk fwd tokens/s + % bf16 MFMA peak at B8·T4096·H6·d128"
 
 # Sources of the timed kernel: a traffic record measured on other sources is stale.
@@ -150,6 +151,14 @@ def algorithmic_flops(B, T, H, K, V, C):
     their structural size, the inverse as C^3/3 per chunk):
     (3C-1)K + 2CV + 6KV + C^2/3."""
     per = (3 * C - 1) * K + 2 * C * V + 6 * K * V + C * C / 3.0
+    return per * B * T * H
+
+
+def tile_flops(B, T, H, K, V, C):
+    """FLOPs of the same products counted as dense tiles (every C x C product in
+    full, the inverse as C^3/3 per chunk): per token-head 6CK + 4CV + 6KV + C^2/3
+    (10Cd + 6d^2 + C^2/3 when K = V = d)."""
+    per = 6 * C * K + 4 * C * V + 6 * K * V + C * C / 3.0
     return per * B * T * H
 
 
@@ -532,8 +541,9 @@ def main():
         ro, rs = oracle.fwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["initial_state"])
         eo = float(np.linalg.norm(outs[0].double().cpu().numpy() - ro) / np.linalg.norm(ro))
         es = float(np.linalg.norm(states[0].double().cpu().numpy() - rs) / np.linalg.norm(rs))
-        gate = {"rel_l2_o": eo, "rel_l2_final_state": es, "tol": 2e-2}
-        if not (eo <= 2e-2 and es <= 2e-2):
+        tol = 2e-2 if w.dtype == torch.bfloat16 else 1e-5
+        gate = {"rel_l2_o": eo, "rel_l2_final_state": es, "tol": tol}
+        if not (eo <= tol and es <= tol):
             print("correctness gate failed: %s" % json.dumps(gate), file=sys.stderr)
             sys.exit(1)
 
@@ -566,6 +576,8 @@ def main():
     abytes = algorithmic_bytes(B, T, H, K, V, esz=2 if w.dtype == torch.bfloat16 else 4,
                                with_s0=w.s0_std is not None)
     aflops = algorithmic_flops(B, T, H, K, V, C)
+    tflops_tile = tile_flops(B, T, H, K, V, C)
+    peak = BF16_PEAK_TFLOPS if w.dtype == torch.bfloat16 else F32_PEAK_TFLOPS
     achieved_gbs = abytes / (kern_ms / 1e3) / 1e9
     traffic = measured_traffic() if args.workload == "train_bf16" else None
     tflops = aflops / (kern_ms / 1e3) / 1e12
@@ -636,11 +648,15 @@ def main():
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel_ms": kern_ms, "kernel_ms_pct": pcts, "algorithmic_bytes": abytes,
                      "copy_gbs": copy_gbs, "frac_of_copy": achieved_gbs / copy_gbs},
-        "mfma": {"tflops_algorithmic": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
-                 "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flops": aflops,
+        "mfma": {"tflops_algorithmic": tflops, "peak_tflops": peak,
+                 "peak_dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+                 "frac": tflops / peak, "algorithmic_flops": aflops,
+                 "tile_flops": tflops_tile,
+                 "tflops_tile": tflops_tile / (kern_ms / 1e3) / 1e12,
+                 "frac_tile": tflops_tile / (kern_ms / 1e3) / 1e12 / peak,
                  "executed_flops": xflops,
                  "tflops_executed": xflops / (kern_ms / 1e3) / 1e12 if xflops else None,
-                 "frac_executed": xflops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS if xflops else None},
+                 "frac_executed": xflops / (kern_ms / 1e3) / 1e12 / peak if xflops else None},
         "cpu_baseline": cpu,
         "gate": gate,
     }

@@ -24,7 +24,10 @@
  * Conventions shared by every entry point:
  *  - All pointers are DEVICE pointers (memory from hipMalloc or a torch CUDA
  *    tensor on the current device), except where stated.  The caller owns every
- *    buffer; the library allocates no device memory for these calls.
+ *    buffer; the library allocates no device memory for these calls, with one
+ *    exception: the float32 forward (gdn_chunk_fwd and gdn_chunk_fwd_varlen with
+ *    GDN_DTYPE_F32) takes a stream-ordered scratch of per-chunk factors from a
+ *    library-owned memory pool on the stream's device (see gdn_chunk_fwd).
  *  - Tensors are dense, contiguous and row-major, each at least 16-byte aligned:
  *        q, k            [B, T, H, K]   element type `dtype`
  *        v, o            [B, T, H, V]   element type `dtype`
@@ -102,6 +105,16 @@ GDN_API const char *gdn_status_string(gdn_status_t status);
  * every output element has one writer and every sum runs in a fixed order.
  * Sizes: B*T*H*max(K,V) must stay below 2^31 elements and the state B*H*V*K
  * at or below 2^31; larger calls return GDN_ERROR_NOT_SUPPORTED.
+ *
+ * Float32 inputs run on the fp32 matrix cores in two launches: one over
+ * (chunk, head) that builds the state-independent factors of every chunk
+ * (cumulative gates, Tm = (I + A)^-1 scaled by beta, the decayed Q K^T), then
+ * the walk over chunks.  The factors, (2 chunk^2 + 2 chunk + 4) * 4 bytes per
+ * (chunk, head) (33 KB at chunk 64; about B*T*H/chunk of them), live in a
+ * stream-ordered allocation from a library-owned pool (hipMallocFromPoolAsync
+ * on `stream`, hipFreeAsync on `stream` after the launches; the pool keeps the
+ * memory for later calls).  If that allocation fails the call returns
+ * GDN_ERROR_LAUNCH.  Bfloat16 inputs allocate nothing.
  */
 GDN_API gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *alpha, const float *beta,

@@ -186,13 +186,11 @@ hipError_t launch_scalar(const FwdArgs& a, float* s_ckpt, hipStream_t stream) {
   const int C = a.chunk;
   const size_t LK = a.K + 1;
   const size_t lds = sizeof(float) * (2 * C * LK + C * VS + 2 * C * C + 2 * C * VS + VS * LK + 3 * C);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_f32_kernel<TIn>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every launch: the attribute belongs to the current device, and a
+  // process-wide "already set" flag would be a data race between host threads
+  hipError_t e = hipFuncSetAttribute((const void*)fwd_f32_kernel<TIn>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e != hipSuccess) return e;
   dim3 grid(a.V / VS * a.H * a.B);
   hipLaunchKernelGGL(fwd_f32_kernel<TIn>, grid, dim3(kThreads), lds, stream,
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
@@ -203,7 +201,7 @@ hipError_t launch_scalar(const FwdArgs& a, float* s_ckpt, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd_f32_scalar(const FwdArgs& a, hipStream_t stream) {
   return launch_scalar<float>(a, nullptr, stream);
 }
 

@@ -26,8 +26,17 @@ struct FwdArgs {
   int vs = 0;
 };
 
-// Float32 q/k/v/o: scalar fp32 kernel (exact fp32 products and sums).
+// Float32 q/k/v/o on the fp32 matrix cores (fwd_f32_mfma.hip): a chunk-parallel
+// launch writes per-(chunk, head) records (gates, Tm, P), then the walk over
+// chunks.  launch_fwd_f32 takes the records from a library-owned stream-ordered
+// pool; launch_fwd_f32_records takes them from the caller
+// (fwd_f32_record_bytes(a) bytes, 16-byte aligned).
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32_records(const FwdArgs& a, float* rec, hipStream_t stream);
+size_t fwd_f32_record_bytes(const FwdArgs& a);
+bool fwd_f32_mfma_supported(int K, int V, int chunk);
+// Float32 q/k/v/o: scalar fp32 kernel (exact fp32 products and sums), no scratch.
+hipError_t launch_fwd_f32_scalar(const FwdArgs& a, hipStream_t stream);
 
 // Chunk-start states only (o null): the state at every chunk start to s_ckpt
 // [B,H,NT,V,K] -- the scalar fp32 kernel for float32 inputs, the MFMA kernel for

@@ -301,7 +301,7 @@ hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int P, void* worksp
   float* Nseg = reinterpret_cast<float*>(ws + g.N_off);
   float* start = reinterpret_cast<float*>(ws + g.start_off);
   float* ends = reinterpret_cast<float*>(ws + g.ends_off);
-  auto fwd = [&](const FwdArgs& f) { return bf16 ? launch_fwd_bf16(f, stream) : launch_fwd_f32(f, stream); };
+  auto fwd = [&](const FwdArgs& f) { return bf16 ? launch_fwd_bf16(f, stream) : launch_fwd_f32_scalar(f, stream); };
   hipError_t e;
 
   hipLaunchKernelGGL(seg_init_kernel, dim3(256), dim3(kThreads), 0, stream, cu, ident, a.B, a.T,

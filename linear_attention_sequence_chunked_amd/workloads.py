@@ -51,6 +51,9 @@ WORKLOADS = {
                          note="mid bf16 forward, B2 T2048 H4 K=V=128, chunk 64"),
     "train_bf16": Workload("train_bf16", 8, 4096, 6, 128, 128, 64, torch.bfloat16, "decay", seed=3,
                            note="training-shape forward, B8 T4096 H6 K=V=128, chunk 64"),
+    "train_f32": Workload("train_f32", 8, 4096, 6, 128, 128, 64, torch.float32, "decay", seed=3,
+                          note="training-shape forward with float32 q, k, v, o, B8 T4096 H6 "
+                               "K=V=128, chunk 64"),
     "fwdbwd_bf16": Workload("fwdbwd_bf16", 4, 2048, 6, 128, 128, 64, torch.bfloat16, "decay",
                             with_do=True, seed=4,
                             note="forward+backward shape, B4 T2048 H6 K=V=128, chunk 64"),

@@ -52,7 +52,7 @@ def check(inp, chunk, tol, label=""):
     return o, sf
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "mid_bf16", "train_bf16", "fwdbwd_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "mid_bf16", "train_bf16", "train_f32", "fwdbwd_bf16"])
 def test_workload_parity(name):
     w = WORKLOADS[name]
     inp = workload_inputs(w)
