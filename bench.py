@@ -185,7 +185,7 @@ def bench_backward(args):
     B, T, H, K, V, C = w.B, w.T, w.H, w.K, w.V, w.chunk
     cpu = workload_inputs(w)
     g = {n: (t.to(dev) if t is not None else None) for n, t in cpu.items()}
-    ws = torch.empty(bwd_workspace_size(B, T, H, K, V, C, dtype=dtype), dtype=torch.uint8, device=dev)
+    ws = torch.empty(bwd_workspace_size(B, T, H, K, V, C, dtype=w.dtype), dtype=torch.uint8, device=dev)
 
     def step():
         return chunk_bwd(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["d_o"],

@@ -354,82 +354,83 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         *reinterpret_cast<f32x4*>(&d_s0[sbase + (size_t)ls * KD + 16 * cb + 4 * lg]) = dS[cb];
   } else {
     // ============================= staging waves =============================
-    // Chunk c is loaded into registers one iteration before it is written to
-    // LDS; 128 staging lanes.
+    // Chunk c is loaded into registers two iterations before it is written to
+    // LDS, in one of two register sets (alternating; the loop is unrolled by
+    // two so that each set keeps its registers); 128 staging lanes.  Every load
+    // is unconditional (past the end of the sequence a row reads the chunk's
+    // first row, past the first chunk the load repeats chunk 0) and the values
+    // are zeroed where needed only when staged, so the wait before staging a
+    // set leaves the other set's loads in flight.
     constexpr int NSL = 128;
     constexpr int NKP = kC * KD / 8;              // 16-byte pieces of a key tile
-    constexpr int KPL = (NKP + NSL - 1) / NSL;
+    constexpr int KPL = NKP / NSL;
     constexpr int NMP = kC * kC / 8;              // pieces of a C x C tile
-    constexpr int MPL = (NMP + NSL - 1) / NSL;
+    constexpr int MPL = NMP / NSL;
+    static_assert(NKP % NSL == 0 && NMP % NSL == 0, "staging pieces");
     const int sl = tid - 128;
     struct Regs {
       bf16x8 k[KPL], q[KPL], tm[MPL], p[MPL], dof[2];
       float g[2], gl, gn, bt;
     };
     auto load = [&](int c, Regs& R) {
+      c = c > 0 ? c : 0;
       const int t0 = c * kC, n = min(kC, T - t0);
       const unsigned char* rc = rec_bh + (size_t)c * kRecBytes;
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const int p = sl + NSL * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
-        R.k[j] = zero8();
-        R.q[j] = zero8();
-        if (p < NKP && r < n) {
-          const size_t off = ((size_t)b * T + t0 + r) * tokk + (size_t)h * KD + c8;
-          R.k[j] = *reinterpret_cast<const bf16x8*>(k + off);
-          R.q[j] = *reinterpret_cast<const bf16x8*>(q + off);
-        }
+        const size_t off = ((size_t)b * T + t0 + (r < n ? r : 0)) * tokk + (size_t)h * KD + c8;
+        R.k[j] = *reinterpret_cast<const bf16x8*>(k + off);
+        R.q[j] = *reinterpret_cast<const bf16x8*>(q + off);
       }
 #pragma unroll
       for (int j = 0; j < MPL; ++j) {
         const int p = sl + NSL * j;
-        if (p < NMP) {
-          R.tm[j] = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * p);
-          R.p[j] = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * p);
-        }
+        R.tm[j] = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * p);
+        R.p[j] = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * p);
       }
       // dO pieces: piece p = sl + 128 j is token p / 4, values 8 (p % 4) .. + 7
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int p = sl + NSL * j, dr = p >> 2;
-        R.dof[j] = zero8();
-        if (dr < n)
-          R.dof[j] = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)b * T + t0 + dr) * tokv + (size_t)h * V + v0 + 8 * (p & 3));
+        R.dof[j] = *reinterpret_cast<const bf16x8*>(
+            d_o + ((size_t)b * T + t0 + (dr < n ? dr : 0)) * tokv + (size_t)h * V + v0 + 8 * (p & 3));
         R.g[j] = reinterpret_cast<const float*>(rc + kRecG)[dr];
       }
-      // gates of token sl (first 64 lanes)
-      if (sl < kC) {
-        R.gl = reinterpret_cast<const float*>(rc + kRecG)[sl];
-        R.gn = reinterpret_cast<const float*>(rc + kRecG)[kC - 1];
-        R.bt = reinterpret_cast<const float*>(rc + kRecB)[sl];
-      }
+      // gates of token sl (lanes sl >= 64 read token sl - 64 and are not staged);
+      // the chunk's last gate is the same for every lane: through a vector
+      // register offset it stays a vector load (a scalar load would be waited
+      // for with the LDS counter)
+      int z = 0;
+      asm volatile("" : "+v"(z));
+      R.gl = reinterpret_cast<const float*>(rc + kRecG)[sl & (kC - 1)];
+      R.gn = reinterpret_cast<const float*>(rc + kRecG)[kC - 1 + z];
+      R.bt = reinterpret_cast<const float*>(rc + kRecB)[sl & (kC - 1)];
     };
     auto stage = [&](int c, const Regs& R) {
       SL& s = slot[c & 1];
+      const int n = min(kC, T - c * kC);
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const int p = sl + NSL * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
-        if (p < NKP) {
-          *reinterpret_cast<bf16x8*>(&s.k[r * LDK + c8]) = R.k[j];
-          *reinterpret_cast<bf16x8*>(&s.q[r * LDK + c8]) = R.q[j];
-        }
+        *reinterpret_cast<bf16x8*>(&s.k[r * LDK + c8]) = r < n ? R.k[j] : zero8();
+        *reinterpret_cast<bf16x8*>(&s.q[r * LDK + c8]) = r < n ? R.q[j] : zero8();
       }
 #pragma unroll
       for (int j = 0; j < MPL; ++j) {
         const int p = sl + NSL * j, r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
-        if (p < NMP) {
-          *reinterpret_cast<bf16x8*>(&s.tm[r * kLDC + c8]) = R.tm[j];
-          *reinterpret_cast<bf16x8*>(&s.p[r * kLDC + c8]) = R.p[j];
-        }
+        *reinterpret_cast<bf16x8*>(&s.tm[r * kLDC + c8]) = R.tm[j];
+        *reinterpret_cast<bf16x8*>(&s.p[r * kLDC + c8]) = R.p[j];
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int p = sl + NSL * j, dr = p >> 2, c8 = 8 * (p & 3);
+        const bf16x8 dof = dr < n ? R.dof[j] : zero8();
         const float gm = __builtin_amdgcn_exp2f(R.g[j]);
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = gm * bf2f(R.dof[j][e]);
-        *reinterpret_cast<bf16x8*>(&s.dob[dr * kLDV + c8]) = R.dof[j];
+        for (int e = 0; e < 8; ++e) x[e] = gm * bf2f(dof[e]);
+        *reinterpret_cast<bf16x8*>(&s.dob[dr * kLDV + c8]) = dof;
         *reinterpret_cast<bf16x8*>(&s.dog[dr * kLDV + c8]) = to_bf8(x);
       }
       if (sl < kC) {
@@ -438,17 +439,27 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         if (sl == 0) s.gamn[0] = __builtin_amdgcn_exp2f(R.gn);
       }
     };
-    Regs R;
-    load(NT - 1, R);
-    stage(NT - 1, R);
-    if (NT >= 2) load(NT - 2, R);
-    for (int c = NT - 1; c >= 0; --c) {
+    // chunk x_j = NT - 1 - j is staged at step j (step 0 before the loop, step
+    // j >= 1 after the chain's j-th barrier) from set j % 2, which is then
+    // reloaded with x_{j+2}
+    Regs R0, R1;
+    load(NT - 1, R0);
+    load(NT - 2, R1);
+    stage(NT - 1, R0);
+    load(NT - 3, R0);
+    // (no step's stage or load is conditional, which keeps the wait counts exact)
+    auto step = [&](int j, Regs& R) {
       lds_barrier();
-      if (c >= 1) {
-        stage(c - 1, R);
-        if (c >= 2) load(c - 2, R);
-      }
+      stage(NT - 1 - j, R);
+      load(NT - 3 - j, R);
+    };
+    int j = 1;
+    for (; j + 1 <= NT - 1; j += 2) {
+      step(j, R1);
+      step(j + 1, R0);
     }
+    if (j <= NT - 1) step(j, R1);
+    lds_barrier();   // the chain's last chunk
   }
 }
 
