@@ -55,19 +55,25 @@ __device__ __forceinline__ f32x4 zero4f() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 
-// Record of one (chunk, head): Tm diag(beta) [C][C] and P [C][C] row-major
-// (blocks right of the diagonal block are not written and never read), then
-// gam_t = 2^g_t [C], dn_t = 2^(g_n - g_t) [C] and 2^g_n (padded to 4 floats).
-// With beta folded into Tm the walk forms U = (Tm diag(beta)) (V - diag(gam) X).
-// The one definition of the record size, used by the kernels and by the
-// host's allocation alike.
-constexpr int record_floats(int C) { return 2 * C * C + 2 * C + 4; }
+// Record of one (chunk, head): the lower 16 x 16 blocks of Tm diag(beta), then
+// those of P, each block 256 floats row-major and block (I, J <= I) at index
+// I (I + 1) / 2 + J, so that a wave's float4 operand load of a block is one
+// contiguous kilobyte; then gam_t = 2^g_t [C], dn_t = 2^(g_n - g_t) [C] and 2^g_n
+// (padded to 4 floats).  With beta folded into Tm the walk forms
+// U = (Tm diag(beta)) (V - diag(gam) X).  record_floats is the one definition of
+// the record size, used by the kernels and by the host's allocation alike.
+constexpr int record_blocks(int C) { return (C / 16) * (C / 16 + 1) / 2; }
+constexpr int record_floats(int C) { return 2 * record_blocks(C) * 256 + 2 * C + 4; }
 template <int C>
 struct Rec {
-  static constexpr int kTm = 0, kP = C * C, kGam = 2 * C * C, kDn = 2 * C * C + C,
-                       kGn = 2 * C * C + 2 * C;
+  static constexpr int kTm = 0, kP = record_blocks(C) * 256, kGam = 2 * record_blocks(C) * 256,
+                       kDn = kGam + C, kGn = kGam + 2 * C;
   static constexpr int kFloats = record_floats(C);
   static_assert(kGn + 4 == kFloats, "record layout");
+  // offset of element (r, c) of lower block (I, J)
+  static __device__ __forceinline__ int at(int I, int J, int r, int c) {
+    return (I * (I + 1) / 2 + J) * 256 + r * 16 + c;
+  }
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
@@ -179,7 +185,7 @@ f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * I + 4 * g + e;
         if (pkind) {
-          R[Rec<C>::kP + i * C + j] = j <= i ? exp2f(sg[i] - sg[j]) * acc[e] : 0.0f;
+          R[Rec<C>::kP + Rec<C>::at(I, J, 4 * g + e, s)] = j <= i ? exp2f(sg[i] - sg[j]) * acc[e] : 0.0f;
         } else {
           sA[i * LC + j] = j < i ? sb[i] * exp2f(sg[i] - sg[j]) * acc[e] : 0.0f;
         }
@@ -229,10 +235,11 @@ f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
   }
   // Tm diag(beta) (lower blocks) and the gate factors to the record.  Padded
   // tokens have log2 alpha = 0, so g_{C-1} = g_{n-1}.
-  for (int i = tid; i < C * (C / 4); i += 256) {
-    const int r = i / (C / 4), c4 = i - r * (C / 4);
-    if (4 * c4 < 16 * (r / 16 + 1))
-      st4(R + Rec<C>::kTm + r * C + 4 * c4, ld4(sT + r * LC + 4 * c4) * ld4(sb + 4 * c4));
+  for (int i = tid; i < record_blocks(C) * 64; i += 256) {
+    const int blk = i >> 6, r = (i >> 2) & 15, c4 = i & 3;
+    const int I = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0, J = blk - I * (I + 1) / 2;
+    st4(R + Rec<C>::kTm + Rec<C>::at(I, J, r, 4 * c4),
+        ld4(sT + (16 * I + r) * LC + 16 * J + 4 * c4) * ld4(sb + 16 * J + 4 * c4));
   }
   if (tid < C) {
     const float gl = sg[C - 1];
@@ -243,47 +250,62 @@ f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
-// Launch 2: the walk over chunks.  One workgroup per (sequence, head, 16 value
-// rows), NB = C / 16 waves: wave w owns token rows 16w .. 16w + 15 of every
-// chunk for X, Z, R, U and O, and state tiles kappa = w, w + NB, ... (16 key
-// channels each) for the update.  The state slice S[v0 .. v0 + 15][0 .. KD)
-// lives in the owners' accumulators and, for the X and Z products, in LDS.
+// Launch 2: the walk over chunks.  One workgroup per (sequence, head, 16 NG
+// value rows): NG groups of NB = C / 16 waves, group j owning value rows
+// v0 + 16 j .. + 15.  Within a group, wave w owns token rows 16w .. 16w + 15 of
+// every chunk for X, Z, R', U and O, and state tiles kappa = w, w + NB, ...
+// (16 key channels each) for the update.  The state slice lives in the owners'
+// accumulators and, for the X and Z products, in the group's LDS.  The chunk's
+// key and query tiles are staged once per workgroup in LDS (keys double
+// buffered), loaded with whole-row pieces two chunks ahead; the groups share
+// them.
+//
 // WO: outputs wanted (q and o used); HV: values given (else V = 0); CK: chunk-start
-// states to s_ckpt [B, H, NT, V, K].  Loads are
-// unconditional, so that none sits under a branch and the compiler's wait
-// counts stay exact across the loop, and their values are used as loaded (a
-// select would make the load wait at once).  Rows past the chunk end read the
-// chunk's first row instead: their X, Z and R' rows are finite junk that meets
-// only zeros -- the record's Tm diag(beta) has zero columns there (beta = 0) and
-// identity-times-beta rows, so those rows of U are exactly 0, and their O rows
-// are not stored.  Blocks right of the diagonal block are loaded as the
-// diagonal block and skipped by the products.
-template <int KD, int C, bool WO, bool HV, bool CK>
-__global__ void __launch_bounds__(64 * (C / 16), 2)
+// states to s_ckpt [B, H, NT, V, K].  No global load sits under a branch, so
+// the compiler's wait counts stay exact across the loop, and loaded values are
+// used as loaded (a select would make the load wait at once).  Rows past the
+// chunk end read the chunk's first row instead: their X, Z and R' rows are finite
+// junk that meets only zeros -- the record's Tm diag(beta) has zero columns there
+// (beta = 0) and identity-times-beta rows, so those rows of U are exactly 0 and
+// the state update adds 0 for them, and their O rows are not stored.  Blocks
+// right of the diagonal block are loaded as the diagonal block and skipped by the
+// products.
+template <int KD, int C, int NG, bool WO, bool HV, bool CK>
+__global__ void __launch_bounds__(64 * NG * (C / 16), 1)
 f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
                  const float* __restrict__ v, const float* __restrict__ s0, float* __restrict__ o,
                  float* __restrict__ s_final, float* __restrict__ s_ckpt,
                  const float* __restrict__ rec, const int* __restrict__ cu, int B, int T, int H,
                  int V, int NT) {
   constexpr int NB = C / 16;
+  constexpr int NTH = 64 * NG * NB;
   constexpr int KQ = KD / 16;             // key-channel tiles
   constexpr int NKT = (KQ + NB - 1) / NB; // state tiles per wave (upper bound)
   constexpr int LS = KD + 4;
   constexpr int LC = C + 4;
-  __shared__ __attribute__((aligned(16))) float sS[16 * LS];   // S[v][k]
-  __shared__ __attribute__((aligned(16))) float sR[16 * LC];   // R^T[v][t]
-  __shared__ __attribute__((aligned(16))) float sU[16 * LC];   // U^T[v][t]
-  __shared__ __attribute__((aligned(16))) float sKd[C * LS];   // diag(dn) K [t][k]
+  constexpr int TP = C * KD / 4;          // float4 pieces of a key (query) tile
+  constexpr int PPT = (TP + NTH - 1) / NTH;
+  struct Grp {
+    float sS[16 * LS];                    // S[v][k]
+    float sR[16 * LC];                    // R'^T[v][t]
+    float sU[16 * LC];                    // U^T[v][t]
+    float sUd[16 * LC];                   // (diag(dn) U)^T[v][t]
+  };
+  __shared__ __attribute__((aligned(16))) float sK[2][C * LS];   // K [t][k]
+  __shared__ __attribute__((aligned(16))) float sQ[WO ? C * LS : 4];
+  __shared__ __attribute__((aligned(16))) Grp grp[NG];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wg = tid >> 6;
+  const int gi = wg / NB, w = wg - gi * NB;   // group, token block
   const int s = lane & 15, g = lane >> 4;
+  Grp& G = grp[gi];
   // workgroups of one (sequence, head) share an XCD (dispatch is round-robin
   // over the 8 XCDs), so its records and key rows are fetched into one L2
-  const int nvs = V / 16, streams = B * H;
+  const int nvs = V / (16 * NG), streams = B * H;
   const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
   const int stream = xcd + 8 * (jx / nvs);
   if (stream >= streams) return;
-  const int v0 = 16 * (jx - (jx / nvs) * nvs);
+  const int v0 = 16 * NG * (jx - (jx / nvs) * nvs) + 16 * gi;
   const int b = stream / H, h = stream - b * H;
 
   size_t seq0;
@@ -307,37 +329,43 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
   for (int m = 0; m < NKT; ++m) {
     const int kap = w + NB * m;
     S[m] = (s0 && kap < KQ) ? ld4(s0 + sbase + 16 * kap + 4 * g) : zero4f();
-    if (kap < KQ) st4(sS + s * LS + 16 * kap + 4 * g, S[m]);
+    if (kap < KQ) st4(G.sS + s * LS + 16 * kap + 4 * g, S[m]);
   }
 
-  // Operands are loaded one chunk ahead, all of them right after the X and Z
-  // products of the chunk before.  gfx9 counts loads and stores in one counter
-  // and a wait for a load while a store is pending waits for everything, so the
-  // output rows of a chunk are stored one chunk late, after the next chunk's
-  // first wait, and every wait then finds loads issued a whole chunk earlier.
-  // The key / query rows are reloaded in place once X and Z have used them; the
-  // other operands alternate between two sets (the loop is unrolled by two), so
-  // no register copy at the back edge waits for a load.
-  struct Ops {
-    f32x4 vv, gw;                  // values and gam of rows 16w + 4g + e (R)
-    f32x4 tmr[NB], pr[NB];         // Tm diag(beta) / P rows 16w + s (U, O)
-    float dnr, gn;                 // dn of row 16w + s, 2^g_n
-  };
-  f32x4 ka[KQ], qa[KQ];            // key / query rows 16w + s (X, Z)
-  Ops opa, opb;
-  opa.vv = opb.vv = zero4f();
   auto rec_of = [&](int cc) { return rec + ((size_t)(slot0 + cc) * H + h) * Rec<C>::kFloats; };
   auto row_of = [&](int cc) { return (seq0 + (size_t)cc * C) * H + h; };
   auto n_of = [&](int cc) { return min(C, Tn - cc * C); };
-  auto load_rows = [&](int cc) {
-    const int r = 16 * w + s;
-    const bool ok = r < n_of(cc);
-    const size_t off = (row_of(cc) + (size_t)(ok ? r : 0) * H) * KD + 4 * g;
+
+  // key / query tiles: piece p = tid + NTH j is row p / (KD / 4), channels
+  // 4 (p % (KD / 4)) .. + 3, so a wave reads whole 512-byte rows
+  f32x4 kreg[PPT], qreg[PPT];
+  auto load_tiles = [&](int cc) {
+    const int n = n_of(cc);
+    const size_t r0 = row_of(cc);
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) {
-      ka[kq] = ld4(k + off + 16 * kq);
-      if (WO) qa[kq] = ld4(q + off + 16 * kq);
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
+      const bool ok = p < TP && r < n;
+      const size_t off = (r0 + (size_t)(ok ? r : 0) * H) * KD + 4 * (ok ? c4 : 0);
+      kreg[j] = ld4(k + off);
+      if (WO) qreg[j] = ld4(q + off);
     }
+  };
+  auto stage_tiles = [&](int cc) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
+      if (p < TP) {
+        st4(sK[cc & 1] + r * LS + 4 * c4, kreg[j]);
+        if (WO) st4(sQ + r * LS + 4 * c4, qreg[j]);
+      }
+    }
+  };
+  // per-wave operands of one chunk, in two alternating sets
+  struct Ops {
+    f32x4 vv, gw, dn;              // values, gam and dn of rows 16w + 4g + e
+    f32x4 tmr[NB], pr[NB];         // Tm diag(beta) / P rows 16w + s (U, O)
+    float gn;                      // 2^g_n
   };
   auto load_ops = [&](int cc, Ops& d) {
     const int n = n_of(cc);
@@ -351,21 +379,22 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
     const float* Rc = rec_of(cc);
     d.gw = ld4(Rc + Rec<C>::kGam + 16 * w + 4 * g);
-    d.dnr = Rc[Rec<C>::kDn + 16 * w + s];
+    d.dn = ld4(Rc + Rec<C>::kDn + 16 * w + 4 * g);
     // 2^g_n is the same for every lane: through a vector register offset it stays
     // a vector load (a scalar load is waited for with the LDS counter, which the
     // next LDS barrier drains)
     int z = 0;
     asm volatile("" : "+v"(z));
     d.gn = Rc[Rec<C>::kGn + z];
-    const float* Rt = Rc + Rec<C>::kTm + (16 * w + s) * C + 4 * g;
-    const float* Rp = Rc + Rec<C>::kP + (16 * w + s) * C + 4 * g;
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
-      d.tmr[J] = ld4(Rt + 16 * (J <= w ? J : w));
-      if (WO) d.pr[J] = ld4(Rp + 16 * (J <= w ? J : w));
+      const int o4 = Rec<C>::at(w, J <= w ? J : w, s, 4 * g);
+      d.tmr[J] = ld4(Rc + Rec<C>::kTm + o4);
+      if (WO) d.pr[J] = ld4(Rc + Rec<C>::kP + o4);
     }
   };
+  Ops opa, opb;
+  opa.vv = opb.vv = zero4f();
   // output rows of the previous chunk, stored one chunk late
   f32x4 Oprev = zero4f();
   size_t oprev = 0;
@@ -377,19 +406,27 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
   };
   if (nch > 0) {
-    load_rows(0);
+    load_tiles(0);
+    stage_tiles(0);
+    load_tiles(nch > 1 ? 1 : 0);
     load_ops(0, opa);
   }
   __syncthreads();
 
-  // One chunk with operands cur, loading chunk c + 1's into nxt (the last chunk
-  // reloads its own: no load is conditional, which keeps the wait counts exact).
-  // TAIL: the last, partial chunk.  The empty asm statements take the
-  // consumer's results and clobber memory, so that a consumer is done before
-  // the loads that reuse its registers are issued.
+  // One chunk with operands cur, loading chunk c + 1's into nxt and chunk c + 2's
+  // key / query tiles (past the end the loads repeat the last chunk: no load is
+  // conditional).  TAIL: the last, partial chunk.  gfx9 counts loads and stores
+  // in one counter and a wait for a load while a store is pending waits for
+  // everything, so the previous chunk's output rows are stored right after this
+  // chunk's one real wait (for cur), and every wait finds its loads issued a
+  // chunk earlier.  The empty asm statements take the consumer's results and
+  // clobber memory, so that a consumer is done before the loads that reuse its
+  // registers are issued.
   auto body = [&](int c, auto tail, Ops& cur, Ops& nxt) {
     constexpr bool TAIL = decltype(tail)::value;
     const int cn = c + 1 < nch ? c + 1 : c;
+    const int cn2 = c + 2 < nch ? c + 2 : nch - 1;
+    const float* kt = sK[c & 1];
     if (CK) {
 #pragma unroll
       for (int m = 0; m < NKT; ++m) {
@@ -400,50 +437,51 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
       }
     }
 
+    // the next chunk's operands go to the other set, whose last reader was the
+    // previous chunk: issued first, they overlap the products below
+    load_ops(cn, nxt);
+
     // X = K S^T and Z = Q S^T for this wave's 16 token rows
     f32x4 X = zero4f(), Z = zero4f();
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
-      const f32x4 bs = ld4(sS + s * LS + 16 * kq + 4 * g);
-      X = mma16(ka[kq], bs, X);
-      if (WO) Z = mma16(qa[kq], bs, Z);
+      const f32x4 bs = ld4(G.sS + s * LS + 16 * kq + 4 * g);
+      X = mma16(ld4(kt + (16 * w + s) * LS + 16 * kq + 4 * g), bs, X);
+      if (WO) Z = mma16(ld4(sQ + (16 * w + s) * LS + 16 * kq + 4 * g), bs, Z);
     }
-    // diag(dn) K to LDS: its columns are the left operand of the state update
-#pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) st4(sKd + (16 * w + s) * LS + 16 * kq + 4 * g, ka[kq] * cur.dnr);
-    asm volatile("" : "+v"(X), "+v"(Z) : : "memory");
-    load_rows(cn);
-    load_ops(cn, nxt);
-    if (WO && c > 0) store_o(oprev, C, false);
-
     // R' = V - diag(gam) X (beta is in the record's Tm); Z <- diag(gam) Z
-    const f32x4 Rv = cur.vv - cur.gw * X;
+    f32x4 Rv = cur.vv - cur.gw * X;
     Z *= cur.gw;
-    st4(sR + s * LC + 16 * w + 4 * g, Rv);
+    asm volatile("" : "+v"(Rv), "+v"(Z) : : "memory");
+    if (WO && c > 0) store_o(oprev, C, false);
+    st4(G.sR + s * LC + 16 * w + 4 * g, Rv);
     mfma::lds_barrier();
+
+    // chunk c + 1's tiles to LDS (Q(c) is dead, K(c + 1) has the other buffer);
+    // the registers are reloaded with chunk c + 2's
+    stage_tiles(c + 1);
+    load_tiles(cn2);
 
     // U = Tm diag(beta) R' (rows of this block; lower block-triangular)
     f32x4 U = zero4f();
 #pragma unroll
     for (int J = 0; J < NB; ++J)
-      if (J <= w) U = mma16(cur.tmr[J], ld4(sR + s * LC + 16 * J + 4 * g), U);
-    st4(sU + s * LC + 16 * w + 4 * g, U);
+      if (J <= w) U = mma16(cur.tmr[J], ld4(G.sR + s * LC + 16 * J + 4 * g), U);
+    st4(G.sU + s * LC + 16 * w + 4 * g, U);
+    st4(G.sUd + s * LC + 16 * w + 4 * g, U * cur.dn);
     mfma::lds_barrier();
 
-    f32x4 ub[NB];
-#pragma unroll
-    for (int J = 0; J < NB; ++J) ub[J] = ld4(sU + s * LC + 16 * J + 4 * g);
     // O = diag(gam) Z + P U
     if (WO) {
       f32x4 O = Z;
 #pragma unroll
       for (int J = 0; J < NB; ++J)
-        if (J <= w) O = mma16(cur.pr[J], ub[J], O);
+        if (J <= w) O = mma16(cur.pr[J], ld4(G.sU + s * LC + 16 * J + 4 * g), O);
       Oprev = O;
       oprev = row_of(c);
       if (TAIL) store_o(oprev, n_of(c), true);
     }
-    // S^T <- 2^g_n S^T + (diag(dn) K)^T U for the owned tiles
+    // S^T <- 2^g_n S^T + K^T (diag(dn) U) for the owned tiles
 #pragma unroll
     for (int m = 0; m < NKT; ++m) {
       const int kap = w + NB * m;
@@ -453,11 +491,11 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
       for (int J = 0; J < NB; ++J) {
         f32x4 a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = sKd[(16 * J + 4 * g + e) * LS + 16 * kap + s];
-        acc = mma16(a, ub[J], acc);
+        for (int e = 0; e < 4; ++e) a[e] = kt[(16 * J + 4 * g + e) * LS + 16 * kap + s];
+        acc = mma16(a, ld4(G.sUd + s * LC + 16 * J + 4 * g), acc);
       }
       S[m] = acc;
-      st4(sS + s * LS + 16 * kap + 4 * g, acc);
+      st4(G.sS + s * LS + 16 * kap + 4 * g, acc);
     }
     mfma::lds_barrier();
   };
@@ -485,10 +523,20 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
   }
 }
 
+// Two value groups per workgroup (32 rows) while that still leaves at least
+// 128 workgroups, else one (16 rows, twice the workgroups).
 template <int KD, int C, bool WO, bool HV, bool CK>
 hipError_t launch_chain(const FwdArgs& a, float* rec, int NT, hipStream_t stream) {
   const long groups = ((long)a.B * a.H + 7) / 8;
-  hipLaunchKernelGGL((f32_chain_kernel<KD, C, WO, HV, CK>), dim3(8 * groups * (a.V / 16)),
+  if (a.V % 32 == 0 && (long)a.B * a.H * (a.V / 32) >= 128) {
+    hipLaunchKernelGGL((f32_chain_kernel<KD, C, 2, WO, HV, CK>), dim3(8 * groups * (a.V / 32)),
+                       dim3(128 * (C / 16)), 0, stream, static_cast<const float*>(a.q),
+                       static_cast<const float*>(a.k), static_cast<const float*>(a.v), a.s0,
+                       static_cast<float*>(a.o), a.s_final, a.s_ckpt, rec, a.cu_seqlens, a.B, a.T,
+                       a.H, a.V, NT);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((f32_chain_kernel<KD, C, 1, WO, HV, CK>), dim3(8 * groups * (a.V / 16)),
                      dim3(64 * (C / 16)), 0, stream, static_cast<const float*>(a.q),
                      static_cast<const float*>(a.k), static_cast<const float*>(a.v), a.s0,
                      static_cast<float*>(a.o), a.s_final, a.s_ckpt, rec, a.cu_seqlens, a.B, a.T,
