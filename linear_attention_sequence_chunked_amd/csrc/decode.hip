@@ -43,10 +43,10 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-// One workgroup per (batch, head, group of RPB rows); K / 4 lanes per row.  Each
-// lane issues the loads of all its rows before any arithmetic, so several 16-byte
-// reads per lane are in flight.
-constexpr int kRowsPerBlock = 8;
+// One workgroup per (batch, head, group of rows_per_block(K) rows); K / 4 lanes
+// per row, so every one of the 256 threads owns one 16-byte piece of a row
+// (8 rows at K = 128, 64 at K = 16).
+constexpr int rows_per_block(int K) { return kThreads / (K / 4); }
 
 template <typename TIn, int K>
 __global__ void __launch_bounds__(kThreads)
@@ -55,6 +55,7 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
               float* __restrict__ state, TIn* __restrict__ o, int H, int V) {
   constexpr int LPR = K / 4;                      // lanes per row
   constexpr int RPI = kThreads / LPR;             // rows per pass of the block
+  constexpr int kRowsPerBlock = rows_per_block(K);
   constexpr int NR = (kRowsPerBlock + RPI - 1) / RPI;  // rows per lane
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;                      // b * H + h
@@ -105,7 +106,8 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
 
 template <typename TIn, int K>
 hipError_t launch_k(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.B * a.H, (a.V + kRowsPerBlock - 1) / kRowsPerBlock);
+  constexpr int RPB = rows_per_block(K);
+  dim3 grid(a.B * a.H, (a.V + RPB - 1) / RPB);
   hipLaunchKernelGGL((decode_kernel<TIn, K>), grid, dim3(kThreads), 0, stream,
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                      static_cast<const TIn*>(a.v), a.alpha, a.beta, a.state,
