@@ -25,11 +25,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 F32_PEAK_TFLOPS = 157.3        # MI355X fp32 (matrix and vector), published
 METRIC = "GDN chunk fwd tokens/s + % bf16 MFMA peak at B8·T4096·H6·d128"
 
-# Sources of the timed kernel: a traffic record measured on other sources is stale.
+# Sources of the timed kernel (its body and the device helpers it includes): a
+# traffic record measured on other sources is stale.
 KERNEL_SOURCES = ["linear_attention_sequence_chunked_amd/csrc/fwd_bf16.hip",
-                  "linear_attention_sequence_chunked_amd/csrc/mfma_common.h",
-                  "linear_attention_sequence_chunked_amd/csrc/gdn_api.hip",
-                  "linear_attention_sequence_chunked_amd/csrc/launch.h"]
+                  "linear_attention_sequence_chunked_amd/csrc/mfma_common.h"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "fwd_bf16_train_B8T4096H6_hbm_traffic.md")
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
 
