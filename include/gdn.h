@@ -291,7 +291,11 @@ GDN_API gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v
  *    (batch, head, backward chunk of C = min(chunk, 32) tokens) two float32
  *    [V, K] states and the chunk's float32 factors (three C x C matrices and
  *    three C-vectors):
- *        B * H * ceil(T / C) * (2 * V * K + 3 * C * C + 3 * C) * 4 bytes.
+ *        B * H * ceil(T / C) * (2 * V * K + 3 * C * C + 3 * C) * 4 bytes,
+ *    and for float32 inputs also the per-chunk records of the matrix-core state
+ *    recompute, R(C) = (C/16) (C/16 + 1) * 256 + 2 C + 4 floats each (1604 at
+ *    C = 32, 548 at C = 16):
+ *        + B * H * ceil(T / C) * R(C) * 4 bytes.
  * Returns 0 when a size is not positive or the dtype is not F32 or BF16.
  */
 GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t K,

@@ -675,7 +675,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   f.K = a.K;
   f.V = a.V;
   f.chunk = C;
-  e = launch_fwd_states(f, sizeof(TIn) == 2, ws_S, stream);
+  if constexpr (sizeof(TIn) == 4) {
+    // float32: the matrix-core forward in its states-only mode, its per-chunk
+    // records after the factors in the workspace
+    f.s_ckpt = ws_S;
+    e = launch_fwd_f32_records(f, ws_F + (size_t)a.B * a.H * NT * factor_floats(C), stream);
+  } else {
+    e = launch_fwd_states(f, true, ws_S, stream);
+  }
   if (e != hipSuccess) return e;
 
   // (2a) chunk factors
@@ -734,7 +741,16 @@ size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V
   if (bf16 && bwd_bf16_supported((int)K, (int)V)) return bwd_bf16_workspace_bytes(B, T, H, K, V);
   const int64_t C = chunk < kBwdC ? chunk : kBwdC;
   const int64_t NT = (T + C - 1) / C;
-  return (size_t)(2 * B * H * NT * V * K + B * H * NT * factor_floats((int)C)) * sizeof(float);
+  size_t bytes = (size_t)(2 * B * H * NT * V * K + B * H * NT * factor_floats((int)C)) * sizeof(float);
+  if (!bf16) {  // float32: the records of the matrix-core state recompute
+    FwdArgs f;
+    f.B = (int)B;
+    f.T = (int)T;
+    f.H = (int)H;
+    f.chunk = (int)C;
+    bytes += fwd_f32_record_bytes(f);
+  }
+  return bytes;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {

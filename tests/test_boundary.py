@@ -124,11 +124,15 @@ def test_bwd_workspace_size():
     lib = gdn.load_library()
     F32, BF16 = gdn.GDN_DTYPE_F32, gdn.GDN_DTYPE_BF16
 
-    def scalar(B, T, H, K, V, chunk):
+    def scalar(B, T, H, K, V, chunk, f32=True):
         # float32 path: per (b, h, chunk of min(chunk, 32) tokens) two fp32 [V,K]
-        # states and 3 C x C + 3 C float32 factors
+        # states and 3 C x C + 3 C float32 factors, and for float32 inputs the
+        # state recompute's records: 16 x 16 lower blocks of two C x C matrices,
+        # two C-vectors and 4 floats
         C = min(chunk, 32)
-        return B * H * -(-T // C) * (2 * V * K + 3 * C * C + 3 * C) * 4
+        nb = C // 16
+        rec = nb * (nb + 1) * 256 + 2 * C + 4 if f32 else 0
+        return B * H * -(-T // C) * (2 * V * K + 3 * C * C + 3 * C + rec) * 4
 
     def mfma(B, T, H, K, V):
         # matrix-core path: per 64-token chunk two fp32 [V,K] states and a 16896-byte
@@ -140,7 +144,9 @@ def test_bwd_workspace_size():
     assert lib.gdn_chunk_bwd_workspace_size(0, 17, 1, 16, 16, 16, F32) == 0
     assert lib.gdn_chunk_bwd_workspace_size(1, 17, 1, 16, 16, 16, 7) == 0
     # bf16 with K or V = 16 takes the float32 path
-    assert lib.gdn_chunk_bwd_workspace_size(1, 100, 2, 16, 64, 32, BF16) == scalar(1, 100, 2, 16, 64, 32)
+    assert lib.gdn_chunk_bwd_workspace_size(1, 100, 2, 16, 64, 32, BF16) == \
+        scalar(1, 100, 2, 16, 64, 32, f32=False)
+    assert scalar(1, 64, 1, 16, 16, 32) - scalar(1, 64, 1, 16, 16, 32, f32=False) == 2 * 1604 * 4
     # bf16 with K, V in {32, 64, 128}: the matrix-core layout alone, whatever the chunk
     for chunk in (16, 32, 64):
         assert lib.gdn_chunk_bwd_workspace_size(1, 256, 1, 128, 128, chunk, BF16) == \
