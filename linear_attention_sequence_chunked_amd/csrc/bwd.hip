@@ -675,11 +675,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   f.K = a.K;
   f.V = a.V;
   f.chunk = C;
+  float* ws_R = ws_F + (size_t)a.B * a.H * NT * factor_floats(C);  // float32: the records
   if constexpr (sizeof(TIn) == 4) {
     // float32: the matrix-core forward in its states-only mode, its per-chunk
     // records after the factors in the workspace
     f.s_ckpt = ws_S;
-    e = launch_fwd_f32_records(f, ws_F + (size_t)a.B * a.H * NT * factor_floats(C), stream);
+    e = launch_fwd_f32_records(f, ws_R, stream);
   } else {
     e = launch_fwd_states(f, true, ws_S, stream);
   }
@@ -695,8 +696,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                        ws_F, a.T, a.H, a.K, C);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // (2b) reverse walk
-  {
+  // (2b) reverse walk (float32: on the matrix cores, from the recompute's records)
+  if constexpr (sizeof(TIn) == 4) {
+    if ((e = launch_bwd_f32_dstate(a, C, ws_R, ws_dS, stream)) != hipSuccess) return e;
+  } else {
     const int VS = 16;
     const size_t LK = a.K + 1, LV = VS + 1;
     const size_t lds = sizeof(float) * (2 * C * LK + C * LV + 2 * C * C + 2 * C * LV + VS * LK + 3 * C);

@@ -66,6 +66,11 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk,
                            bool bf16);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
+// Float32 reverse walk on the matrix cores over `chunk`-token chunks (16 or 32),
+// reading the records launch_fwd_f32_records wrote for the same chunks; stores
+// every chunk's end-state gradient to ws_dS [B, H, NT, V, K] and d_s0.
+hipError_t launch_bwd_f32_dstate(const BwdArgs& a, int chunk, const float* rec, float* ws_dS,
+                                 hipStream_t stream);
 
 // Bfloat16 backward on MFMA with 64-token chunks, whatever chunk the caller gave
 // (K and V 32, 64 or 128).  Workspace: chunk-start states, chunk-end state
