@@ -715,8 +715,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     };
     if ((e = with_k(a.K, run)) != hipSuccess) return e;
   }
-  // (3) token gradients
-  {
+  // (3) token gradients (float32: on the matrix cores)
+  if constexpr (sizeof(TIn) == 4) {
+    if ((e = launch_bwd_f32_local(a, C, ws_S, ws_dS, ws_F, stream)) != hipSuccess) return e;
+  } else {
     const size_t LK = a.K + 1, LV = kBwdVS + 1;
     const size_t lds = sizeof(float) * (2 * C * LK + 5 * C * C + 8 * C * LV + 2 * kBwdVS * LK + 7 * C + kThreads);
     auto run = [&](auto kc) -> hipError_t {

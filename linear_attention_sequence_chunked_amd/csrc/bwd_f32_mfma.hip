@@ -223,6 +223,408 @@ f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Token gradients of one chunk on the fp32 matrix cores: one workgroup (four
+// waves) per (chunk, head, batch).  Wave w walks the value axis in 16-wide
+// slices w, w + 4, ...; per slice (with S and dS' the chunk's start state and
+// end-state gradient, the slice's rows):
+//
+//   Y = K S^T, Z = Q S^T, W = K dS'^T, R = diag(beta) V - diag(beta gam) Y
+//   U = Tm R, dU = diag(D) W + P^T dO, dR = Tm^T dU, dV = diag(beta) dR
+//   dP += dO U^T, dA -= dR U^T, dQ += diag(gam) dO S,
+//   dK += diag(D) U dS' - diag(beta gam) dR S
+//
+// and the per-token sums of the gate gradients; the waves' partial dP, dA, dQ,
+// dK and sums are then added in wave order through LDS, and the chunk's
+// token-axis products finish dQ and dK:
+//
+//   dQ += (dP o E) K,  dK += (dP o E)^T Q + (dA o bE) K + (dA o bE)^T K.
+//
+// The factors (M, P, Tm, gates) are the float32 prep's; the gate gradients use
+// its cancellation-free sums (bwd.hip).  Rows past the chunk end are staged as
+// zeros, with zero gates and factors, so they add nothing anywhere.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// sum over the 16 lanes of a lane group, in a fixed order; every lane ends with it
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, 16);
+  return x;
+}
+
+template <int KD, int C>
+__global__ void __launch_bounds__(256, 1)
+f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                 const float* __restrict__ v, const float* __restrict__ d_o,
+                 const float* __restrict__ alpha, const float* __restrict__ ws_S,
+                 const float* __restrict__ ws_dS, const float* __restrict__ ws_F,
+                 float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+                 float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H, int V) {
+  constexpr int NB = C / 16;
+  constexpr int KQ = KD / 16;
+  constexpr int LK = KD + 4, LCC = C + 4, LV = 16 + 4;
+  constexpr int NW = 4;
+  constexpr int NBL = NB * (NB + 1) / 2;       // lower token blocks
+  struct WaveArea {                             // one wave's slice tiles
+    float S[16 * LK], dS[16 * LK];              // [v][k]
+    float dO[C * LV], U[C * LV], dR[C * LV];    // [t][v]
+  };
+  struct Red {                                  // the waves' partials, added in order
+    float dQ[C * KD], dK[C * KD];               // [t][k]
+    float dP[C * LCC], dA[C * LCC];             // [r][i]
+  };
+  union Area {
+    WaveArea wave[NW];
+    Red red;
+  };
+  __shared__ __attribute__((aligned(16))) float sK[C * LK], sQ[C * LK];
+  __shared__ __attribute__((aligned(16))) float sM[C * LCC], sP[C * LCC], sT[C * LCC];
+  __shared__ __attribute__((aligned(16))) Area area;
+  __shared__ float sg[C], sgam[C], sb[C], sD[C];
+  __shared__ float sdb[C], sdg[C], sdu[C], sxr[C], sdot[NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int s = lane & 15, g = lane >> 4;
+  const int NT = (T + C - 1) / C;
+  const int c = blockIdx.x % NT, h = (blockIdx.x / NT) % H, b = blockIdx.x / NT / H;
+  const int t0 = c * C, n = min(C, T - t0);
+  const size_t ck = (((size_t)b * H + h) * NT + c) * (size_t)V * KD;
+  const size_t row0 = ((size_t)b * T + t0) * H + h;   // token row of the chunk's first token
+
+  // key / query tiles (rows past the end zero), the prep's factors and gates
+  for (int i = tid; i < C * (KD / 4); i += 256) {
+    const int r = i / (KD / 4), c4 = i - r * (KD / 4);
+    const bool ok = r < n;
+    const size_t off = (row0 + (size_t)(ok ? r : 0) * H) * KD + 4 * c4;
+    const f32x4 kx = ld4(k + off), qx = ld4(q + off);
+    st4(sK + r * LK + 4 * c4, ok ? kx : zero4f());
+    st4(sQ + r * LK + 4 * c4, ok ? qx : zero4f());
+  }
+  const float* F = ws_F + (((size_t)b * H + h) * NT + c) * (3 * C * C + 3 * C);
+  for (int i = tid; i < C * C; i += 256) {
+    const int r = i / C, j = i - r * C;
+    sM[r * LCC + j] = F[i];
+    sP[r * LCC + j] = F[C * C + i];
+    sT[r * LCC + j] = F[2 * C * C + i];
+  }
+  if (tid < C) {
+    const float gl = F[3 * C * C + n - 1];
+    const bool ok = tid < n;
+    sg[tid] = F[3 * C * C + tid];
+    sgam[tid] = ok ? F[3 * C * C + C + tid] : 0.0f;
+    sb[tid] = ok ? F[3 * C * C + 2 * C + tid] : 0.0f;
+    sD[tid] = ok ? expf(gl - F[3 * C * C + tid]) : 0.0f;
+  }
+  __syncthreads();
+
+  f32x4 aQ[NB][KQ], aK[NB][KQ], aP[NBL], aA[NBL];
+#pragma unroll
+  for (int I = 0; I < NB; ++I)
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) aQ[I][kq] = aK[I][kq] = zero4f();
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) aP[i] = aA[i] = zero4f();
+  float pdb[NB][4], poz[NB][4], pry[NB][4], puw[NB][4];
+#pragma unroll
+  for (int I = 0; I < NB; ++I)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pdb[I][e] = poz[I][e] = pry[I][e] = puw[I][e] = 0.0f;
+  float pdot = 0.0f;
+
+  WaveArea& A = area.wave[w];
+  for (int sl = w; sl < V / 16; sl += NW) {
+    const int v0 = 16 * sl;
+    // the slice's rows of S and dS' ([v][k]), and its dO columns ([t][v])
+#pragma unroll
+    for (int j = 0; j < 16 * KD / 4 / 64; ++j) {
+      const int p = lane + 64 * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
+      const f32x4 sx = ld4(ws_S + ck + (size_t)(v0 + r) * KD + 4 * c4);
+      const f32x4 dx = ld4(ws_dS + ck + (size_t)(v0 + r) * KD + 4 * c4);
+      pdot += (sx[0] * dx[0] + sx[1] * dx[1]) + (sx[2] * dx[2] + sx[3] * dx[3]);
+      st4(A.S + r * LK + 4 * c4, sx);
+      st4(A.dS + r * LK + 4 * c4, dx);
+    }
+#pragma unroll
+    for (int j = 0; j < (C * 4 + 63) / 64; ++j) {
+      const int p = lane + 64 * j, r = p >> 2, c4 = p & 3;
+      if (p < C * 4) {
+        const bool ok = r < n;
+        const f32x4 x = ld4(d_o + (row0 + (size_t)(ok ? r : 0) * H) * V + v0 + 4 * c4);
+        st4(A.dO + r * LV + 4 * c4, ok ? x : zero4f());
+      }
+    }
+    float vv[NB][4];
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * g + e;
+        const float x = v[(row0 + (size_t)(t < n ? t : 0) * H) * V + v0 + s];
+        vv[I][e] = t < n ? x : 0.0f;
+      }
+    wave_lds_sync();
+
+    // Y, Z, W
+    f32x4 Y[NB], Z[NB], Wt[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      Y[I] = Z[I] = Wt[I] = zero4f();
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        const f32x4 ak = ld4(sK + (16 * I + s) * LK + 16 * kq + 4 * g);
+        const f32x4 bs = ld4(A.S + s * LK + 16 * kq + 4 * g);
+        Y[I] = mma16(ak, bs, Y[I]);
+        Z[I] = mma16(ld4(sQ + (16 * I + s) * LK + 16 * kq + 4 * g), bs, Z[I]);
+        Wt[I] = mma16(ak, ld4(A.dS + s * LK + 16 * kq + 4 * g), Wt[I]);
+      }
+    }
+    // R, U = Tm R
+    f32x4 R[NB], U[NB], dU[NB], dR[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * g + e;
+        R[I][e] = sb[t] * vv[I][e] - sb[t] * sgam[t] * Y[I][e];
+      }
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      U[I] = zero4f();
+#pragma unroll
+      for (int J = 0; J <= I; ++J) U[I] = mma16(ld4(sT + (16 * I + s) * LCC + 16 * J + 4 * g), R[J], U[I]);
+    }
+    // dU = diag(D) W + P^T dO, dR = Tm^T dU
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dU[I][e] = sD[16 * I + 4 * g + e] * Wt[I][e];
+#pragma unroll
+      for (int J = I; J < NB; ++J) {
+        f32x4 a, bo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = sP[(16 * J + 4 * g + e) * LCC + 16 * I + s];
+          bo[e] = A.dO[(16 * J + 4 * g + e) * LV + s];
+        }
+        dU[I] = mma16(a, bo, dU[I]);
+      }
+    }
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      dR[I] = zero4f();
+#pragma unroll
+      for (int J = I; J < NB; ++J) {
+        f32x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = sT[(16 * J + 4 * g + e) * LCC + 16 * I + s];
+        dR[I] = mma16(a, dU[J], dR[I]);
+      }
+    }
+    // dV, the per-token partial sums, U and dR to LDS
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * g + e;
+        if (t < n) dv[(row0 + (size_t)t * H) * V + v0 + s] = sb[t] * dR[I][e];
+        pdb[I][e] += dR[I][e] * (vv[I][e] - sgam[t] * Y[I][e]);
+        poz[I][e] += A.dO[t * LV + s] * Z[I][e];
+        pry[I][e] += dR[I][e] * Y[I][e];
+        puw[I][e] += U[I][e] * Wt[I][e];
+        A.U[t * LV + s] = U[I][e];
+        A.dR[t * LV + s] = dR[I][e];
+      }
+    wave_lds_sync();
+    // dP += dO U^T, dA += dR U^T (negated at the end), lower blocks
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        const int blk = I * (I + 1) / 2 + J;
+        const f32x4 bu = ld4(A.U + (16 * J + s) * LV + 4 * g);
+        aP[blk] = mma16(ld4(A.dO + (16 * I + s) * LV + 4 * g), bu, aP[blk]);
+        aA[blk] = mma16(ld4(A.dR + (16 * I + s) * LV + 4 * g), bu, aA[blk]);
+      }
+    // dQ += diag(gam) dO S;  dK += diag(D) U dS' - diag(beta gam) dR S
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      const int r = 16 * I + s;
+      const f32x4 ao = ld4(A.dO + r * LV + 4 * g) * sgam[r];
+      const f32x4 au = ld4(A.U + r * LV + 4 * g) * sD[r];
+      const f32x4 ar = ld4(A.dR + r * LV + 4 * g) * (-sb[r] * sgam[r]);
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        f32x4 bs, bd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bs[e] = A.S[(4 * g + e) * LK + 16 * kq + s];
+          bd[e] = A.dS[(4 * g + e) * LK + 16 * kq + s];
+        }
+        aQ[I][kq] = mma16(ao, bs, aQ[I][kq]);
+        aK[I][kq] = mma16(ar, bs, mma16(au, bd, aK[I][kq]));
+      }
+    }
+  }
+
+  // per-token sums: over the 16 lanes of a group, then over the waves
+#pragma unroll
+  for (int I = 0; I < NB; ++I)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pdb[I][e] = group_sum(pdb[I][e]);
+      poz[I][e] = group_sum(poz[I][e]);
+      pry[I][e] = group_sum(pry[I][e]);
+      puw[I][e] = group_sum(puw[I][e]);
+    }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) pdot += __shfl_xor(pdot, m, 64);
+  __syncthreads();   // every wave is done with its slice tiles: the union turns into Red
+  Red& RD = area.red;
+  for (int ww = 0; ww < NW; ++ww) {
+    if (w == ww) {
+      const bool first = ww == 0;
+#pragma unroll
+      for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int o4 = (16 * I + 4 * g + e) * KD + 16 * kq + s;
+            RD.dQ[o4] = first ? aQ[I][kq][e] : RD.dQ[o4] + aQ[I][kq][e];
+            RD.dK[o4] = first ? aK[I][kq][e] : RD.dK[o4] + aK[I][kq][e];
+          }
+#pragma unroll
+      for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+          const int blk = I * (I + 1) / 2 + J;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int o2 = (16 * I + 4 * g + e) * LCC + 16 * J + s;
+            RD.dP[o2] = first ? aP[blk][e] : RD.dP[o2] + aP[blk][e];
+            RD.dA[o2] = first ? aA[blk][e] : RD.dA[o2] + aA[blk][e];
+          }
+        }
+      if (s == 0) {
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * I + 4 * g + e;
+            const float dg = sgam[t] * poz[I][e] - sb[t] * sgam[t] * pry[I][e];
+            sdb[t] = first ? pdb[I][e] : sdb[t] + pdb[I][e];
+            sdg[t] = first ? dg : sdg[t] + dg;
+            sdu[t] = first ? sD[t] * puw[I][e] : fmaf(sD[t], puw[I][e], sdu[t]);
+          }
+      }
+      if (lane == 0) sdot[ww] = pdot;
+    }
+    __syncthreads();
+  }
+  // masks and signs: dP lower (j <= r), dA = -(dR U^T) strictly lower; the pair
+  // sums of the gate gradients, then (dP o E) and (dA o beta E) in place
+  for (int i = tid; i < C * C; i += 256) {
+    const int r = i / C, j = i - r * C;
+    if (r >= NB * 16 || j > r || r >= n) {
+      if (r < C) {
+        RD.dP[r * LCC + j] = 0.0f;
+        RD.dA[r * LCC + j] = 0.0f;
+      }
+    } else {
+      if (j == r) RD.dA[r * LCC + j] = 0.0f;
+      else RD.dA[r * LCC + j] = -RD.dA[r * LCC + j];
+    }
+  }
+  __syncthreads();
+  if (tid < n) {
+    const int t = tid;
+    float sx = 0.0f, db = 0.0f;
+    for (int r = t; r < n; ++r) {
+      const float br = sb[r];
+      for (int i = 0; i < t; ++i) {
+        sx = fmaf(RD.dP[r * LCC + i], sP[r * LCC + i], sx);
+        sx = fmaf(RD.dA[r * LCC + i], br * sM[r * LCC + i], sx);
+      }
+    }
+    for (int i = 0; i < t; ++i) db = fmaf(RD.dA[t * LCC + i], sM[t * LCC + i], db);
+    sxr[t] = sx;
+    sdb[t] += db;
+  }
+  __syncthreads();
+  for (int i = tid; i < C * C; i += 256) {
+    const int r = i / C, j = i - r * C;
+    if (r < n && j <= r) {
+      const float e = expf(sg[r] - sg[j]);
+      RD.dP[r * LCC + j] *= e;
+      RD.dA[r * LCC + j] *= sb[r] * e;
+    }
+  }
+  __syncthreads();
+  // dQ += (dP o E) K;  dK += (dP o E)^T Q + (dA o bE) K + (dA o bE)^T K: wave w
+  // finishes key-channel tiles w, w + 4, ...
+  for (int kq = w; kq < KQ; kq += NW) {
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      f32x4 accq, acck;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        accq[e] = RD.dQ[(16 * I + 4 * g + e) * KD + 16 * kq + s];
+        acck[e] = RD.dK[(16 * I + 4 * g + e) * KD + 16 * kq + s];
+      }
+#pragma unroll
+      for (int J = 0; J < NB; ++J) {
+        f32x4 bk, bq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bk[e] = sK[(16 * J + 4 * g + e) * LK + 16 * kq + s];
+          bq[e] = sQ[(16 * J + 4 * g + e) * LK + 16 * kq + s];
+        }
+        if (J <= I) {
+          accq = mma16(ld4(RD.dP + (16 * I + s) * LCC + 16 * J + 4 * g), bk, accq);
+          acck = mma16(ld4(RD.dA + (16 * I + s) * LCC + 16 * J + 4 * g), bk, acck);
+        }
+        if (J >= I) {
+          f32x4 pt, at;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pt[e] = RD.dP[(16 * J + 4 * g + e) * LCC + 16 * I + s];
+            at[e] = RD.dA[(16 * J + 4 * g + e) * LCC + 16 * I + s];
+          }
+          acck = mma16(pt, bq, acck);
+          acck = mma16(at, bk, acck);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * g + e;
+        if (t < n) {
+          dq[(row0 + (size_t)t * H) * KD + 16 * kq + s] = accq[e];
+          dk[(row0 + (size_t)t * H) * KD + 16 * kq + s] = acck[e];
+        }
+      }
+    }
+  }
+  // gate gradients (the cancellation-free sums of bwd.hip), one thread
+  if (tid == 0) {
+    float dot = 0.0f;
+    for (int ww = 0; ww < NW; ++ww) dot += sdot[ww];
+    sdg[n - 1] += sgam[n - 1] * dot;
+    float pre = 0.0f;
+    for (int r = 0; r < n; ++r) {
+      const float du = sdu[r];
+      sdu[r] = pre;
+      pre += du;
+    }
+    float acc = 0.0f;
+    for (int r = n - 1; r >= 0; --r) {
+      acc += sdg[r];
+      const size_t go = row0 + (size_t)r * H;
+      dalpha[go] = (acc + sxr[r] + sdu[r]) / alpha[go];
+      dbeta[go] = sdb[r];
+    }
+  }
+}
+
 template <int KD, int C>
 hipError_t launch_kc(const BwdArgs& a, const float* rec, float* ws_dS, hipStream_t stream) {
   const long groups = ((long)a.B * a.H + 7) / 8;
@@ -246,7 +648,35 @@ hipError_t launch_k(const BwdArgs& a, int C, const float* rec, float* ws_dS, hip
   return launch_kc<KD, 32>(a, rec, ws_dS, stream);
 }
 
+template <int KD>
+hipError_t launch_local_k(const BwdArgs& a, int C, const float* ws_S, const float* ws_dS,
+                          const float* ws_F, hipStream_t stream) {
+  const int NT = (a.T + C - 1) / C;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(NT * a.H * a.B), dim3(256), 0, stream,
+                       static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                       static_cast<const float*>(a.v), static_cast<const float*>(a.d_o), a.alpha,
+                       ws_S, ws_dS, ws_F, static_cast<float*>(a.dq), static_cast<float*>(a.dk),
+                       static_cast<float*>(a.dv), a.dalpha, a.dbeta, a.T, a.H, a.V);
+    return hipGetLastError();
+  };
+  if (C == 16) return go(f32_local_kernel<KD, 16>);
+  return go(f32_local_kernel<KD, 32>);
+}
+
 }  // namespace
+
+hipError_t launch_bwd_f32_local(const BwdArgs& a, int chunk, const float* ws_S, const float* ws_dS,
+                                const float* ws_F, hipStream_t stream) {
+  if ((chunk != 16 && chunk != 32) || a.V % 16 != 0) return hipErrorInvalidValue;
+  switch (a.K) {
+    case 16: return launch_local_k<16>(a, chunk, ws_S, ws_dS, ws_F, stream);
+    case 32: return launch_local_k<32>(a, chunk, ws_S, ws_dS, ws_F, stream);
+    case 64: return launch_local_k<64>(a, chunk, ws_S, ws_dS, ws_F, stream);
+    case 128: return launch_local_k<128>(a, chunk, ws_S, ws_dS, ws_F, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_bwd_f32_dstate(const BwdArgs& a, int chunk, const float* rec, float* ws_dS,
                                  hipStream_t stream) {

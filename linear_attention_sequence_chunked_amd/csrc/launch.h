@@ -71,6 +71,10 @@ hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 // every chunk's end-state gradient to ws_dS [B, H, NT, V, K] and d_s0.
 hipError_t launch_bwd_f32_dstate(const BwdArgs& a, int chunk, const float* rec, float* ws_dS,
                                  hipStream_t stream);
+// Float32 token gradients on the matrix cores, from the chunk-start states, the
+// end-state gradients and the float32 prep's factors (M, P, Tm, gates).
+hipError_t launch_bwd_f32_local(const BwdArgs& a, int chunk, const float* ws_S, const float* ws_dS,
+                                const float* ws_F, hipStream_t stream);
 
 // Bfloat16 backward on MFMA with 64-token chunks, whatever chunk the caller gave
 // (K and V 32, 64 or 128).  Workspace: chunk-start states, chunk-end state
