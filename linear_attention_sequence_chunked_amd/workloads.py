@@ -57,6 +57,10 @@ WORKLOADS = {
     "fwdbwd_bf16": Workload("fwdbwd_bf16", 4, 2048, 6, 128, 128, 64, torch.bfloat16, "decay",
                             with_do=True, seed=4,
                             note="forward+backward shape, B4 T2048 H6 K=V=128, chunk 64"),
+    "fwdbwd_f32": Workload("fwdbwd_f32", 4, 2048, 6, 128, 128, 64, torch.float32, "decay",
+                           with_do=True, seed=4,
+                           note="forward+backward shape with float32 q, k, v, d_o, B4 T2048 H6 "
+                                "K=V=128, chunk 64"),
     "long_few_bf16": Workload("long_few_bf16", 1, 32768, 2, 128, 128, 64, torch.bfloat16, "decay",
                               s0_std=0.02, seed=9,
                               note="long context with few streams, B1 T32768 H2 K=V=128, chunk 64 "

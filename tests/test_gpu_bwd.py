@@ -142,6 +142,13 @@ def test_fwdbwd_workload_parity():
     check(workload_inputs(w), w.chunk, TOL[w.dtype], w.name)
 
 
+def test_fwdbwd_f32_workload_parity():
+    # the same shape with float32 q, k, v, d_o: 32-token chunks with the state
+    # recompute, reverse walk and token gradients on the fp32 matrix cores
+    w = WORKLOADS["fwdbwd_f32"]
+    check(workload_inputs(w), w.chunk, TOL[w.dtype], w.name)
+
+
 def test_bwd_mfma_on_a_side_stream_matches_default_stream():
     # the MFMA backward forks to a library stream and joins back; on a caller
     # stream other than the default the result must be the same bits
