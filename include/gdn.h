@@ -284,9 +284,11 @@ GDN_API gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v
  * gdn_chunk_bwd_workspace_size -- bytes of device workspace gdn_chunk_bwd needs
  * for these sizes and this dtype (the layout of the path the call takes).
  *  - bfloat16 with K and V in {32, 64, 128}: the MFMA path with 64-token chunks,
- *    whatever `chunk` is; per (batch, head, chunk) two float32 [V, K] states and
- *    a 16896-byte record (two bf16 64 x 64 matrices, two float32 64-vectors):
- *        B * H * ceil(T / 64) * (2 * V * K * 4 + 16896) bytes.
+ *    whatever `chunk` is; per (batch, head, chunk) two [V, K] states rounded to
+ *    bfloat16 (the chunk-start state and the state gradient, kept in the precision
+ *    the path's matrix products read them in) and a 16896-byte record (two bf16
+ *    64 x 64 matrices, two float32 64-vectors):
+ *        B * H * ceil(T / 64) * (2 * V * K * 2 + 16896) bytes.
  *  - otherwise (float32, or bfloat16 with K or V = 16): the float32 path, per
  *    (batch, head, backward chunk of C = min(chunk, 32) tokens) two float32
  *    [V, K] states and the chunk's float32 factors (three C x C matrices and

@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(256)
 bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ d_o, const float* __restrict__ d_sfinal,
                     float* __restrict__ d_s0, const unsigned char* __restrict__ rec,
-                    float* __restrict__ ws_dS, int T, int H, int V) {
+                    bf16* __restrict__ ws_dS, int T, int H, int V) {
   using SL = WalkSlot<KD>;
   constexpr int LDK = SL::LDK;
   constexpr int KS = KD / 32, NCB = KD / 16;
@@ -293,9 +293,11 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int c = NT - 1; c >= 0; --c) {
       lds_barrier();
       const SL& sl = slot[c & 1];
-      float* dst = ws_dS + (((size_t)b * H + h) * NT + c) * (size_t)V * KD + (size_t)(v0 + vw + ls) * KD + 4 * lg;
+      // dS' of every chunk, rounded to bf16 (the token-gradient kernel's operand
+      // precision)
+      bf16* dst = ws_dS + (((size_t)b * H + h) * NT + c) * (size_t)V * KD + (size_t)(v0 + vw + ls) * KD + 4 * lg;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<f32x4*>(dst + 16 * cb) = dS[cb];
+      for (int cb = 0; cb < NCB; ++cb) store_bf4(dst + 16 * cb, dS[cb]);
       bf16x8 sbf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) sbf[ks] = acc_pair_to_frag(dS[2 * ks], dS[2 * ks + 1]);
@@ -496,8 +498,8 @@ template <int KD, int VD>
 __global__ void __launch_bounds__(512)
 bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    const bf16* __restrict__ v, const bf16* __restrict__ d_o,
-                   const float* __restrict__ alpha, const float* __restrict__ ws_S,
-                   const float* __restrict__ ws_dS, const unsigned char* __restrict__ rec,
+                   const float* __restrict__ alpha, const bf16* __restrict__ ws_S,
+                   const bf16* __restrict__ ws_dS, const unsigned char* __restrict__ rec,
                    bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
                    float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H) {
   using SM = LocalSmem<KD, VD>;
@@ -521,12 +523,12 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const size_t ck = (((size_t)b * H + h) * NT + c) * (size_t)VD * KD;
 
   // ---- slice operands travel through registers, so the next slice is
-  // requested while the current one is computed: S and dS' pieces (fp32), dO
+  // requested while the current one is computed: S and dS' pieces (bf16), dO
   // pieces, and the V values of this wave's tiles
   constexpr int SP = VSL * KD / 8, SPL = (SP + 511) / 512;
   constexpr int OP = kC * VSL / 8, OPL = (OP + 511) / 512;
   struct SliceRegs {
-    f32x4 s[SPL][2], d[SPL][2];
+    bf16x8 s[SPL], d[SPL];
     bf16x8 o[OPL];
     bf16x4 v[NST];
   };
@@ -535,12 +537,8 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int j = 0; j < SPL; ++j) {
       const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
       if (p < SP) {
-        const float* sp = ws_S + ck + (size_t)(vs0 + r) * KD + c8;
-        const float* dp = ws_dS + ck + (size_t)(vs0 + r) * KD + c8;
-        R.s[j][0] = *reinterpret_cast<const f32x4*>(sp);
-        R.s[j][1] = *reinterpret_cast<const f32x4*>(sp + 4);
-        R.d[j][0] = *reinterpret_cast<const f32x4*>(dp);
-        R.d[j][1] = *reinterpret_cast<const f32x4*>(dp + 4);
+        R.s[j] = *reinterpret_cast<const bf16x8*>(ws_S + ck + (size_t)(vs0 + r) * KD + c8);
+        R.d[j] = *reinterpret_cast<const bf16x8*>(ws_dS + ck + (size_t)(vs0 + r) * KD + c8);
       }
     }
 #pragma unroll
@@ -565,14 +563,10 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int j = 0; j < SPL; ++j) {
       const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
       if (p < SP) {
-        const float sv[8] = {R.s[j][0][0], R.s[j][0][1], R.s[j][0][2], R.s[j][0][3],
-                             R.s[j][1][0], R.s[j][1][1], R.s[j][1][2], R.s[j][1][3]};
-        const float dvv[8] = {R.d[j][0][0], R.d[j][0][1], R.d[j][0][2], R.d[j][0][3],
-                              R.d[j][1][0], R.d[j][1][1], R.d[j][1][2], R.d[j][1][3]};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(dvv[e], sv[e], dot);
-        *reinterpret_cast<bf16x8*>(&sm.u.sl.s[r * LDK + c8]) = to_bf8(sv);
-        *reinterpret_cast<bf16x8*>(&sm.u.sl.ds[r * LDK + c8]) = to_bf8(dvv);
+        for (int e = 0; e < 8; ++e) dot = fmaf(bf2f(R.d[j][e]), bf2f(R.s[j][e]), dot);
+        *reinterpret_cast<bf16x8*>(&sm.u.sl.s[r * LDK + c8]) = R.s[j];
+        *reinterpret_cast<bf16x8*>(&sm.u.sl.ds[r * LDK + c8]) = R.d[j];
       }
     }
 #pragma unroll
@@ -937,7 +931,7 @@ bool bwd_bf16_supported(int K, int V) {
 
 size_t bwd_bf16_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
   const int64_t NT = (T + kC - 1) / kC;
-  return (size_t)(2 * B * H * NT * V * K * 4 + B * H * NT * (int64_t)kRecBytes);
+  return (size_t)(2 * B * H * NT * V * K * 2 + B * H * NT * (int64_t)kRecBytes);
 }
 
 namespace {
@@ -996,8 +990,9 @@ SideStream* side_stream(int dev) {
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   if (!bwd_bf16_supported(a.K, a.V)) return hipErrorInvalidValue;
   const int NT = (a.T + kC - 1) / kC;
-  float* ws_S = a.workspace;
-  float* ws_dS = ws_S + (size_t)a.B * a.H * NT * a.V * a.K;
+  // workspace: chunk-start states and state gradients (bf16), then the records
+  bf16* ws_S = reinterpret_cast<bf16*>(a.workspace);
+  bf16* ws_dS = ws_S + (size_t)a.B * a.H * NT * a.V * a.K;
   unsigned char* rec = reinterpret_cast<unsigned char*>(ws_dS + (size_t)a.B * a.H * NT * a.V * a.K);
   // (1) chunk-start states (launched after prep, below)
   FwdArgs f;
@@ -1016,6 +1011,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   f.V = a.V;
   f.chunk = kC;
   f.vs = 32;
+  f.s_ckpt_bf16 = ws_S;
   const int dev = stream_device(stream);
   std::unique_lock<std::mutex> lock;
   if (dev >= 0) lock = std::unique_lock<std::mutex>(g_side[dev].mu);
@@ -1038,7 +1034,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
       if ((r = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return r;
       st_states = sd->s;
     }
-    if ((r = launch_fwd_states(f, true, ws_S, st_states)) != hipSuccess) return r;
+    if ((r = launch_fwd_bf16(f, st_states)) != hipSuccess) return r;
     if (sd && (r = hipEventRecord(sd->join, sd->s)) != hipSuccess) return r;
     hipLaunchKernelGGL((bwd16_dstate_kernel<KD>), dim3(a.B * a.H * (a.V / 32)), dim3(256), 0, stream, q, k,
                        d_o, a.d_sfinal, a.d_s0, rec, ws_dS, a.T, a.H, a.V);

@@ -274,8 +274,8 @@ __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_e
 fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const float* __restrict__ alpha, const float* __restrict__ beta,
                 const float* __restrict__ s0, bf16* __restrict__ o, float* __restrict__ s_final,
-                float* __restrict__ s_ckpt, const int* __restrict__ cu, int T, int H, int K, int V,
-                int C, int nslice) {
+                float* __restrict__ s_ckpt, bf16* __restrict__ s_ckpt_h, const int* __restrict__ cu,
+                int T, int H, int K, int V, int C, int nslice) {
   using SM = Smem<KD, VS, CP>;
   constexpr int LDC = SM::LDC;
   constexpr int NTB = CP / 16;          // token blocks per chunk tile
@@ -499,6 +499,16 @@ fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           if (chan(cb) < K) *reinterpret_cast<f32x4*>(dst + chan(cb)) = S[cb];
+      }
+      if constexpr (!WO) {
+        if (s_ckpt_h) {  // the same, rounded to bf16 (the MFMA backward's operand precision)
+          bf16* dst = s_ckpt_h + ((((size_t)b * H + h) * NT + x) * V + v0 + 16 * vb + ls) * (size_t)K;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            if (chan(cb) < K)
+              *reinterpret_cast<bf16x4*>(dst + chan(cb)) =
+                  bf16x4{(bf16)S[cb][0], (bf16)S[cb][1], (bf16)S[cb][2], (bf16)S[cb][3]};
+        }
       }
       const int gs = x % 3;
       constexpr int LDK = SM::LDK;
@@ -756,13 +766,14 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP, true>), dim3(nblk), dim3(kThreads), 0, stream,
                        static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                        static_cast<const bf16*>(a.v), a.alpha, a.beta, a.s0,
-                       static_cast<bf16*>(a.o), a.s_final, a.s_ckpt, a.cu_seqlens, a.T, a.H, a.K, a.V,
-                       a.chunk, nslice);
+                       static_cast<bf16*>(a.o), a.s_final, a.s_ckpt, nullptr, a.cu_seqlens, a.T, a.H, a.K,
+                       a.V, a.chunk, nslice);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<KD, VS, CP, false>), dim3(nblk), dim3(kThreads), 0, stream,
                        static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                        static_cast<const bf16*>(a.v), a.alpha, a.beta, a.s0, nullptr, a.s_final,
-                       a.s_ckpt, a.cu_seqlens, a.T, a.H, a.K, a.V, a.chunk, nslice);
+                       a.s_ckpt, static_cast<bf16*>(a.s_ckpt_bf16), a.cu_seqlens, a.T, a.H, a.K, a.V,
+                       a.chunk, nslice);
   return hipGetLastError();
 }
 

@@ -19,6 +19,9 @@ struct FwdArgs {
   float* s_final;   // may be null (skip)
   int B, T, H, K, V, chunk;
   float* s_ckpt = nullptr;  // optional chunk-start states [B, H, NT, V, K]
+  // bf16 kernel, states only (o null): optional chunk-start states rounded to
+  // bf16, [B, H, NT, V, K]
+  void* s_ckpt_bf16 = nullptr;
   // optional packed batch: B sequences, sequence b = tokens [cu[b], cu[b+1]) of
   // the [1, T, H, *] tensors; states are [B, H, V, K]
   const int* cu_seqlens = nullptr;
