@@ -501,7 +501,7 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    const float* __restrict__ alpha, const bf16* __restrict__ ws_S,
                    const bf16* __restrict__ ws_dS, const unsigned char* __restrict__ rec,
                    bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
-                   float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H) {
+                   float* __restrict__ dalpha, float* __restrict__ dbeta, int B, int T, int H) {
   using SM = LocalSmem<KD, VD>;
   constexpr int LDK = SM::LDK, LDW = SM::LDW, VSL = SM::VSL;
   constexpr int KS = KD / 32, VKS = VSL / 32;
@@ -511,16 +511,34 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int NQT = NCB * 4 / 8;         // dQ / dK tiles per wave
   static_assert(NST >= 1 && NQT >= 1, "shape too small for 8 waves");
   __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63;
+  // the lane indices are re-made opaque at every item (below), so that the
+  // compiler keeps each item's per-lane addresses next to their use instead of
+  // hoisting them all out of the item loop (which exceeds the register file)
+  int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ls = lane & 15, lg = lane >> 4;
+  int ls = lane & 15, lg = lane >> 4;
   const int NT = (T + kC - 1) / kC;
-  // one-dimensional grid over (chunk, head, batch), chunk fastest
-  const int c = blockIdx.x % NT, h = (blockIdx.x / NT) % H, b = blockIdx.x / NT / H;
-  const int t0 = c * kC, n = min(kC, T - t0);
   const size_t tokk = (size_t)H * KD, tokv = (size_t)H * VD;
-  const unsigned char* rc = rec + (((size_t)b * H + h) * NT + c) * kRecBytes;
-  const size_t ck = (((size_t)b * H + h) * NT + c) * (size_t)VD * KD;
+  // Items are (chunk, head, batch), chunk fastest; the grid holds at most one
+  // workgroup per CU and each workgroup takes items blockIdx.x, + gridDim.x, ...
+  // so that the next item's operands are requested while this one is computed.
+  const int items = NT * H * B;
+  struct Item {
+    int c, h, b, t0, n;
+    size_t ck;                  // element offset of the item's [V, K] states
+    const unsigned char* rc;    // the item's record
+  };
+  auto item_of = [&](int it) {
+    Item I;
+    I.c = it % NT;
+    I.h = (it / NT) % H;
+    I.b = it / NT / H;
+    I.t0 = I.c * kC;
+    I.n = min(kC, T - I.t0);
+    I.ck = (((size_t)I.b * H + I.h) * NT + I.c) * (size_t)VD * KD;
+    I.rc = rec + (((size_t)I.b * H + I.h) * NT + I.c) * kRecBytes;
+    return I;
+  };
 
   // ---- slice operands travel through registers, so the next slice is
   // requested while the current one is computed: S and dS' pieces (bf16), dO
@@ -532,32 +550,32 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     bf16x8 o[OPL];
     bf16x4 v[NST];
   };
-  auto load_slice = [&](int vs0, SliceRegs& R) {
+  auto load_slice = [&](const Item& I, int vs0, SliceRegs& R) {
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
       const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
       if (p < SP) {
-        R.s[j] = *reinterpret_cast<const bf16x8*>(ws_S + ck + (size_t)(vs0 + r) * KD + c8);
-        R.d[j] = *reinterpret_cast<const bf16x8*>(ws_dS + ck + (size_t)(vs0 + r) * KD + c8);
+        R.s[j] = *reinterpret_cast<const bf16x8*>(ws_S + I.ck + (size_t)(vs0 + r) * KD + c8);
+        R.d[j] = *reinterpret_cast<const bf16x8*>(ws_dS + I.ck + (size_t)(vs0 + r) * KD + c8);
       }
     }
 #pragma unroll
     for (int j = 0; j < OPL; ++j) {
       const int p = tid + 512 * j, r = p / (VSL / 8), c8 = (p % (VSL / 8)) * 8;
       R.o[j] = zero8();
-      if (p < OP && r < n)
-        R.o[j] = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)b * T + t0 + r) * tokv + (size_t)h * VD + vs0 + c8);
+      if (p < OP && r < I.n)
+        R.o[j] = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)I.b * T + I.t0 + r) * tokv + (size_t)I.h * VD + vs0 + c8);
     }
 #pragma unroll
     for (int u = 0; u < NST; ++u) {
       const int t = wave + 8 * u, vb = t % NVB, tk = 16 * (t / NVB) + ls;
       const bf16 z = (bf16)0.0f;
       R.v[u] = bf16x4{z, z, z, z};
-      if (tk < n)
-        R.v[u] = *reinterpret_cast<const bf16x4*>(v + ((size_t)b * T + t0 + tk) * tokv + (size_t)h * VD + vs0 + 16 * vb + 4 * lg);
+      if (tk < I.n)
+        R.v[u] = *reinterpret_cast<const bf16x4*>(v + ((size_t)I.b * T + I.t0 + tk) * tokv + (size_t)I.h * VD + vs0 + 16 * vb + 4 * lg);
     }
   };
-  float dot = 0.0f;   // <dS', S> partial
+  float dot = 0.0f;   // <dS', S> partial of the current item
   auto stage_slice = [&](const SliceRegs& R) {
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
@@ -575,341 +593,371 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       if (p < OP) *reinterpret_cast<bf16x8*>(&sm.u.sl.dob[r * LDW + c8]) = R.o[j];
     }
   };
-  SliceRegs R;
-  load_slice(0, R);
-
-  // ---- chunk operands: keys, queries, Tm, P, gates (all requested before any
-  // LDS write)
-  {
-    constexpr int KP = kC * KD / 8, KPL = (KP + 511) / 512;
-    bf16x8 kv[KPL], qv[KPL];
+  // ---- chunk operands: keys, queries, Tm, P, gates, through registers so that
+  // the next item's are requested while this one is computed
+  constexpr int KP = kC * KD / 8, KPL = (KP + 511) / 512;
+  static_assert(kC * kC / 8 == 512, "one C x C piece per thread");
+  struct ChunkRegs {
+    bf16x8 kv[KPL], qv[KPL], tv, pv;
+    float gv, bv;
+  };
+  auto load_chunk = [&](const Item& I, ChunkRegs& C) {
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
-      kv[j] = qv[j] = zero8();
-      if (p < KP && r < n) {
-        const size_t off = ((size_t)b * T + t0 + r) * tokk + (size_t)h * KD + c8;
-        kv[j] = *reinterpret_cast<const bf16x8*>(k + off);
-        qv[j] = *reinterpret_cast<const bf16x8*>(q + off);
+      C.kv[j] = C.qv[j] = zero8();
+      if (p < KP && r < I.n) {
+        const size_t off = ((size_t)I.b * T + I.t0 + r) * tokk + (size_t)I.h * KD + c8;
+        C.kv[j] = *reinterpret_cast<const bf16x8*>(k + off);
+        C.qv[j] = *reinterpret_cast<const bf16x8*>(q + off);
       }
     }
-    static_assert(kC * kC / 8 == 512, "one C x C piece per thread");
-    const bf16x8 tv = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * tid);
-    const bf16x8 pv = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * tid);
-    float gv = 0.0f, bv = 0.0f;
-    if (tid < kC) {
-      gv = reinterpret_cast<const float*>(rc + kRecG)[tid];
-      bv = reinterpret_cast<const float*>(rc + kRecB)[tid];
-    }
+    C.tv = *reinterpret_cast<const bf16x8*>(I.rc + kRecTm + 16 * tid);
+    C.pv = *reinterpret_cast<const bf16x8*>(I.rc + kRecP + 16 * tid);
+    // every thread reads a gate (threads past the chunk a valid duplicate), so
+    // no load sits under a branch
+    C.gv = reinterpret_cast<const float*>(I.rc + kRecG)[tid & (kC - 1)];
+    C.bv = reinterpret_cast<const float*>(I.rc + kRecB)[tid & (kC - 1)];
+  };
+  auto stage_chunk = [&](const ChunkRegs& C) {
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       const int p = tid + 512 * j, r = p / (KD / 8), c8 = (p % (KD / 8)) * 8;
       if (p < KP) {
-        *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = kv[j];
-        *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = qv[j];
+        *reinterpret_cast<bf16x8*>(&sm.k[r * LDK + c8]) = C.kv[j];
+        *reinterpret_cast<bf16x8*>(&sm.q[r * LDK + c8]) = C.qv[j];
       }
     }
     const int r = tid / (kC / 8), c8 = (tid % (kC / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(&sm.tm[r * kLDC + c8]) = tv;
-    *reinterpret_cast<bf16x8*>(&sm.p[r * kLDC + c8]) = pv;
+    *reinterpret_cast<bf16x8*>(&sm.tm[r * kLDC + c8]) = C.tv;
+    *reinterpret_cast<bf16x8*>(&sm.p[r * kLDC + c8]) = C.pv;
     if (tid < kC) {
-      sm.g[tid] = gv;
-      sm.bt[tid] = bv;
+      sm.g[tid] = C.gv;
+      sm.bt[tid] = C.bv;
     }
-  }
+  };
 
-  // per-wave accumulators
-  // slice tiles: t = wave + 8 u -> value block t % NVB, token block t / NVB
-  float rs_oz[NST], rs_uw[NST], rs_db[NST], rs_ry[NST];   // per-lane row-sum partials
-#pragma unroll
-  for (int u = 0; u < NST; ++u) rs_oz[u] = rs_uw[u] = rs_db[u] = rs_ry[u] = 0.0f;
-  // dP^T / dA^T tiles: job j = wave + 8 u < 20 (10 upper (i, r) block pairs each)
-  f32x4 pa[3];
-#pragma unroll
-  for (int u = 0; u < 3; ++u) pa[u] = zero4();
-  // dQ^T / dK^T tiles: t = wave + 8 u -> channel block t % NCB, token block t / NCB
-  f32x4 aq[NQT], ak1[NQT], ak2[NQT];
-#pragma unroll
-  for (int u = 0; u < NQT; ++u) aq[u] = ak1[u] = ak2[u] = zero4();
+  int it = blockIdx.x;
+  Item I = item_of(it);
+  ChunkRegs CR;
+  SliceRegs R;
+  load_chunk(I, CR);
+  load_slice(I, 0, R);
+  for (;;) {
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(ls), "+v"(lg));
+    const int h = I.h, b = I.b, t0 = I.t0, n = I.n;
+    // the next item (this one again after the last: its loads are then unused but
+    // keep every load unconditional, so the wait counts stay exact)
+    const int nx = it + (int)gridDim.x;
+    const bool more = nx < items;
+    const Item J = item_of(more ? nx : it);
+    stage_chunk(CR);
+    dot = 0.0f;
 
-  for (int vs0 = 0; vs0 < VD; vs0 += VSL) {
-    __syncthreads();
-    stage_slice(R);
-    bf16x4 vcur[NST];
+    // per-wave accumulators
+    // slice tiles: t = wave + 8 u -> value block t % NVB, token block t / NVB
+    float rs_oz[NST], rs_uw[NST], rs_db[NST], rs_ry[NST];   // per-lane row-sum partials
 #pragma unroll
-    for (int u = 0; u < NST; ++u) vcur[u] = R.v[u];
-    if (vs0 + VSL < VD) load_slice(vs0 + VSL, R);
-    __syncthreads();
+    for (int u = 0; u < NST; ++u) rs_oz[u] = rs_uw[u] = rs_db[u] = rs_ry[u] = 0.0f;
+    // dP^T / dA^T tiles: job j = wave + 8 u < 20 (10 upper (i, r) block pairs each)
+    f32x4 pa[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) pa[u] = zero4();
+    // dQ^T / dK^T tiles: t = wave + 8 u -> channel block t % NCB, token block t / NCB
+    f32x4 aq[NQT], ak1[NQT], ak2[NQT];
+#pragma unroll
+    for (int u = 0; u < NQT; ++u) aq[u] = ak1[u] = ak2[u] = zero4();
 
-    // ---- (a) Y^T = S K^T, Z^T = S Q^T, W^T = dS' K^T; R^T = beta V^T - beta gam Y^T
-    f32x4 YT[NST], WT[NST], VT[NST];
+    for (int vs0 = 0; vs0 < VD; vs0 += VSL) {
+      __syncthreads();
+      stage_slice(R);
+      bf16x4 vcur[NST];
+#pragma unroll
+      for (int u = 0; u < NST; ++u) vcur[u] = R.v[u];
+      {
+        const bool last = vs0 + VSL >= VD;
+        load_slice(last ? J : I, last ? 0 : vs0 + VSL, R);
+      }
+      __syncthreads();
+
+      // ---- (a) Y^T = S K^T, Z^T = S Q^T, W^T = dS' K^T; R^T = beta V^T - beta gam Y^T
+      f32x4 YT[NST], WT[NST], VT[NST];
+#pragma unroll
+      for (int u = 0; u < NST; ++u) {
+        const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
+        f32x4 y = zero4(), z = zero4(), w = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 sa = frag_rows(sm.u.sl.s, LDK, 16 * vb, 32 * ks, lane);
+          const bf16x8 da = frag_rows(sm.u.sl.ds, LDK, 16 * vb, 32 * ks, lane);
+          const bf16x8 kb = frag_rows(sm.k, LDK, 16 * tb, 32 * ks, lane);
+          y = mma(sa, kb, y);
+          z = mma(sa, frag_rows(sm.q, LDK, 16 * tb, 32 * ks, lane), z);
+          w = mma(da, kb, w);
+        }
+        // lane: values vs0 + 16 vb + 4 lg + e, token tk = 16 tb + ls
+        const int tk = 16 * tb + ls;
+        const float gm = __builtin_amdgcn_exp2f(sm.g[tk]), bt = sm.bt[tk];
+        const f32x4 vv = f32x4{bf2f(vcur[u][0]), bf2f(vcur[u][1]), bf2f(vcur[u][2]), bf2f(vcur[u][3])};
+        const bf16x4 ov = *reinterpret_cast<const bf16x4*>(&sm.u.sl.dob[tk * LDW + 16 * vb + 4 * lg]);
+        f32x4 r;
+        float oz = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r[e] = bt * vv[e] - bt * gm * y[e];
+          oz = fmaf(bf2f(ov[e]), z[e], oz);
+        }
+        rs_oz[u] += oz;
+        store_tile_t(sm.u.sl.rb, LDW, 16 * tb, 16 * vb, r, lane);
+        YT[u] = y;
+        WT[u] = w;
+        VT[u] = vv;
+      }
+      __syncthreads();
+      // ---- (b) U^T = R^T Tm^T,  dU^T = diag(D) W^T + dO^T P
+#pragma unroll
+      for (int u = 0; u < NST; ++u) {
+        const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
+        f32x4 uu = zero4(), du = zero4();
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+          if (32 * cs <= 16 * tb + 15)  // Tm lower
+            uu = mma(frag_cols(sm.u.sl.rb, LDW, 16 * vb, 32 * cs, lane), frag_rows(sm.tm, kLDC, 16 * tb, 32 * cs, lane), uu);
+          if (32 * cs + 31 >= 16 * tb)  // P lower: rows r >= i
+            du = mma(frag_cols(sm.u.sl.dob, LDW, 16 * vb, 32 * cs, lane), frag_cols(sm.p, kLDC, 16 * tb, 32 * cs, lane), du);
+        }
+        const int tk = 16 * tb + ls;
+        const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[tk]);
+        float uw = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          du[e] = fmaf(dd, WT[u][e], du[e]);
+          uw = fmaf(uu[e], WT[u][e], uw);
+        }
+        rs_uw[u] += uw;
+        store_tile_t(sm.u.sl.ub, LDW, 16 * tb, 16 * vb, uu, lane);
+        store_tile_t(sm.u.sl.dub, LDW, 16 * tb, 16 * vb, du, lane);
+      }
+      __syncthreads();
+      // ---- (c) dR^T = dU^T Tm;  dV = diag(beta) dR
+#pragma unroll
+      for (int u = 0; u < NST; ++u) {
+        const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
+        f32x4 dr = zero4();
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs)
+          if (32 * cs + 31 >= 16 * tb)  // Tm[i][r] with i >= r
+            dr = mma(frag_cols(sm.u.sl.dub, LDW, 16 * vb, 32 * cs, lane), frag_cols(sm.tm, kLDC, 16 * tb, 32 * cs, lane), dr);
+        const int tk = 16 * tb + ls;
+        const float gm = __builtin_amdgcn_exp2f(sm.g[tk]), bt = sm.bt[tk];
+        float db = 0.0f, ry = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          db = fmaf(dr[e], VT[u][e] - gm * YT[u][e], db);
+          ry = fmaf(dr[e], YT[u][e], ry);
+        }
+        rs_db[u] += db;
+        rs_ry[u] += ry;
+        if (tk < n) store_bf4(dv + ((size_t)b * T + t0 + tk) * tokv + (size_t)h * VD + vs0 + 16 * vb + 4 * lg, dr * bt);
+        store_tile_t(sm.u.sl.drb, LDW, 16 * tb, 16 * vb, dr, lane);
+      }
+      __syncthreads();
+      // ---- (d) dP^T += U dO^T,  dA^T -= U dR^T   (upper (i, r) blocks, i <= r)
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int j = wave + 8 * u;
+        if (j < 20) {
+          const int jt = j % 10;
+          const int rbk = jt < 1 ? 0 : (jt < 3 ? 1 : (jt < 6 ? 2 : 3));   // r block
+          const int ibk = jt - rbk * (rbk + 1) / 2;                        // i block <= r block
+          const bf16* bsrc = j < 10 ? sm.u.sl.dob : sm.u.sl.drb;
+#pragma unroll
+          for (int ks = 0; ks < VKS; ++ks)
+            pa[u] = mma(frag_rows(sm.u.sl.ub, LDW, 16 * ibk, 32 * ks, lane), frag_rows(bsrc, LDW, 16 * rbk, 32 * ks, lane), pa[u]);
+        }
+      }
+      // ---- (e) dQ^T += S^T dO^T,  dK^T += dS'^T U^T (part 1), S^T dR^T (part 2)
+#pragma unroll
+      for (int u = 0; u < NQT; ++u) {
+        const int t = wave + 8 * u, cb = t % NCB, tb = t / NCB;
+#pragma unroll
+        for (int ks = 0; ks < VKS; ++ks) {
+          const bf16x8 st = frag_cols(sm.u.sl.s, LDK, 16 * cb, 32 * ks, lane);
+          aq[u] = mma(st, frag_rows(sm.u.sl.dob, LDW, 16 * tb, 32 * ks, lane), aq[u]);
+          ak1[u] = mma(frag_cols(sm.u.sl.ds, LDK, 16 * cb, 32 * ks, lane), frag_rows(sm.u.sl.ub, LDW, 16 * tb, 32 * ks, lane), ak1[u]);
+          ak2[u] = mma(st, frag_rows(sm.u.sl.drb, LDW, 16 * tb, 32 * ks, lane), ak2[u]);
+        }
+      }
+    }
+    // the next item's chunk operands, requested now so that they arrive during
+    // this item's final products (requested at the item's start instead, they
+    // hold 26 more registers through the slice loop and gained nothing)
+    load_chunk(J, CR);
+    // per-token row sums of the slice tiles: reduce over the four lane groups
 #pragma unroll
     for (int u = 0; u < NST; ++u) {
-      const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
-      f32x4 y = zero4(), z = zero4(), w = zero4();
+      float x[4] = {rs_oz[u], rs_uw[u], rs_db[u], rs_ry[u]};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 sa = frag_rows(sm.u.sl.s, LDK, 16 * vb, 32 * ks, lane);
-        const bf16x8 da = frag_rows(sm.u.sl.ds, LDK, 16 * vb, 32 * ks, lane);
-        const bf16x8 kb = frag_rows(sm.k, LDK, 16 * tb, 32 * ks, lane);
-        y = mma(sa, kb, y);
-        z = mma(sa, frag_rows(sm.q, LDK, 16 * tb, 32 * ks, lane), z);
-        w = mma(da, kb, w);
+      for (int qn = 0; qn < 4; ++qn) {
+        x[qn] += __shfl_xor(x[qn], 16);
+        x[qn] += __shfl_xor(x[qn], 32);
       }
-      // lane: values vs0 + 16 vb + 4 lg + e, token tk = 16 tb + ls
-      const int tk = 16 * tb + ls;
-      const float gm = __builtin_amdgcn_exp2f(sm.g[tk]), bt = sm.bt[tk];
-      const f32x4 vv = f32x4{bf2f(vcur[u][0]), bf2f(vcur[u][1]), bf2f(vcur[u][2]), bf2f(vcur[u][3])};
-      const bf16x4 ov = *reinterpret_cast<const bf16x4*>(&sm.u.sl.dob[tk * LDW + 16 * vb + 4 * lg]);
-      f32x4 r;
-      float oz = 0.0f;
+      const int t = wave + 8 * u;
+      if (lg == 0)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r[e] = bt * vv[e] - bt * gm * y[e];
-        oz = fmaf(bf2f(ov[e]), z[e], oz);
-      }
-      rs_oz[u] += oz;
-      store_tile_t(sm.u.sl.rb, LDW, 16 * tb, 16 * vb, r, lane);
-      YT[u] = y;
-      WT[u] = w;
-      VT[u] = vv;
+        for (int qn = 0; qn < 4; ++qn) sm.red[qn][t][ls] = x[qn];
+    }
+    // <dS', S>: wave partial
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+    if (lane == 0) sm.dot[wave] = dot;
+    __syncthreads();   // every slice array is dead from here
+
+    // ---- (f) dP o E, dA o beta E to LDS (bf16, [r][i]); dP o P and dA o M (fp32,
+    // with P and M recomputed in fp32 from the key and query tiles)
+    for (int p = tid; p < kC * kC / 8; p += 512) {   // zero the tiles no job writes
+      const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
+      *reinterpret_cast<bf16x8*>(&sm.u.fin.dpe[r * kLDC + c8]) = zero8();
+      *reinterpret_cast<bf16x8*>(&sm.u.fin.dae[r * kLDC + c8]) = zero8();
     }
     __syncthreads();
-    // ---- (b) U^T = R^T Tm^T,  dU^T = diag(D) W^T + dO^T P
-#pragma unroll
-    for (int u = 0; u < NST; ++u) {
-      const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
-      f32x4 uu = zero4(), du = zero4();
-#pragma unroll
-      for (int cs = 0; cs < 2; ++cs) {
-        if (32 * cs <= 16 * tb + 15)  // Tm lower
-          uu = mma(frag_cols(sm.u.sl.rb, LDW, 16 * vb, 32 * cs, lane), frag_rows(sm.tm, kLDC, 16 * tb, 32 * cs, lane), uu);
-        if (32 * cs + 31 >= 16 * tb)  // P lower: rows r >= i
-          du = mma(frag_cols(sm.u.sl.dob, LDW, 16 * vb, 32 * cs, lane), frag_cols(sm.p, kLDC, 16 * tb, 32 * cs, lane), du);
-      }
-      const int tk = 16 * tb + ls;
-      const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[tk]);
-      float uw = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        du[e] = fmaf(dd, WT[u][e], du[e]);
-        uw = fmaf(uu[e], WT[u][e], uw);
-      }
-      rs_uw[u] += uw;
-      store_tile_t(sm.u.sl.ub, LDW, 16 * tb, 16 * vb, uu, lane);
-      store_tile_t(sm.u.sl.dub, LDW, 16 * tb, 16 * vb, du, lane);
-    }
-    __syncthreads();
-    // ---- (c) dR^T = dU^T Tm;  dV = diag(beta) dR
-#pragma unroll
-    for (int u = 0; u < NST; ++u) {
-      const int t = wave + 8 * u, vb = t % NVB, tb = t / NVB;
-      f32x4 dr = zero4();
-#pragma unroll
-      for (int cs = 0; cs < 2; ++cs)
-        if (32 * cs + 31 >= 16 * tb)  // Tm[i][r] with i >= r
-          dr = mma(frag_cols(sm.u.sl.dub, LDW, 16 * vb, 32 * cs, lane), frag_cols(sm.tm, kLDC, 16 * tb, 32 * cs, lane), dr);
-      const int tk = 16 * tb + ls;
-      const float gm = __builtin_amdgcn_exp2f(sm.g[tk]), bt = sm.bt[tk];
-      float db = 0.0f, ry = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        db = fmaf(dr[e], VT[u][e] - gm * YT[u][e], db);
-        ry = fmaf(dr[e], YT[u][e], ry);
-      }
-      rs_db[u] += db;
-      rs_ry[u] += ry;
-      if (tk < n) store_bf4(dv + ((size_t)b * T + t0 + tk) * tokv + (size_t)h * VD + vs0 + 16 * vb + 4 * lg, dr * bt);
-      store_tile_t(sm.u.sl.drb, LDW, 16 * tb, 16 * vb, dr, lane);
-    }
-    __syncthreads();
-    // ---- (d) dP^T += U dO^T,  dA^T -= U dR^T   (upper (i, r) blocks, i <= r)
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int j = wave + 8 * u;
       if (j < 20) {
         const int jt = j % 10;
-        const int rbk = jt < 1 ? 0 : (jt < 3 ? 1 : (jt < 6 ? 2 : 3));   // r block
-        const int ibk = jt - rbk * (rbk + 1) / 2;                        // i block <= r block
-        const bf16* bsrc = j < 10 ? sm.u.sl.dob : sm.u.sl.drb;
+        const int rbk = jt < 1 ? 0 : (jt < 3 ? 1 : (jt < 6 ? 2 : 3));
+        const int ibk = jt - rbk * (rbk + 1) / 2;
+        // lane: i = 16 ibk + 4 lg + e, r = 16 rbk + ls
+        const int r = 16 * rbk + ls;
+        const float gr = sm.g[r], br = sm.bt[r];
+        // Gram tile in the same layout: G[i][r] = k_i . q_r (dP jobs) or
+        // k_i . k_r (dA jobs), exact bf16 products summed in fp32
+        const bf16* gsrc = j < 10 ? sm.q : sm.k;
+        f32x4 gram = zero4();
 #pragma unroll
-        for (int ks = 0; ks < VKS; ++ks)
-          pa[u] = mma(frag_rows(sm.u.sl.ub, LDW, 16 * ibk, 32 * ks, lane), frag_rows(bsrc, LDW, 16 * rbk, 32 * ks, lane), pa[u]);
+        for (int ks = 0; ks < KS; ++ks)
+          gram = mma(frag_rows(sm.k, LDK, 16 * ibk, 32 * ks, lane), frag_rows(gsrc, LDK, 16 * rbk, 32 * ks, lane), gram);
+        f32x4 val, prod;
+        if (j < 10) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * ibk + 4 * lg + e;
+            const float ee = __builtin_amdgcn_exp2f(i <= r ? gr - sm.g[i] : -INFINITY);
+            const float dp = i <= r ? pa[u][e] : 0.0f;
+            val[e] = dp * ee;
+            prod[e] = dp * (ee * gram[e]);   // dP o P, P = E o (Q K^T)
+          }
+          store_tile_t(sm.u.fin.dpe, kLDC, 16 * rbk, 16 * ibk, val, lane);
+          *reinterpret_cast<f32x4*>(&sm.u.fin.xp[r][16 * ibk + 4 * lg]) = prod;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * ibk + 4 * lg + e;
+            const float ee = __builtin_amdgcn_exp2f(i < r ? gr - sm.g[i] : -INFINITY);
+            const float da = i < r ? -pa[u][e] : 0.0f;
+            val[e] = da * br * ee;
+            prod[e] = da * (ee * gram[e]);   // dA o M, M = E o (K K^T), strictly lower
+          }
+          store_tile_t(sm.u.fin.dae, kLDC, 16 * rbk, 16 * ibk, val, lane);
+          *reinterpret_cast<f32x4*>(&sm.u.fin.xa[r][16 * ibk + 4 * lg]) = prod;
+        }
       }
     }
-    // ---- (e) dQ^T += S^T dO^T,  dK^T += dS'^T U^T (part 1), S^T dR^T (part 2)
+    __syncthreads();
+    // ---- (g) dQ^T = diag(gam) S^T dO^T + K^T (dP o E)^T
+    //          dK^T = D dS'^T U^T - beta gam S^T dR^T + Q^T (dP o E) + K^T (dA o bE)^T + K^T (dA o bE)
 #pragma unroll
     for (int u = 0; u < NQT; ++u) {
       const int t = wave + 8 * u, cb = t % NCB, tb = t / NCB;
+      const int tk = 16 * tb + ls;
+      const float gm = __builtin_amdgcn_exp2f(sm.g[tk]);
+      const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[tk]);
+      const float bg = sm.bt[tk] * gm;
+      f32x4 xq = aq[u] * gm;
+      f32x4 xk = ak1[u] * dd - ak2[u] * bg;
 #pragma unroll
-      for (int ks = 0; ks < VKS; ++ks) {
-        const bf16x8 st = frag_cols(sm.u.sl.s, LDK, 16 * cb, 32 * ks, lane);
-        aq[u] = mma(st, frag_rows(sm.u.sl.dob, LDW, 16 * tb, 32 * ks, lane), aq[u]);
-        ak1[u] = mma(frag_cols(sm.u.sl.ds, LDK, 16 * cb, 32 * ks, lane), frag_rows(sm.u.sl.ub, LDW, 16 * tb, 32 * ks, lane), ak1[u]);
-        ak2[u] = mma(st, frag_rows(sm.u.sl.drb, LDW, 16 * tb, 32 * ks, lane), ak2[u]);
-      }
-    }
-  }
-  // per-token row sums of the slice tiles: reduce over the four lane groups
-#pragma unroll
-  for (int u = 0; u < NST; ++u) {
-    float x[4] = {rs_oz[u], rs_uw[u], rs_db[u], rs_ry[u]};
-#pragma unroll
-    for (int qn = 0; qn < 4; ++qn) {
-      x[qn] += __shfl_xor(x[qn], 16);
-      x[qn] += __shfl_xor(x[qn], 32);
-    }
-    const int t = wave + 8 * u;
-    if (lg == 0)
-#pragma unroll
-      for (int qn = 0; qn < 4; ++qn) sm.red[qn][t][ls] = x[qn];
-  }
-  // <dS', S>: wave partial
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
-  if (lane == 0) sm.dot[wave] = dot;
-  __syncthreads();   // every slice array is dead from here
-
-  // ---- (f) dP o E, dA o beta E to LDS (bf16, [r][i]); dP o P and dA o M (fp32,
-  // with P and M recomputed in fp32 from the key and query tiles)
-  for (int p = tid; p < kC * kC / 8; p += 512) {   // zero the tiles no job writes
-    const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(&sm.u.fin.dpe[r * kLDC + c8]) = zero8();
-    *reinterpret_cast<bf16x8*>(&sm.u.fin.dae[r * kLDC + c8]) = zero8();
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int j = wave + 8 * u;
-    if (j < 20) {
-      const int jt = j % 10;
-      const int rbk = jt < 1 ? 0 : (jt < 3 ? 1 : (jt < 6 ? 2 : 3));
-      const int ibk = jt - rbk * (rbk + 1) / 2;
-      // lane: i = 16 ibk + 4 lg + e, r = 16 rbk + ls
-      const int r = 16 * rbk + ls;
-      const float gr = sm.g[r], br = sm.bt[r];
-      // Gram tile in the same layout: G[i][r] = k_i . q_r (dP jobs) or
-      // k_i . k_r (dA jobs), exact bf16 products summed in fp32
-      const bf16* gsrc = j < 10 ? sm.q : sm.k;
-      f32x4 gram = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        gram = mma(frag_rows(sm.k, LDK, 16 * ibk, 32 * ks, lane), frag_rows(gsrc, LDK, 16 * rbk, 32 * ks, lane), gram);
-      f32x4 val, prod;
-      if (j < 10) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * ibk + 4 * lg + e;
-          const float ee = __builtin_amdgcn_exp2f(i <= r ? gr - sm.g[i] : -INFINITY);
-          const float dp = i <= r ? pa[u][e] : 0.0f;
-          val[e] = dp * ee;
-          prod[e] = dp * (ee * gram[e]);   // dP o P, P = E o (Q K^T)
+      for (int cs = 0; cs < 2; ++cs) {
+        const bf16x8 kt = frag_cols(sm.k, LDK, 16 * cb, 32 * cs, lane);
+        if (32 * cs <= 16 * tb + 15) {   // (dP o E)[t][i], (dA o bE)[t][i]: i <= t
+          xq = mma(kt, frag_rows(sm.u.fin.dpe, kLDC, 16 * tb, 32 * cs, lane), xq);
+          xk = mma(kt, frag_rows(sm.u.fin.dae, kLDC, 16 * tb, 32 * cs, lane), xk);
         }
-        store_tile_t(sm.u.fin.dpe, kLDC, 16 * rbk, 16 * ibk, val, lane);
-        *reinterpret_cast<f32x4*>(&sm.u.fin.xp[r][16 * ibk + 4 * lg]) = prod;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * ibk + 4 * lg + e;
-          const float ee = __builtin_amdgcn_exp2f(i < r ? gr - sm.g[i] : -INFINITY);
-          const float da = i < r ? -pa[u][e] : 0.0f;
-          val[e] = da * br * ee;
-          prod[e] = da * (ee * gram[e]);   // dA o M, M = E o (K K^T), strictly lower
+        if (32 * cs + 31 >= 16 * tb) {   // (dP o E)[r][t], (dA o bE)[r][t]: r >= t
+          xk = mma(frag_cols(sm.q, LDK, 16 * cb, 32 * cs, lane), frag_cols(sm.u.fin.dpe, kLDC, 16 * tb, 32 * cs, lane), xk);
+          xk = mma(kt, frag_cols(sm.u.fin.dae, kLDC, 16 * tb, 32 * cs, lane), xk);
         }
-        store_tile_t(sm.u.fin.dae, kLDC, 16 * rbk, 16 * ibk, val, lane);
-        *reinterpret_cast<f32x4*>(&sm.u.fin.xa[r][16 * ibk + 4 * lg]) = prod;
+      }
+      if (tk < n) {
+        const size_t off = ((size_t)b * T + t0 + tk) * tokk + (size_t)h * KD + 16 * cb + 4 * lg;
+        store_bf4(dq + off, xq);
+        store_bf4(dk + off, xk);
       }
     }
-  }
-  __syncthreads();
-  // ---- (g) dQ^T = diag(gam) S^T dO^T + K^T (dP o E)^T
-  //          dK^T = D dS'^T U^T - beta gam S^T dR^T + Q^T (dP o E) + K^T (dA o bE)^T + K^T (dA o bE)
-#pragma unroll
-  for (int u = 0; u < NQT; ++u) {
-    const int t = wave + 8 * u, cb = t % NCB, tb = t / NCB;
-    const int tk = 16 * tb + ls;
-    const float gm = __builtin_amdgcn_exp2f(sm.g[tk]);
-    const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[tk]);
-    const float bg = sm.bt[tk] * gm;
-    f32x4 xq = aq[u] * gm;
-    f32x4 xk = ak1[u] * dd - ak2[u] * bg;
-#pragma unroll
-    for (int cs = 0; cs < 2; ++cs) {
-      const bf16x8 kt = frag_cols(sm.k, LDK, 16 * cb, 32 * cs, lane);
-      if (32 * cs <= 16 * tb + 15) {   // (dP o E)[t][i], (dA o bE)[t][i]: i <= t
-        xq = mma(kt, frag_rows(sm.u.fin.dpe, kLDC, 16 * tb, 32 * cs, lane), xq);
-        xk = mma(kt, frag_rows(sm.u.fin.dae, kLDC, 16 * tb, 32 * cs, lane), xk);
+    // ---- (h) per-token gate gradients: eight lanes per token split the row and
+    // column sums of dP o P and dA o M by index mod 8 and combine them with three
+    // shuffles (fixed order).  The sums skip the diagonal (dP o P's diagonal term
+    // would enter both and cancel; dA o M's diagonal is zero).
+    {
+      const int r = tid >> 3, q8 = tid & 7;
+      float sp = 0.0f, sa = 0.0f, cp = 0.0f, ca = 0.0f;
+      for (int i = q8; i < r; i += 8) {
+        sp += sm.u.fin.xp[r][i];
+        sa += sm.u.fin.xa[r][i];
       }
-      if (32 * cs + 31 >= 16 * tb) {   // (dP o E)[r][t], (dA o bE)[r][t]: r >= t
-        xk = mma(frag_cols(sm.q, LDK, 16 * cb, 32 * cs, lane), frag_cols(sm.u.fin.dpe, kLDC, 16 * tb, 32 * cs, lane), xk);
-        xk = mma(kt, frag_cols(sm.u.fin.dae, kLDC, 16 * tb, 32 * cs, lane), xk);
+      for (int rr = r + 1 + ((q8 - r - 1) & 7); rr < kC; rr += 8) {
+        cp += sm.u.fin.xp[rr][r];
+        ca += sm.bt[rr] * sm.u.fin.xa[rr][r];
+      }
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) {
+        sp += __shfl_xor(sp, m);
+        sa += __shfl_xor(sa, m);
+        cp += __shfl_xor(cp, m);
+        ca += __shfl_xor(ca, m);
+      }
+      if (q8 == 0) {
+        const int tb = r / 16, s = r % 16;
+        float oz = 0.0f, uw = 0.0f, db = 0.0f, ry = 0.0f;
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          oz += sm.red[0][tb * NVB + vb][s];
+          uw += sm.red[1][tb * NVB + vb][s];
+          db += sm.red[2][tb * NVB + vb][s];
+          ry += sm.red[3][tb * NVB + vb][s];
+        }
+        const float gm = __builtin_amdgcn_exp2f(sm.g[r]), br = sm.bt[r];
+        const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[r]);
+        sm.dgs[r] = gm * oz - br * gm * ry + (sp - cp) + (br * sa - ca);
+        sm.dbs[r] = db + sa;
+        sm.dus[r] = dd * uw;   // zero past the end (U rows are zero there)
       }
     }
-    if (tk < n) {
-      const size_t off = ((size_t)b * T + t0 + tk) * tokk + (size_t)h * KD + 16 * cb + 4 * lg;
-      store_bf4(dq + off, xq);
-      store_bf4(dk + off, xk);
-    }
-  }
-  // ---- (h) per-token gate gradients: eight lanes per token split the row and
-  // column sums of dP o P and dA o M by index mod 8 and combine them with three
-  // shuffles (fixed order).  The sums skip the diagonal (dP o P's diagonal term
-  // would enter both and cancel; dA o M's diagonal is zero).
-  {
-    const int r = tid >> 3, q8 = tid & 7;
-    float sp = 0.0f, sa = 0.0f, cp = 0.0f, ca = 0.0f;
-    for (int i = q8; i < r; i += 8) {
-      sp += sm.u.fin.xp[r][i];
-      sa += sm.u.fin.xa[r][i];
-    }
-    for (int rr = r + 1 + ((q8 - r - 1) & 7); rr < kC; rr += 8) {
-      cp += sm.u.fin.xp[rr][r];
-      ca += sm.bt[rr] * sm.u.fin.xa[rr][r];
-    }
+    __syncthreads();
+    if (wave == 0) {
+      // d ln alpha_t = sum_{t <= r < n} dg_r (a scan over the reversed tokens, with
+      // gam_last <dS', S> on the last real token) + sum_{r < t} D_r U_r.W_r (an
+      // exclusive scan): the U.W terms reach token t only through the gates of
+      // tokens before it, and summing them so, rather than as the chunk total minus
+      // a suffix, keeps small gates free of cancellation
+      float dsum = 0.0f;
 #pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-      sp += __shfl_xor(sp, m);
-      sa += __shfl_xor(sa, m);
-      cp += __shfl_xor(cp, m);
-      ca += __shfl_xor(ca, m);
-    }
-    if (q8 == 0) {
-      const int tb = r / 16, s = r % 16;
-      float oz = 0.0f, uw = 0.0f, db = 0.0f, ry = 0.0f;
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        oz += sm.red[0][tb * NVB + vb][s];
-        uw += sm.red[1][tb * NVB + vb][s];
-        db += sm.red[2][tb * NVB + vb][s];
-        ry += sm.red[3][tb * NVB + vb][s];
+      for (int w = 0; w < 8; ++w) dsum += sm.dot[w];
+      float dg = lane < n ? sm.dgs[lane] : 0.0f;
+      if (lane == n - 1) dg += __builtin_amdgcn_exp2f(sm.g[kC - 1]) * dsum;
+      const float suf = __shfl(wave_scan(__shfl(dg, 63 - lane), lane), 63 - lane);
+      // exclusive scan: shift by one token first (inclusive minus own would cancel)
+      const float pre = wave_scan(lane > 0 ? sm.dus[lane - 1] : 0.0f, lane);
+      if (lane < n) {
+        const size_t go = ((size_t)b * T + t0 + lane) * H + h;
+        dalpha[go] = (suf + pre) / alpha[go];
+        dbeta[go] = sm.dbs[lane];
       }
-      const float gm = __builtin_amdgcn_exp2f(sm.g[r]), br = sm.bt[r];
-      const float dd = __builtin_amdgcn_exp2f(sm.g[kC - 1] - sm.g[r]);
-      sm.dgs[r] = gm * oz - br * gm * ry + (sp - cp) + (br * sa - ca);
-      sm.dbs[r] = db + sa;
-      sm.dus[r] = dd * uw;   // zero past the end (U rows are zero there)
     }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // d ln alpha_t = sum_{t <= r < n} dg_r (a scan over the reversed tokens, with
-    // gam_last <dS', S> on the last real token) + sum_{r < t} D_r U_r.W_r (an
-    // exclusive scan): the U.W terms reach token t only through the gates of
-    // tokens before it, and summing them so, rather than as the chunk total minus
-    // a suffix, keeps small gates free of cancellation
-    float dsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) dsum += sm.dot[w];
-    float dg = lane < n ? sm.dgs[lane] : 0.0f;
-    if (lane == n - 1) dg += __builtin_amdgcn_exp2f(sm.g[kC - 1]) * dsum;
-    const float suf = __shfl(wave_scan(__shfl(dg, 63 - lane), lane), 63 - lane);
-    // exclusive scan: shift by one token first (inclusive minus own would cancel)
-    const float pre = wave_scan(lane > 0 ? sm.dus[lane - 1] : 0.0f, lane);
-    if (lane < n) {
-      const size_t go = ((size_t)b * T + t0 + lane) * H + h;
-      dalpha[go] = (suf + pre) / alpha[go];
-      dbeta[go] = sm.dbs[lane];
-    }
+    if (!more) break;
+    it = nx;
+    I = J;
+    __syncthreads();   // this item's reads of the chunk operands and sums are done
   }
 }
 
@@ -947,6 +995,7 @@ struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   bool failed = false;
+  int cus = 0;   // compute units of the device (0: not queried yet)
   std::mutex mu;
 };
 constexpr int kMaxDevices = 64;
@@ -1020,6 +1069,19 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   const bf16* k = static_cast<const bf16*>(a.k);
   const bf16* v = static_cast<const bf16*>(a.v);
   const bf16* d_o = static_cast<const bf16*>(a.d_o);
+  int cus = dev >= 0 ? g_side[dev].cus : 0;
+  if (cus <= 0) {
+    int d = dev, nc = 0;
+    if ((d >= 0 || hipGetDevice(&d) == hipSuccess) &&
+        hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, d) == hipSuccess && nc > 0) {
+      cus = nc;
+      if (dev >= 0) g_side[dev].cus = nc;   // under the device's lock
+    } else {
+      cus = 256;
+    }
+  }
+  const long items_local = (long)NT * a.H * a.B;
+  const int grid_local = (int)(items_local < cus ? items_local : cus);
   auto run = [&](auto kc) -> hipError_t {
     constexpr int KD = decltype(kc)::value;
     // (2) prep first, with the whole GPU; then (1) on the side stream beside (3):
@@ -1042,9 +1104,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     if (sd && (r = hipStreamWaitEvent(stream, sd->join, 0)) != hipSuccess) return r;   // states ready
     auto local = [&](auto vc) -> hipError_t {
       constexpr int VD = decltype(vc)::value;
-      hipLaunchKernelGGL((bwd16_local_kernel<KD, VD>), dim3(NT * a.H * a.B), dim3(512), 0, stream, q, k, v,
+      // one workgroup per CU (the kernel's LDS allows no more), each walking
+      // items blockIdx.x, + gridDim.x, ...
+      hipLaunchKernelGGL((bwd16_local_kernel<KD, VD>), dim3(grid_local), dim3(512), 0, stream, q, k, v,
                          d_o, a.alpha, ws_S, ws_dS, rec, static_cast<bf16*>(a.dq), static_cast<bf16*>(a.dk),
-                         static_cast<bf16*>(a.dv), a.dalpha, a.dbeta, a.T, a.H);
+                         static_cast<bf16*>(a.dv), a.dalpha, a.dbeta, a.B, a.T, a.H);
       return hipGetLastError();
     };
     switch (a.V) {

@@ -187,13 +187,15 @@ def bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, chunk: int = 64,
 
 def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
               chunk: int = 64, *, want_d_initial_state: bool = True, workspace=None,
-              stream=None):
+              out=None, stream=None):
     """Reverse mode of :func:`chunk_fwd` through ``gdn_chunk_bwd`` for the loss
     ``<o, d_o> + <final_state, d_final_state>``.
 
     Returns ``(dq, dk, dv, dalpha, dbeta, d_initial_state)``; the last is None
     when ``want_d_initial_state`` is False.  ``workspace`` may be a preallocated
-    uint8 device tensor of at least :func:`bwd_workspace_size` bytes.
+    uint8 device tensor of at least :func:`bwd_workspace_size` bytes; ``out`` may
+    be a tuple of the six preallocated results (d_initial_state None to skip it),
+    which are then written and returned.
     """
     lib = load_library()
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
@@ -224,13 +226,26 @@ def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
         made.append(workspace)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
-    dalpha = torch.empty_like(alpha)
-    dbeta = torch.empty_like(beta)
-    d_s0 = torch.empty((B, H, V, K), dtype=torch.float32, device=dev) if want_d_initial_state else None
-    made += [dq, dk, dv, dalpha, dbeta, d_s0]
+    if out is not None:
+        if len(out) != 6:
+            raise ValueError("out must hold (dq, dk, dv, dalpha, dbeta, d_initial_state)")
+        dq, dk, dv, dalpha, dbeta, d_s0 = out
+        _check(dq, "dq", (B, T, H, K), q.dtype, dev)
+        _check(dk, "dk", (B, T, H, K), q.dtype, dev)
+        _check(dv, "dv", (B, T, H, V), q.dtype, dev)
+        _check(dalpha, "dalpha", (B, T, H), torch.float32, dev)
+        _check(dbeta, "dbeta", (B, T, H), torch.float32, dev)
+        if d_s0 is not None:
+            _check(d_s0, "d_initial_state", (B, H, V, K), torch.float32, dev)
+    else:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        dalpha = torch.empty_like(alpha)
+        dbeta = torch.empty_like(beta)
+        d_s0 = (torch.empty((B, H, V, K), dtype=torch.float32, device=dev)
+                if want_d_initial_state else None)
+        made += [dq, dk, dv, dalpha, dbeta, d_s0]
     with torch.cuda.device(dev):
         s, other = _launch_stream(dev, stream)
         rc = lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),

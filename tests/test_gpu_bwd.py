@@ -149,6 +149,40 @@ def test_fwdbwd_f32_workload_parity():
     check(workload_inputs(w), w.chunk, TOL[w.dtype], w.name)
 
 
+def test_bwd_mfma_more_chunks_than_compute_units():
+    # the token-gradient kernel runs one workgroup per CU, each taking every
+    # gridDim-th (chunk, head, batch): 2 x 133 chunks (a ragged last one) > 256
+    # CUs, so some workgroups take two items and carry the prefetched operands of
+    # the second
+    inp = make_inputs(1, 64 * 132 + 17, 2, 64, 32, dtype=torch.bfloat16, seed=650, s0_std=0.05,
+                      with_do=True)
+    check(inp, 64, TOL[torch.bfloat16], "more chunks than CUs")
+
+
+def test_bwd_writes_preallocated_results():
+    inp = make_inputs(2, 150, 2, 64, 32, dtype=torch.bfloat16, seed=660, s0_std=0.05, with_do=True)
+    g = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
+    args = (g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["d_o"], g["initial_state"])
+    ref = chunk_bwd(*args, chunk=64)
+    res = tuple(torch.full_like(x, float("nan")) for x in ref)
+    got = chunk_bwd(*args, chunk=64, out=res)
+    torch.cuda.synchronize()
+    assert all(a is b for a, b in zip(got, res))
+    for x, y in zip(ref, got):
+        assert torch.equal(x, y)
+    # d_initial_state skipped
+    res2 = res[:5] + (None,)
+    got2 = chunk_bwd(*args, chunk=64, out=res2)
+    torch.cuda.synchronize()
+    assert got2[5] is None
+    for x, y in zip(ref[:5], got2[:5]):
+        assert torch.equal(x, y)
+    with pytest.raises(ValueError):
+        chunk_bwd(*args, chunk=64, out=res[:5])
+    with pytest.raises(ValueError):
+        chunk_bwd(*args, chunk=64, out=(res[2],) + res[1:])   # a dq of the wrong shape
+
+
 def test_bwd_mfma_on_a_side_stream_matches_default_stream():
     # the MFMA backward forks to a library stream and joins back; on a caller
     # stream other than the default the result must be the same bits
