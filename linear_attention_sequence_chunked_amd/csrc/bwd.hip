@@ -678,16 +678,18 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   float* ws_R = ws_F + (size_t)a.B * a.H * NT * factor_floats(C);  // float32: the records
   if constexpr (sizeof(TIn) == 4) {
     // float32: the matrix-core forward in its states-only mode, its per-chunk
-    // records after the factors in the workspace
+    // records after the factors in the workspace; its chunk-parallel launch
+    // writes the factors (2a) as well
     f.s_ckpt = ws_S;
+    f.factors = ws_F;
     e = launch_fwd_f32_records(f, ws_R, stream);
   } else {
     e = launch_fwd_states(f, true, ws_S, stream);
   }
   if (e != hipSuccess) return e;
 
-  // (2a) chunk factors
-  {
+  // (2a) chunk factors (bf16 inputs with K or V = 16; float32 ones have them)
+  if constexpr (sizeof(TIn) != 4) {
     const size_t LK = a.K + 1;
     const size_t lds = sizeof(float) * (2 * C * LK + 3 * C * C + 3 * C);
     if ((e = set_lds_limit<TIn>((const void*)bwd_prep_kernel<TIn>)) != hipSuccess) return e;

@@ -225,24 +225,31 @@ f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
 // ---------------------------------------------------------------------------
 // Token gradients of one chunk on the fp32 matrix cores: one workgroup (four
-// waves) per (chunk, head, batch).  Wave w walks the value axis in 16-wide
-// slices w, w + 4, ...; per slice (with S and dS' the chunk's start state and
-// end-state gradient, the slice's rows):
+// waves) per (chunk, head, batch).  The value axis is walked in rounds of four
+// 16-wide slices, wave w taking slice 4 rho + w of round rho; per slice (with S
+// and dS' the chunk's start state and end-state gradient, the slice's rows):
 //
 //   Y = K S^T, Z = Q S^T, W = K dS'^T, R = diag(beta) V - diag(beta gam) Y
 //   U = Tm R, dU = diag(D) W + P^T dO, dR = Tm^T dU, dV = diag(beta) dR
-//   dP += dO U^T, dA -= dR U^T, dQ += diag(gam) dO S,
-//   dK += diag(D) U dS' - diag(beta gam) dR S
+//   dP += dO U^T, dA -= dR U^T
 //
-// and the per-token sums of the gate gradients; the waves' partial dP, dA, dQ,
-// dK and sums are then added in wave order through LDS, and the chunk's
-// token-axis products finish dQ and dK:
+// and the per-token sums of the gate gradients.  The round's slice tiles (S,
+// dS', dO, U, dR) then stay in LDS for all four waves, and wave w adds every
+// slice's share of
+//
+//   dQ += diag(gam) dO S,  dK += diag(D) U dS' - diag(beta gam) dR S
+//
+// to the key-channel tiles it owns (w, w + 4, ...), so dQ and dK need no
+// reduction across waves; the waves' partial dP, dA and sums are added in wave
+// order through LDS, and the owners finish dQ and dK with the chunk's
+// token-axis products:
 //
 //   dQ += (dP o E) K,  dK += (dP o E)^T Q + (dA o bE) K + (dA o bE)^T K.
 //
 // The factors (M, P, Tm, gates) are the float32 prep's; the gate gradients use
-// its cancellation-free sums (bwd.hip).  Rows past the chunk end are staged as
-// zeros, with zero gates and factors, so they add nothing anywhere.
+// its cancellation-free sums (bwd.hip): the pair terms of token t run over
+// i < t <= r only.  Rows past the chunk end are staged as zeros, with zero
+// gates and factors, so they add nothing anywhere.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // sum over the 16 lanes of a lane group, in a fixed order; every lane ends with it
@@ -265,13 +272,17 @@ f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
   constexpr int LK = KD + 4, LCC = C + 4, LV = 16 + 4;
   constexpr int NW = 4;
   constexpr int NBL = NB * (NB + 1) / 2;       // lower token blocks
-  struct WaveArea {                             // one wave's slice tiles
+  constexpr int NKO = (KQ + NW - 1) / NW;      // key-channel tiles a wave owns
+  static_assert(C <= 64, "one lane per token in the gate scans");
+  struct WaveArea {                             // one slice's tiles
     float S[16 * LK], dS[16 * LK];              // [v][k]
     float dO[C * LV], U[C * LV], dR[C * LV];    // [t][v]
   };
-  struct Red {                                  // the waves' partials, added in order
-    float dQ[C * KD], dK[C * KD];               // [t][k]
+  struct Red {                                  // after the value walk
     float dP[C * LCC], dA[C * LCC];             // [r][i]
+    float X[C * LCC];                           // pair terms of the gate sums
+    float pP[NW][C * LCC], pA[NW][C * LCC];     // the waves' partial dP, dA
+    float pdb[NW][C], pdg[NW][C], puw[NW][C];   // the waves' per-token sums
   };
   union Area {
     WaveArea wave[NW];
@@ -291,37 +302,61 @@ f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
   const size_t ck = (((size_t)b * H + h) * NT + c) * (size_t)V * KD;
   const size_t row0 = ((size_t)b * T + t0) * H + h;   // token row of the chunk's first token
 
-  // key / query tiles (rows past the end zero), the prep's factors and gates
-  for (int i = tid; i < C * (KD / 4); i += 256) {
-    const int r = i / (KD / 4), c4 = i - r * (KD / 4);
-    const bool ok = r < n;
-    const size_t off = (row0 + (size_t)(ok ? r : 0) * H) * KD + 4 * c4;
-    const f32x4 kx = ld4(k + off), qx = ld4(q + off);
-    st4(sK + r * LK + 4 * c4, ok ? kx : zero4f());
-    st4(sQ + r * LK + 4 * c4, ok ? qx : zero4f());
-  }
-  const float* F = ws_F + (((size_t)b * H + h) * NT + c) * (3 * C * C + 3 * C);
-  for (int i = tid; i < C * C; i += 256) {
-    const int r = i / C, j = i - r * C;
-    sM[r * LCC + j] = F[i];
-    sP[r * LCC + j] = F[C * C + i];
-    sT[r * LCC + j] = F[2 * C * C + i];
-  }
-  if (tid < C) {
-    const float gl = F[3 * C * C + n - 1];
-    const bool ok = tid < n;
-    sg[tid] = F[3 * C * C + tid];
-    sgam[tid] = ok ? F[3 * C * C + C + tid] : 0.0f;
-    sb[tid] = ok ? F[3 * C * C + 2 * C + tid] : 0.0f;
-    sD[tid] = ok ? expf(gl - F[3 * C * C + tid]) : 0.0f;
+  // key / query tiles (rows past the end zero), the prep's factors and gates:
+  // every load is issued before the first LDS write
+  {
+    constexpr int NKP = C * (KD / 4), KP = (NKP + 255) / 256;
+    static_assert(C * C % 256 == 0, "whole factor pieces per thread");
+    f32x4 kx[KP], qx[KP];
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      const int i = min(tid + 256 * j, NKP - 1), r = i / (KD / 4), c4 = i - r * (KD / 4);
+      const size_t off = (row0 + (size_t)(r < n ? r : 0) * H) * KD + 4 * c4;
+      kx[j] = ld4(k + off);
+      qx[j] = ld4(q + off);
+    }
+    const float* F = ws_F + (((size_t)b * H + h) * NT + c) * (3 * C * C + 3 * C);
+    constexpr int FP = C * C / 256;
+    float fm[FP], fp[FP], ft[FP];
+#pragma unroll
+    for (int j = 0; j < FP; ++j) {
+      fm[j] = F[tid + 256 * j];
+      fp[j] = F[C * C + tid + 256 * j];
+      ft[j] = F[2 * C * C + tid + 256 * j];
+    }
+    const int tg = tid & (C - 1);
+    const float gl = F[3 * C * C + n - 1], gt = F[3 * C * C + tg];
+    const float gam = F[3 * C * C + C + tg], bet = F[3 * C * C + 2 * C + tg];
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      const int i = tid + 256 * j, r = i / (KD / 4), c4 = i - r * (KD / 4);
+      if (i < NKP) {
+        st4(sK + r * LK + 4 * c4, r < n ? kx[j] : zero4f());
+        st4(sQ + r * LK + 4 * c4, r < n ? qx[j] : zero4f());
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FP; ++j) {
+      const int i = tid + 256 * j, r = i / C, jj = i - r * C;
+      sM[r * LCC + jj] = fm[j];
+      sP[r * LCC + jj] = fp[j];
+      sT[r * LCC + jj] = ft[j];
+    }
+    if (tid < C) {
+      const bool ok = tid < n;
+      sg[tid] = gt;
+      sgam[tid] = ok ? gam : 0.0f;
+      sb[tid] = ok ? bet : 0.0f;
+      sD[tid] = ok ? expf(gl - gt) : 0.0f;
+    }
   }
   __syncthreads();
 
-  f32x4 aQ[NB][KQ], aK[NB][KQ], aP[NBL], aA[NBL];
+  f32x4 aQ[NB][NKO], aK[NB][NKO], aP[NBL], aA[NBL];
 #pragma unroll
   for (int I = 0; I < NB; ++I)
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) aQ[I][kq] = aK[I][kq] = zero4f();
+    for (int m = 0; m < NKO; ++m) aQ[I][m] = aK[I][m] = zero4f();
 #pragma unroll
   for (int i = 0; i < NBL; ++i) aP[i] = aA[i] = zero4f();
   float pdb[NB][4], poz[NB][4], pry[NB][4], puw[NB][4];
@@ -332,138 +367,165 @@ f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
   float pdot = 0.0f;
 
   WaveArea& A = area.wave[w];
-  for (int sl = w; sl < V / 16; sl += NW) {
-    const int v0 = 16 * sl;
-    // the slice's rows of S and dS' ([v][k]), and its dO columns ([t][v])
+  const int nsl = V / 16;
+  for (int sl0 = 0; sl0 < nsl; sl0 += NW) {
+    // ---- this wave's slice (a wave past the last slice loads the last one
+    // again, so that no load sits under a branch, and adds nothing)
+    const bool act = sl0 + w < nsl;
+    const int v0 = 16 * min(sl0 + w, nsl - 1);
+    {
+      constexpr int SPL = 16 * KD / 4 / 64;     // float4 pieces per lane of 16 state rows
+      constexpr int OPL = (C * 4 + 63) / 64;    // float4 pieces per lane of the dO columns
+      f32x4 sx[SPL], dx[SPL], ox[OPL];
 #pragma unroll
-    for (int j = 0; j < 16 * KD / 4 / 64; ++j) {
-      const int p = lane + 64 * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
-      const f32x4 sx = ld4(ws_S + ck + (size_t)(v0 + r) * KD + 4 * c4);
-      const f32x4 dx = ld4(ws_dS + ck + (size_t)(v0 + r) * KD + 4 * c4);
-      pdot += (sx[0] * dx[0] + sx[1] * dx[1]) + (sx[2] * dx[2] + sx[3] * dx[3]);
-      st4(A.S + r * LK + 4 * c4, sx);
-      st4(A.dS + r * LK + 4 * c4, dx);
-    }
-#pragma unroll
-    for (int j = 0; j < (C * 4 + 63) / 64; ++j) {
-      const int p = lane + 64 * j, r = p >> 2, c4 = p & 3;
-      if (p < C * 4) {
-        const bool ok = r < n;
-        const f32x4 x = ld4(d_o + (row0 + (size_t)(ok ? r : 0) * H) * V + v0 + 4 * c4);
-        st4(A.dO + r * LV + 4 * c4, ok ? x : zero4f());
+      for (int j = 0; j < SPL; ++j) {
+        const int p = lane + 64 * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
+        sx[j] = ld4(ws_S + ck + (size_t)(v0 + r) * KD + 4 * c4);
+        dx[j] = ld4(ws_dS + ck + (size_t)(v0 + r) * KD + 4 * c4);
       }
-    }
-    float vv[NB][4];
 #pragma unroll
-    for (int I = 0; I < NB; ++I)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + 4 * g + e;
-        const float x = v[(row0 + (size_t)(t < n ? t : 0) * H) * V + v0 + s];
-        vv[I][e] = t < n ? x : 0.0f;
+      for (int j = 0; j < OPL; ++j) {
+        const int p = min(lane + 64 * j, C * 4 - 1), r = p >> 2, c4 = p & 3;
+        ox[j] = ld4(d_o + (row0 + (size_t)(r < n ? r : 0) * H) * V + v0 + 4 * c4);
       }
-    wave_lds_sync();
+      float vv[NB][4];
+#pragma unroll
+      for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * I + 4 * g + e;
+          vv[I][e] = v[(row0 + (size_t)(t < n ? t : 0) * H) * V + v0 + s];
+        }
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const int p = lane + 64 * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
+        if (act) pdot += (sx[j][0] * dx[j][0] + sx[j][1] * dx[j][1]) + (sx[j][2] * dx[j][2] + sx[j][3] * dx[j][3]);
+        st4(A.S + r * LK + 4 * c4, sx[j]);
+        st4(A.dS + r * LK + 4 * c4, dx[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < OPL; ++j) {
+        const int p = lane + 64 * j, r = p >> 2, c4 = p & 3;
+        if (p < C * 4) st4(A.dO + r * LV + 4 * c4, r < n ? ox[j] : zero4f());
+      }
+      wave_lds_sync();
 
-    // Y, Z, W
-    f32x4 Y[NB], Z[NB], Wt[NB];
+      // Y, Z, W
+      f32x4 Y[NB], Z[NB], Wt[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      Y[I] = Z[I] = Wt[I] = zero4f();
+      for (int I = 0; I < NB; ++I) {
+        Y[I] = Z[I] = Wt[I] = zero4f();
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq) {
-        const f32x4 ak = ld4(sK + (16 * I + s) * LK + 16 * kq + 4 * g);
-        const f32x4 bs = ld4(A.S + s * LK + 16 * kq + 4 * g);
-        Y[I] = mma16(ak, bs, Y[I]);
-        Z[I] = mma16(ld4(sQ + (16 * I + s) * LK + 16 * kq + 4 * g), bs, Z[I]);
-        Wt[I] = mma16(ak, ld4(A.dS + s * LK + 16 * kq + 4 * g), Wt[I]);
+        for (int kq = 0; kq < KQ; ++kq) {
+          const f32x4 ak = ld4(sK + (16 * I + s) * LK + 16 * kq + 4 * g);
+          const f32x4 bs = ld4(A.S + s * LK + 16 * kq + 4 * g);
+          Y[I] = mma16(ak, bs, Y[I]);
+          Z[I] = mma16(ld4(sQ + (16 * I + s) * LK + 16 * kq + 4 * g), bs, Z[I]);
+          Wt[I] = mma16(ak, ld4(A.dS + s * LK + 16 * kq + 4 * g), Wt[I]);
+        }
       }
-    }
-    // R, U = Tm R
-    f32x4 R[NB], U[NB], dU[NB], dR[NB];
+      // R, U = Tm R
+      f32x4 R[NB], U[NB], dU[NB], dR[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + 4 * g + e;
-        R[I][e] = sb[t] * vv[I][e] - sb[t] * sgam[t] * Y[I][e];
-      }
-#pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      U[I] = zero4f();
-#pragma unroll
-      for (int J = 0; J <= I; ++J) U[I] = mma16(ld4(sT + (16 * I + s) * LCC + 16 * J + 4 * g), R[J], U[I]);
-    }
-    // dU = diag(D) W + P^T dO, dR = Tm^T dU
-#pragma unroll
-    for (int I = 0; I < NB; ++I) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dU[I][e] = sD[16 * I + 4 * g + e] * Wt[I][e];
-#pragma unroll
-      for (int J = I; J < NB; ++J) {
-        f32x4 a, bo;
+      for (int I = 0; I < NB; ++I)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = sP[(16 * J + 4 * g + e) * LCC + 16 * I + s];
-          bo[e] = A.dO[(16 * J + 4 * g + e) * LV + s];
+          const int t = 16 * I + 4 * g + e;
+          const float x = t < n ? vv[I][e] : 0.0f;
+          vv[I][e] = x;
+          R[I][e] = sb[t] * x - sb[t] * sgam[t] * Y[I][e];
         }
-        dU[I] = mma16(a, bo, dU[I]);
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        U[I] = zero4f();
+#pragma unroll
+        for (int J = 0; J <= I; ++J) U[I] = mma16(ld4(sT + (16 * I + s) * LCC + 16 * J + 4 * g), R[J], U[I]);
       }
-    }
+      // dU = diag(D) W + P^T dO, dR = Tm^T dU
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      dR[I] = zero4f();
+      for (int I = 0; I < NB; ++I) {
 #pragma unroll
-      for (int J = I; J < NB; ++J) {
-        f32x4 a;
+        for (int e = 0; e < 4; ++e) dU[I][e] = sD[16 * I + 4 * g + e] * Wt[I][e];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = sT[(16 * J + 4 * g + e) * LCC + 16 * I + s];
-        dR[I] = mma16(a, dU[J], dR[I]);
+        for (int J = I; J < NB; ++J) {
+          f32x4 a, bo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = sP[(16 * J + 4 * g + e) * LCC + 16 * I + s];
+            bo[e] = A.dO[(16 * J + 4 * g + e) * LV + s];
+          }
+          dU[I] = mma16(a, bo, dU[I]);
+        }
       }
-    }
-    // dV, the per-token partial sums, U and dR to LDS
 #pragma unroll
-    for (int I = 0; I < NB; ++I)
+      for (int I = 0; I < NB; ++I) {
+        dR[I] = zero4f();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + 4 * g + e;
-        if (t < n) dv[(row0 + (size_t)t * H) * V + v0 + s] = sb[t] * dR[I][e];
-        pdb[I][e] += dR[I][e] * (vv[I][e] - sgam[t] * Y[I][e]);
-        poz[I][e] += A.dO[t * LV + s] * Z[I][e];
-        pry[I][e] += dR[I][e] * Y[I][e];
-        puw[I][e] += U[I][e] * Wt[I][e];
-        A.U[t * LV + s] = U[I][e];
-        A.dR[t * LV + s] = dR[I][e];
+        for (int J = I; J < NB; ++J) {
+          f32x4 a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = sT[(16 * J + 4 * g + e) * LCC + 16 * I + s];
+          dR[I] = mma16(a, dU[J], dR[I]);
+        }
       }
-    wave_lds_sync();
-    // dP += dO U^T, dA += dR U^T (negated at the end), lower blocks
+      // dV, the per-token partial sums, U and dR to LDS
 #pragma unroll
-    for (int I = 0; I < NB; ++I)
-#pragma unroll
-      for (int J = 0; J <= I; ++J) {
-        const int blk = I * (I + 1) / 2 + J;
-        const f32x4 bu = ld4(A.U + (16 * J + s) * LV + 4 * g);
-        aP[blk] = mma16(ld4(A.dO + (16 * I + s) * LV + 4 * g), bu, aP[blk]);
-        aA[blk] = mma16(ld4(A.dR + (16 * I + s) * LV + 4 * g), bu, aA[blk]);
-      }
-    // dQ += diag(gam) dO S;  dK += diag(D) U dS' - diag(beta gam) dR S
-#pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      const int r = 16 * I + s;
-      const f32x4 ao = ld4(A.dO + r * LV + 4 * g) * sgam[r];
-      const f32x4 au = ld4(A.U + r * LV + 4 * g) * sD[r];
-      const f32x4 ar = ld4(A.dR + r * LV + 4 * g) * (-sb[r] * sgam[r]);
-#pragma unroll
-      for (int kq = 0; kq < KQ; ++kq) {
-        f32x4 bs, bd;
+      for (int I = 0; I < NB; ++I)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          bs[e] = A.S[(4 * g + e) * LK + 16 * kq + s];
-          bd[e] = A.dS[(4 * g + e) * LK + 16 * kq + s];
+          const int t = 16 * I + 4 * g + e;
+          if (act) {
+            if (t < n) dv[(row0 + (size_t)t * H) * V + v0 + s] = sb[t] * dR[I][e];
+            pdb[I][e] += dR[I][e] * (vv[I][e] - sgam[t] * Y[I][e]);
+            poz[I][e] += A.dO[t * LV + s] * Z[I][e];
+            pry[I][e] += dR[I][e] * Y[I][e];
+            puw[I][e] += U[I][e] * Wt[I][e];
+          }
+          A.U[t * LV + s] = U[I][e];
+          A.dR[t * LV + s] = dR[I][e];
         }
-        aQ[I][kq] = mma16(ao, bs, aQ[I][kq]);
-        aK[I][kq] = mma16(ar, bs, mma16(au, bd, aK[I][kq]));
+      wave_lds_sync();
+      // dP += dO U^T, dA += dR U^T (negated at the end), lower blocks
+      if (act) {
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+          for (int J = 0; J <= I; ++J) {
+            const int blk = I * (I + 1) / 2 + J;
+            const f32x4 bu = ld4(A.U + (16 * J + s) * LV + 4 * g);
+            aP[blk] = mma16(ld4(A.dO + (16 * I + s) * LV + 4 * g), bu, aP[blk]);
+            aA[blk] = mma16(ld4(A.dR + (16 * I + s) * LV + 4 * g), bu, aA[blk]);
+          }
       }
     }
+    __syncthreads();   // the round's slice tiles are complete
+    // ---- dQ += diag(gam) dO S;  dK += diag(D) U dS' - diag(beta gam) dR S, over
+    // the round's slices, for the key-channel tiles this wave owns
+    for (int x = 0; x < NW && sl0 + x < nsl; ++x) {
+      const WaveArea& X = area.wave[x];
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        const int r = 16 * I + s;
+        const f32x4 ao = ld4(X.dO + r * LV + 4 * g) * sgam[r];
+        const f32x4 au = ld4(X.U + r * LV + 4 * g) * sD[r];
+        const f32x4 ar = ld4(X.dR + r * LV + 4 * g) * (-sb[r] * sgam[r]);
+#pragma unroll
+        for (int m = 0; m < NKO; ++m) {
+          const int kq = w + NW * m;
+          if (kq < KQ) {
+            f32x4 bs, bd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              bs[e] = X.S[(4 * g + e) * LK + 16 * kq + s];
+              bd[e] = X.dS[(4 * g + e) * LK + 16 * kq + s];
+            }
+            aQ[I][m] = mma16(ao, bs, aQ[I][m]);
+            aK[I][m] = mma16(ar, bs, mma16(au, bd, aK[I][m]));
+          }
+        }
+      }
+    }
+    __syncthreads();   // the slice tiles may be overwritten
   }
 
   // per-token sums: over the 16 lanes of a group, then over the waves
@@ -478,79 +540,92 @@ f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) pdot += __shfl_xor(pdot, m, 64);
-  __syncthreads();   // every wave is done with its slice tiles: the union turns into Red
+  // the waves' partials to their own slots, then added in wave order
   Red& RD = area.red;
-  for (int ww = 0; ww < NW; ++ww) {
-    if (w == ww) {
-      const bool first = ww == 0;
 #pragma unroll
-      for (int I = 0; I < NB; ++I)
+  for (int I = 0; I < NB; ++I)
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq)
+    for (int J = 0; J <= I; ++J) {
+      const int blk = I * (I + 1) / 2 + J;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int o4 = (16 * I + 4 * g + e) * KD + 16 * kq + s;
-            RD.dQ[o4] = first ? aQ[I][kq][e] : RD.dQ[o4] + aQ[I][kq][e];
-            RD.dK[o4] = first ? aK[I][kq][e] : RD.dK[o4] + aK[I][kq][e];
-          }
-#pragma unroll
-      for (int I = 0; I < NB; ++I)
-#pragma unroll
-        for (int J = 0; J <= I; ++J) {
-          const int blk = I * (I + 1) / 2 + J;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int o2 = (16 * I + 4 * g + e) * LCC + 16 * J + s;
-            RD.dP[o2] = first ? aP[blk][e] : RD.dP[o2] + aP[blk][e];
-            RD.dA[o2] = first ? aA[blk][e] : RD.dA[o2] + aA[blk][e];
-          }
-        }
-      if (s == 0) {
-#pragma unroll
-        for (int I = 0; I < NB; ++I)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = 16 * I + 4 * g + e;
-            const float dg = sgam[t] * poz[I][e] - sb[t] * sgam[t] * pry[I][e];
-            sdb[t] = first ? pdb[I][e] : sdb[t] + pdb[I][e];
-            sdg[t] = first ? dg : sdg[t] + dg;
-            sdu[t] = first ? sD[t] * puw[I][e] : fmaf(sD[t], puw[I][e], sdu[t]);
-          }
+      for (int e = 0; e < 4; ++e) {
+        const int o2 = (16 * I + 4 * g + e) * LCC + 16 * J + s;
+        RD.pP[w][o2] = aP[blk][e];
+        RD.pA[w][o2] = aA[blk][e];
       }
-      if (lane == 0) sdot[ww] = pdot;
     }
-    __syncthreads();
+  if (s == 0) {
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * g + e;
+        RD.pdb[w][t] = pdb[I][e];
+        RD.pdg[w][t] = sgam[t] * poz[I][e] - sb[t] * sgam[t] * pry[I][e];
+        RD.puw[w][t] = puw[I][e];
+      }
   }
+  if (lane == 0) sdot[w] = pdot;
+  __syncthreads();
   // masks and signs: dP lower (j <= r), dA = -(dR U^T) strictly lower; the pair
-  // sums of the gate gradients, then (dP o E) and (dA o beta E) in place
+  // terms X[r][j] = dP[r][j] P[r][j] + dA[r][j] beta_r M[r][j] (j < r)
   for (int i = tid; i < C * C; i += 256) {
     const int r = i / C, j = i - r * C;
-    if (r >= NB * 16 || j > r || r >= n) {
-      if (r < C) {
-        RD.dP[r * LCC + j] = 0.0f;
-        RD.dA[r * LCC + j] = 0.0f;
-      }
+    const int o = r * LCC + j;
+    if (r >= n || j > r) {
+      RD.dP[o] = 0.0f;
+      RD.dA[o] = 0.0f;
+      RD.X[o] = 0.0f;
     } else {
-      if (j == r) RD.dA[r * LCC + j] = 0.0f;
-      else RD.dA[r * LCC + j] = -RD.dA[r * LCC + j];
+      float dp = RD.pP[0][o], da = RD.pA[0][o];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) {
+        dp += RD.pP[ww][o];
+        da += RD.pA[ww][o];
+      }
+      da = j == r ? 0.0f : -da;
+      RD.dP[o] = dp;
+      RD.dA[o] = da;
+      RD.X[o] = j < r ? fmaf(da, sb[r] * sM[o], dp * sP[o]) : 0.0f;
+    }
+  }
+  if (tid < C) {
+    const int t = tid;
+    float db = RD.pdb[0][t], dg = RD.pdg[0][t], du = sD[t] * RD.puw[0][t];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) {
+      db += RD.pdb[ww][t];
+      dg += RD.pdg[ww][t];
+      du = fmaf(sD[t], RD.puw[ww][t], du);
+    }
+    sdb[t] = db;
+    sdg[t] = dg;
+    sdu[t] = du;
+  }
+  __syncthreads();
+  // sxr[t] = sum over i < t <= r of X[r][i]: suffix sums down each column (one
+  // thread per column), then the part of row t left of the diagonal (one
+  // thread per row); and the row sums of dA o M for dbeta
+  if (tid < C) {
+    float acc = 0.0f;
+    for (int r = C - 1; r > tid; --r) {
+      acc += RD.X[r * LCC + tid];
+      RD.X[r * LCC + tid] = acc;
     }
   }
   __syncthreads();
-  if (tid < n) {
+  if (tid < C) {
     const int t = tid;
     float sx = 0.0f, db = 0.0f;
-    for (int r = t; r < n; ++r) {
-      const float br = sb[r];
-      for (int i = 0; i < t; ++i) {
-        sx = fmaf(RD.dP[r * LCC + i], sP[r * LCC + i], sx);
-        sx = fmaf(RD.dA[r * LCC + i], br * sM[r * LCC + i], sx);
-      }
+    for (int i = 0; i < t; ++i) {
+      sx += RD.X[t * LCC + i];
+      db = fmaf(RD.dA[t * LCC + i], sM[t * LCC + i], db);
     }
-    for (int i = 0; i < t; ++i) db = fmaf(RD.dA[t * LCC + i], sM[t * LCC + i], db);
     sxr[t] = sx;
     sdb[t] += db;
   }
   __syncthreads();
+  // (dP o E) and (dA o beta E) in place
   for (int i = tid; i < C * C; i += 256) {
     const int r = i / C, j = i - r * C;
     if (r < n && j <= r) {
@@ -560,17 +635,15 @@ f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
   }
   __syncthreads();
-  // dQ += (dP o E) K;  dK += (dP o E)^T Q + (dA o bE) K + (dA o bE)^T K: wave w
-  // finishes key-channel tiles w, w + 4, ...
-  for (int kq = w; kq < KQ; kq += NW) {
+  // dQ += (dP o E) K;  dK += (dP o E)^T Q + (dA o bE) K + (dA o bE)^T K on the
+  // owned key-channel tiles
+#pragma unroll
+  for (int m = 0; m < NKO; ++m) {
+    const int kq = w + NW * m;
+    if (kq >= KQ) continue;
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
-      f32x4 accq, acck;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        accq[e] = RD.dQ[(16 * I + 4 * g + e) * KD + 16 * kq + s];
-        acck[e] = RD.dK[(16 * I + 4 * g + e) * KD + 16 * kq + s];
-      }
+      f32x4 accq = aQ[I][m], acck = aK[I][m];
 #pragma unroll
       for (int J = 0; J < NB; ++J) {
         f32x4 bk, bq;
@@ -604,23 +677,21 @@ f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
       }
     }
   }
-  // gate gradients (the cancellation-free sums of bwd.hip), one thread
-  if (tid == 0) {
+  // gate gradients (the cancellation-free sums of bwd.hip), one lane per token:
+  // d ln alpha_t = sum_{r >= t} dg_r (with gam_last <dS', S> on the last token)
+  // + sxr_t + sum_{r < t} D_r U_r.W_r
+  if (w == 0) {
     float dot = 0.0f;
+#pragma unroll
     for (int ww = 0; ww < NW; ++ww) dot += sdot[ww];
-    sdg[n - 1] += sgam[n - 1] * dot;
-    float pre = 0.0f;
-    for (int r = 0; r < n; ++r) {
-      const float du = sdu[r];
-      sdu[r] = pre;
-      pre += du;
-    }
-    float acc = 0.0f;
-    for (int r = n - 1; r >= 0; --r) {
-      acc += sdg[r];
-      const size_t go = row0 + (size_t)r * H;
-      dalpha[go] = (acc + sxr[r] + sdu[r]) / alpha[go];
-      dbeta[go] = sdb[r];
+    float dg = lane < n ? sdg[lane] : 0.0f;
+    if (lane == n - 1) dg += sgam[n - 1] * dot;
+    const float suf = __shfl(mfma::wave_scan(__shfl(dg, 63 - lane), lane), 63 - lane);
+    const float pre = mfma::wave_scan(lane > 0 && lane - 1 < n ? sdu[lane - 1] : 0.0f, lane);
+    if (lane < n) {
+      const size_t go = row0 + (size_t)lane * H;
+      dalpha[go] = (suf + sxr[lane] + pre) / alpha[go];
+      dbeta[go] = sdb[lane];
     }
   }
 }

@@ -49,7 +49,8 @@ template <int KD, int C>
 __global__ void __launch_bounds__(256)
 f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
                   const float* __restrict__ alpha, const float* __restrict__ beta,
-                  float* __restrict__ rec, const int* __restrict__ cu, int B, int T, int H, int NT) {
+                  float* __restrict__ rec, float* __restrict__ fact, const int* __restrict__ cu, int B,
+                  int T, int H, int NT) {
   constexpr int NB = C / 16;
   constexpr int LK = KD + 4;            // K rows in LDS: 16 lanes of a float4 read hit 16 bank quads
   constexpr int LC = C + 4;
@@ -90,6 +91,9 @@ f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
   const int n = min(C, Tn - t0);
   float* R = rec + ((size_t)slot * H + h) * Rec<C>::kFloats;
   const size_t row0 = (seq0 + t0) * H + h;   // token row of the chunk's first token
+  // the backward's factors of this chunk (dense batches only): M, P, Tm as C x C
+  // row-major, then the cumulative natural-log gate, gam and beta
+  float* Fc = fact ? fact + (((size_t)b * H + h) * NT + c) * (3 * C * C + 3 * C) : nullptr;
 
   // K tile to LDS (rows past the chunk end are zero)
   for (int i = tid; i < C * (KD / 4); i += 256) {
@@ -142,9 +146,13 @@ f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * I + 4 * g + e;
         if (pkind) {
-          R[Rec<C>::kP + Rec<C>::at(I, J, 4 * g + e, s)] = j <= i ? exp2f(sg[i] - sg[j]) * acc[e] : 0.0f;
+          const float p = j <= i ? exp2f(sg[i] - sg[j]) * acc[e] : 0.0f;
+          R[Rec<C>::kP + Rec<C>::at(I, J, 4 * g + e, s)] = p;
+          if (Fc) Fc[C * C + i * C + j] = p;
         } else {
-          sA[i * LC + j] = j < i ? sb[i] * exp2f(sg[i] - sg[j]) * acc[e] : 0.0f;
+          const float m = j < i ? exp2f(sg[i] - sg[j]) * acc[e] : 0.0f;
+          sA[i * LC + j] = sb[i] * m;
+          if (Fc) Fc[i * C + j] = m;
         }
       }
     }
@@ -203,6 +211,24 @@ f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
     R[Rec<C>::kGam + tid] = exp2f(sg[tid]);
     R[Rec<C>::kDn + tid] = exp2f(gl - sg[tid]);
     if (tid < 4) R[Rec<C>::kGn + tid] = tid == 0 ? exp2f(gl) : 0.0f;
+  }
+  if (Fc) {
+    // the blocks above the diagonal of M and P are zero; Tm with the rows and
+    // columns past the chunk end zero (the layout of the scalar prep's factors)
+    for (int i = tid; i < C * C; i += 256) {
+      const int r = i / C, j = i - r * C;
+      if (j / 16 > r / 16) {
+        Fc[i] = 0.0f;
+        Fc[C * C + i] = 0.0f;
+      }
+      Fc[2 * C * C + i] = r < n && j < n && j / 16 <= r / 16 ? sT[r * LC + j] : 0.0f;
+    }
+    if (tid < C) {
+      const bool live = tid < n;
+      Fc[3 * C * C + tid] = live ? sg[tid] * 0.69314718055994531f : 0.0f;
+      Fc[3 * C * C + C + tid] = live ? exp2f(sg[tid]) : 0.0f;
+      Fc[3 * C * C + 2 * C + tid] = sb[tid];
+    }
   }
 }
 
@@ -507,7 +533,7 @@ hipError_t launch_kc(const FwdArgs& a, float* rec, hipStream_t stream) {
   const long slots = a.cu_seqlens ? (long)(a.T / C) + a.B + 1 : (long)a.B * NT;
   hipLaunchKernelGGL((f32_record_kernel<KD, C>), dim3(slots * a.H), dim3(256), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k), a.alpha,
-                     a.beta, rec, a.cu_seqlens, a.B, a.T, a.H, NT);
+                     a.beta, rec, a.cu_seqlens ? nullptr : a.factors, a.cu_seqlens, a.B, a.T, a.H, NT);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.o && a.v && !a.s_ckpt) return launch_chain<KD, C, true, true, false>(a, rec, NT, stream);

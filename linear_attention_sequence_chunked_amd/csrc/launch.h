@@ -22,6 +22,10 @@ struct FwdArgs {
   // bf16 kernel, states only (o null): optional chunk-start states rounded to
   // bf16, [B, H, NT, V, K]
   void* s_ckpt_bf16 = nullptr;
+  // fp32 matrix-core kernel, dense batches: optional per-chunk factors for the
+  // backward, [B, H, NT] records of 3 C^2 + 3 C floats (M, P, Tm as C x C, the
+  // cumulative natural-log gate, gam, beta)
+  float* factors = nullptr;
   // optional packed batch: B sequences, sequence b = tokens [cu[b], cu[b+1]) of
   // the [1, T, H, *] tensors; states are [B, H, V, K]
   const int* cu_seqlens = nullptr;
