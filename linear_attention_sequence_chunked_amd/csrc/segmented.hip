@@ -216,21 +216,29 @@ int64_t fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                           int64_t cus) {
   if (B <= 0 || T <= 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0 || cus <= 0) return 0;
   if (B * H > (INT64_C(1) << 24)) return 1;  // that many streams fill the GPU by themselves
+  // Per-chunk times of the forward kernel (microseconds at 64-token chunks, from
+  // kernel traces on MI355X): with outputs 1.97 (32 value rows per workgroup) or
+  // 1.71 (16 rows); states only 1.57 or 1.40.  Each pass also runs two
+  // pipeline-fill iterations and costs about 6 us of launch; the combine 1.8 us
+  // per segment step plus its launch.
   const double scale = (double)chunk / 64.0;
-  auto pass = [&](int64_t streams, int64_t rows, int64_t nchunks) {
+  constexpr double kLaunch = 6.0;
+  auto pass = [&](int64_t streams, int64_t rows, int64_t nchunks, bool outputs) {
     if (streams > (INT64_C(1) << 24)) return 1e30;  // beyond any useful segment count
     const int vs = fwd_bf16_value_slice((int)streams, (int)H, (int)rows);
     const int64_t wgs = streams * H * ((rows + vs - 1) / vs);
     const int64_t rounds = (wgs + cus - 1) / cus;
-    return (double)rounds * (double)nchunks * (vs == 32 ? 2.2 : 1.86) * scale;
+    const double per = outputs ? (vs == 32 ? 1.97 : 1.71) : (vs == 32 ? 1.57 : 1.40);
+    return (double)rounds * (double)(nchunks + 2) * per * scale + kLaunch;
   };
   const int64_t nch = (T + chunk - 1) / chunk;
-  double best = pass(B, V, nch);
+  double best = pass(B, V, nch, true);
   int64_t best_p = 1;
   // at least four chunks per segment, at most 256 segments
   for (int64_t P = 2; P <= 256 && 4 * P <= nch; ++P) {
     const int64_t L = ((T + P - 1) / P + chunk - 1) / chunk;  // chunks per segment
-    const double t = pass(B * P, V, L) + pass(B * P, K, L) + pass(B * P, V, L) + 1.8 * (double)(P - 1);
+    const double t = pass(B * P, V, L, false) + pass(B * P, K, L, false) + pass(B * P, V, L, true) +
+                     1.8 * (double)(P - 1) + kLaunch;
     if (t < best) {
       best = t;
       best_p = P;
