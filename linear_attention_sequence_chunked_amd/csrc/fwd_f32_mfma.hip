@@ -95,22 +95,18 @@ f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
   // row-major, then the cumulative natural-log gate, gam and beta
   float* Fc = fact ? fact + (((size_t)b * H + h) * NT + c) * (3 * C * C + 3 * C) : nullptr;
 
-  // K tile to LDS (rows past the chunk end are zero)
-  for (int i = tid; i < C * (KD / 4); i += 256) {
-    const int r = i / (KD / 4), c4 = i - r * (KD / 4);
-    const f32x4 x = r < n ? ld4(k + (row0 + (size_t)r * H) * KD + 4 * c4) : zero4f();
-    st4(sKT + r * LK + 4 * c4, x);
+  // every global read of the chunk (K tile, gates, the P waves' query rows) is
+  // requested before the first LDS write
+  constexpr int NKP = C * (KD / 4), KP = (NKP + 255) / 256;
+  f32x4 kx[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const int i = min(tid + 256 * j, NKP - 1), r = i / (KD / 4), c4 = i - r * (KD / 4);
+    kx[j] = ld4(k + (row0 + (size_t)(r < n ? r : 0) * H) * KD + 4 * c4);
   }
-  // cumulative log2 gates (padded tokens add log2 1 = 0) and beta
-  if (w == 0) {
-    const bool live = lane < n;
-    const float la = live ? log2f(alpha[row0 + (size_t)lane * H]) : 0.0f;
-    const float gc = mfma::wave_scan(la, lane);
-    if (lane < C) {
-      sg[lane] = gc;
-      sb[lane] = live ? beta[row0 + (size_t)lane * H] : 0.0f;
-    }
-  }
+  const bool live = lane < n;
+  const float av = alpha[row0 + (size_t)(live ? lane : 0) * H];
+  const float bv = beta[row0 + (size_t)(live ? lane : 0) * H];
   // Gram tasks: waves 0, 1 build A, waves 2, 3 P; each takes row blocks
   // {w % 2, NB - 1 - w % 2} (two for NB = 4) so that both do 5 of the 10 blocks.
   const bool pkind = w >= 2;
@@ -125,6 +121,20 @@ f32_record_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq)
         qa[ri][kq] = ok ? ld4(q + (row0 + (size_t)r * H) * KD + 16 * kq + 4 * g) : zero4f();
+    }
+  }
+  // K tile to LDS (rows past the chunk end are zero)
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const int i = tid + 256 * j, r = i / (KD / 4), c4 = i - r * (KD / 4);
+    if (i < NKP) st4(sKT + r * LK + 4 * c4, r < n ? kx[j] : zero4f());
+  }
+  // cumulative log2 gates (padded tokens add log2 1 = 0) and beta
+  if (w == 0) {
+    const float gc = mfma::wave_scan(live ? log2f(av) : 0.0f, lane);
+    if (lane < C) {
+      sg[lane] = gc;
+      sb[lane] = live ? bv : 0.0f;
     }
   }
   __syncthreads();
