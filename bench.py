@@ -41,6 +41,38 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+# Every EVENT_EVERY-th timed launch is bracketed by its own pair of events (the
+# kernel's duration for the roofline); the others run back to back.  An event
+# pair adds two packets to the stream between launches, about 5 us per step at
+# the training shape, which is measurement, not work.
+EVENT_EVERY = 8
+
+
+def time_steps(step, steps, stream):
+    """Time `steps` calls of step(i) on `stream`: (total ms between events recorded
+    before the first and after the last call, per-launch ms of the bracketed ones)."""
+    import numpy as np
+    import torch
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    pairs = []
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        if i % EVENT_EVERY == 0:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step(i)
+            b.record(stream)
+            pairs.append((a, b))
+        else:
+            step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end), np.array([a.elapsed_time(b) for a, b in pairs])
+
+
 def measured_traffic():
     """HBM bytes per launch from the committed rocprofv3 counter record, or None
     when there is none or it was taken on different kernel sources.
@@ -331,19 +363,9 @@ def bench_decode(args):
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        step(i)
-        b.record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    ms = t0.elapsed_time(t1) / args.steps
+    total_ms, per_launch = time_steps(step, args.steps, stream)
+    kern_ms = float(per_launch.mean())
+    ms = total_ms / args.steps
     abytes = B * H * (2 * V * K * 4 + (2 * K + 2 * V) * 2 + 8)
     gbs = abytes / (kern_ms / 1e3) / 1e9
     cpub = None
@@ -420,14 +442,8 @@ def bench_varlen(args):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    total_ms, per_launch = time_steps(lambda i: step(), args.steps, stream)
+    ms = total_ms / args.steps
     abytes = T * H * 1032 + N * H * V * K * 4
     longest_chunks = -(-max(lengths) // C)
     cpub = None
@@ -563,20 +579,7 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)   # the stream the kernel is launched on
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
+    total_ms, per_launch = time_steps(step, args.steps, stream)
     ms_per_step = total_ms / args.steps
     kern_ms = float(per_launch.mean())
     pcts = {"p10": float(np.percentile(per_launch, 10)), "p50": float(np.percentile(per_launch, 50)),
@@ -657,7 +660,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel_ms": kern_ms, "kernel_ms_pct": pcts, "algorithmic_bytes": abytes,
+                     "kernel_ms": kern_ms, "kernel_ms_pct": pcts, "kernel_ms_launches": int(per_launch.size),
+                     "algorithmic_bytes": abytes,
                      "copy_gbs": copy_gbs, "frac_of_copy": achieved_gbs / copy_gbs},
         "mfma": {"tflops_algorithmic": tflops, "peak_tflops": peak,
                  "peak_dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
