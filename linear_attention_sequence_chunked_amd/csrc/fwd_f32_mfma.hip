@@ -289,7 +289,11 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
   __shared__ __attribute__((aligned(16))) Grp grp[NG];
 
   const int tid = threadIdx.x, lane = tid & 63, wg = tid >> 6;
-  const int gi = wg / NB, w = wg - gi * NB;   // group, token block
+  // group, token block.  The odd groups take their token blocks in reverse, so
+  // that the two waves of a SIMD (wave i and i + NB share one) hold blocks w and
+  // NB - 1 - w: the lower-triangular U and O products cost a block-row w wave
+  // w + 1 steps, and each SIMD then carries NB + 1 of them.
+  const int gi = wg / NB, w = (gi & 1) ? NB - 1 - (wg - gi * NB) : wg - gi * NB;
   const int s = lane & 15, g = lane >> 4;
   Grp& G = grp[gi];
   // workgroups of one (sequence, head) share an XCD (dispatch is round-robin
@@ -332,27 +336,35 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
   // key / query tiles: piece p = tid + NTH j is row p / (KD / 4), channels
   // 4 (p % (KD / 4)) .. + 3, so a wave reads whole 512-byte rows
   f32x4 kreg[PPT], qreg[PPT];
-  auto load_tiles = [&](int cc) {
+  auto tile_off = [&](int cc, int j) {
     const int n = n_of(cc);
-    const size_t r0 = row_of(cc);
+    const int p = tid + NTH * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
+    const bool ok = p < TP && r < n;
+    return (row_of(cc) + (size_t)(ok ? r : 0) * H) * KD + 4 * (ok ? c4 : 0);
+  };
+  auto load_k = [&](int cc) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) kreg[j] = ld4(k + tile_off(cc, j));
+  };
+  auto load_q = [&](int cc) {
+    if (WO)
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) qreg[j] = ld4(q + tile_off(cc, j));
+  };
+  auto stage_k = [&](int cc) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int p = tid + NTH * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
-      const bool ok = p < TP && r < n;
-      const size_t off = (r0 + (size_t)(ok ? r : 0) * H) * KD + 4 * (ok ? c4 : 0);
-      kreg[j] = ld4(k + off);
-      if (WO) qreg[j] = ld4(q + off);
+      if (p < TP) st4(sK[cc & 1] + r * LS + 4 * c4, kreg[j]);
     }
   };
-  auto stage_tiles = [&](int cc) {
+  auto stage_q = [&](int cc) {
+    if (WO)
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int p = tid + NTH * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
-      if (p < TP) {
-        st4(sK[cc & 1] + r * LS + 4 * c4, kreg[j]);
-        if (WO) st4(sQ + r * LS + 4 * c4, qreg[j]);
+      for (int j = 0; j < PPT; ++j) {
+        const int p = tid + NTH * j, r = p / (KD / 4), c4 = p - r * (KD / 4);
+        if (p < TP) st4(sQ + r * LS + 4 * c4, qreg[j]);
       }
-    }
   };
   // per-wave operands of one chunk, in two alternating sets
   struct Ops {
@@ -399,9 +411,12 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
   };
   if (nch > 0) {
-    load_tiles(0);
-    stage_tiles(0);
-    load_tiles(nch > 1 ? 1 : 0);
+    load_k(0);
+    load_q(0);
+    stage_k(0);
+    stage_q(0);
+    load_k(nch > 1 ? 1 : 0);
+    load_q(nch > 1 ? 1 : 0);
     load_ops(0, opa);
   }
   __syncthreads();
@@ -448,12 +463,17 @@ f32_chain_kernel(const float* __restrict__ q, const float* __restrict__ k,
     asm volatile("" : "+v"(Rv), "+v"(Z) : : "memory");
     if (WO && c > 0) store_o(oprev, C, false);
     st4(G.sR + s * LC + 16 * w + 4 * g, Rv);
+    // chunk c + 1's keys to the other key buffer (its last reader, chunk c - 1's
+    // state update, finished before the previous barrier) ahead of this barrier;
+    // the registers are reloaded with chunk c + 2's
+    stage_k(c + 1);
+    load_k(cn2);
     mfma::lds_barrier();
 
-    // chunk c + 1's tiles to LDS (Q(c) is dead, K(c + 1) has the other buffer);
-    // the registers are reloaded with chunk c + 2's
-    stage_tiles(c + 1);
-    load_tiles(cn2);
+    // chunk c + 1's queries to LDS (Q(c) is dead); the registers are reloaded
+    // with chunk c + 2's
+    stage_q(c + 1);
+    load_q(cn2);
 
     // U = Tm diag(beta) R' (rows of this block; lower block-triangular)
     f32x4 U = zero4f();
