@@ -35,11 +35,15 @@
 // d ln alpha_t is tiny next to those terms, and the chunk total minus a suffix
 // would lose it to rounding).
 //
-// Four launches: (1) the forward kernel of the input dtype recomputes the
+// Four steps: (1) the forward kernel of the input dtype recomputes the
 // chunk-start states into the workspace; (2a) every chunk builds its
-// state-independent factors M, P, Tm and gates in parallel; (2b) a reverse walk
-// over the chunks carries dS and stores each chunk's dS'; (3) every chunk
-// computes its token gradients independently.
+// state-independent factors M, P, Tm and gates in parallel (for float32 inputs
+// the chunk-parallel launch of (1)'s matrix-core forward writes them); (2b) a
+// reverse walk over the chunks carries dS and stores each chunk's dS'; (3)
+// every chunk computes its token gradients independently.  Float32 inputs run
+// (1), (2b) and (3) on the fp32 matrix cores (fwd_f32_mfma.hip,
+// bwd_f32_mfma.hip); bfloat16 inputs with K or V = 16 take the scalar kernels
+// of this file.
 // All arithmetic is fp32 in a fixed order (bitwise reproducible); inputs and the
 // dq, dk, dv outputs have the dtype of q.  The backward chunk is at most 32
 // tokens (chunk size changes results only by rounding).

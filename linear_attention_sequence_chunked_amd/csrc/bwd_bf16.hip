@@ -10,17 +10,17 @@
 // results are bitwise reproducible.
 //
 // Launches:
-//   (1) the bf16 forward kernel's states-only instance writes the fp32
-//       chunk-start states S_c; it runs on a second stream after (2) and beside
-//       (3), which does not need it;
+//   (1) the bf16 forward kernel's states-only instance writes the chunk-start
+//       states S_c, rounded to bf16 (the precision (4) reads them in); it runs
+//       on a second stream after (2) and beside (3), which does not need it;
 //   (2) prep, one workgroup per chunk: gates, the Gram matrices A = diag(beta) M
 //       and P, Tm = (I + A)^-1 in fp32 by 16 x 16 blocks; record = Tm, P
 //       (bf16) and the gates (fp32);
 //   (3) reverse walk, one workgroup per (stream, 32 value rows): the state
 //       gradient dS^T lives in MFMA accumulator tiles across chunks (like the
-//       forward's state); stores every chunk's end-state gradient dS'_c;
-//   (4) token gradients, one workgroup per chunk, fully parallel, after the
-//       join with (1).  The gate gradients are sums of dP o P and dA o M whose
+//       forward's state); stores every chunk's end-state gradient dS'_c (bf16);
+//   (4) token gradients, every chunk independent, after the join with (1): one
+//       persistent workgroup per CU taking the chunks in turn.  The gate gradients are sums of dP o P and dA o M whose
 //       terms cancel (strongly so for correlated keys); their P and M are
 //       recomputed here in fp32 (exact bf16 products summed in fp32, as prep
 //       forms them before rounding) rather than read back as bf16, which halves
@@ -466,9 +466,10 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 }
 
 // ===========================================================================
-// (4) token gradients: one workgroup (8 waves) per (chunk, head, batch).  The
-// value axis is walked in slices of VSL columns; dP, dA and the S / dS' parts
-// of dQ and dK accumulate in registers across slices.
+// (4) token gradients: one workgroup (8 waves) per CU, each taking (chunk, head,
+// batch) items in turn.  Per item the value axis is walked in slices of VSL
+// columns; dP, dA and the S / dS' parts of dQ and dK accumulate in registers
+// across slices.
 template <int KD, int VD>
 struct alignas(16) LocalSmem {
   static constexpr int VSL = 32;                    // value slice
