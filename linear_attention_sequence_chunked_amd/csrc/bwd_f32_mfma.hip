@@ -189,8 +189,16 @@ f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
     st4(G.sdR + s * LC + 16 * w + 4 * g, -(ld4(rc + Rec<C>::kGam + 16 * w + 4 * g) * dR));
     mfma::lds_barrier();
 
-    // dS'^T <- gam_n dS'^T + Q^T diag(gam) dO + K^T (-beta gam dR), owned tiles
+    // dS'^T <- gam_n dS'^T + Q^T diag(gam) dO + K^T (-beta gam dR), owned tiles;
+    // the right operands are the same for every tile, so they are read once, and
+    // the new tiles go to LDS after all of the products
     const float gn = rc[Rec<C>::kGn];
+    f32x4 gdv[NB], drv[NB];
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      gdv[J] = ld4(dot + s * LC + 16 * J + 4 * g) * ld4(rc + Rec<C>::kGam + 16 * J + 4 * g);
+      drv[J] = ld4(G.sdR + s * LC + 16 * J + 4 * g);
+    }
 #pragma unroll
     for (int m = 0; m < NKT; ++m) {
       const int kap = w + NB * m;
@@ -204,12 +212,15 @@ f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
           aq[e] = qt[(16 * J + 4 * g + e) * LS + 16 * kap + s];
           ak[e] = kt[(16 * J + 4 * g + e) * LS + 16 * kap + s];
         }
-        const f32x4 gd = ld4(dot + s * LC + 16 * J + 4 * g) * ld4(rc + Rec<C>::kGam + 16 * J + 4 * g);
-        acc = mma16(aq, gd, acc);
-        acc = mma16(ak, ld4(G.sdR + s * LC + 16 * J + 4 * g), acc);
+        acc = mma16(aq, gdv[J], acc);
+        acc = mma16(ak, drv[J], acc);
       }
       S[m] = acc;
-      st4(G.sS + s * LS + 16 * kap + 4 * g, acc);
+    }
+#pragma unroll
+    for (int m = 0; m < NKT; ++m) {
+      const int kap = w + NB * m;
+      if (kap < KQ) st4(G.sS + s * LS + 16 * kap + 4 * g, S[m]);
     }
     mfma::lds_barrier();
   }
