@@ -514,6 +514,17 @@ f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // the round's slices, for the key-channel tiles this wave owns
     for (int x = 0; x < NW && sl0 + x < nsl; ++x) {
       const WaveArea& X = area.wave[x];
+      // the slice's S and dS' columns of the owned tiles serve every token block
+      f32x4 bs[NKO], bd[NKO];
+#pragma unroll
+      for (int m = 0; m < NKO; ++m) {
+        const int kq = min(w + NW * m, KQ - 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bs[m][e] = X.S[(4 * g + e) * LK + 16 * kq + s];
+          bd[m][e] = X.dS[(4 * g + e) * LK + 16 * kq + s];
+        }
+      }
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         const int r = 16 * I + s;
@@ -522,16 +533,9 @@ f32_local_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const f32x4 ar = ld4(X.dR + r * LV + 4 * g) * (-sb[r] * sgam[r]);
 #pragma unroll
         for (int m = 0; m < NKO; ++m) {
-          const int kq = w + NW * m;
-          if (kq < KQ) {
-            f32x4 bs, bd;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              bs[e] = X.S[(4 * g + e) * LK + 16 * kq + s];
-              bd[e] = X.dS[(4 * g + e) * LK + 16 * kq + s];
-            }
-            aQ[I][m] = mma16(ao, bs, aQ[I][m]);
-            aK[I][m] = mma16(ar, bs, mma16(au, bd, aK[I][m]));
+          if (w + NW * m < KQ) {
+            aQ[I][m] = mma16(ao, bs[m], aQ[I][m]);
+            aK[I][m] = mma16(ar, bs[m], mma16(au, bd[m], aK[I][m]));
           }
         }
       }
