@@ -9,33 +9,35 @@
 // fp32.  Each output element has one writer and every sum a fixed order, so
 // results are bitwise reproducible.
 //
-// Launches:
-//   (1) the bf16 forward kernel's states-only instance writes the chunk-start
-//       states S_c, rounded to bf16 (the precision (4) reads them in); it runs
-//       on a second stream after (2) and beside (3), which does not need it;
-//   (2) prep, one workgroup per chunk: gates, the Gram matrices A = diag(beta) M
+// Launches, all on the caller's stream:
+//   (1) prep, one workgroup per chunk: gates, the Gram matrices A = diag(beta) M
 //       and P, Tm = (I + A)^-1 in fp32 by 16 x 16 blocks; record = Tm, P
 //       (bf16) and the gates (fp32);
-//   (3) reverse walk, one workgroup per (stream, 32 value rows): the state
-//       gradient dS^T lives in MFMA accumulator tiles across chunks (like the
-//       forward's state); stores every chunk's end-state gradient dS'_c (bf16);
-//   (4) token gradients, every chunk independent, after the join with (1): one
-//       persistent workgroup per CU taking the chunks in turn.  The gate gradients are sums of dP o P and dA o M whose
-//       terms cancel (strongly so for correlated keys); their P and M are
-//       recomputed here in fp32 (exact bf16 products summed in fp32, as prep
-//       forms them before rounding) rather than read back as bf16, which halves
-//       the error of dalpha in that regime.
+//   (2) the two sequential walks, one launch, one workgroup per CU:
+//       - the reverse walk, one workgroup per (stream, 32 value rows): the state
+//         gradient dS^T lives in MFMA accumulator tiles across chunks (like the
+//         forward's state); stores every chunk's end-state gradient dS'_c (bf16);
+//       - the bf16 forward kernel's states-only body (fwd_bf16_kernel.h), one
+//         workgroup per (stream, 32 value rows): the chunk-start states S_c,
+//         rounded to bf16 (the precision (3) reads them in);
+//   (3) token gradients, every chunk independent: one persistent workgroup per
+//       CU taking the chunks in turn.  The gate gradients are sums of dP o P and
+//       dA o M whose terms cancel (strongly so for correlated keys); their P and
+//       M are recomputed here in fp32 (exact bf16 products summed in fp32, as
+//       prep forms them before rounding) rather than read back as bf16, which
+//       halves the error of dalpha in that regime.
 //
-// Layout conventions of the products in (4): quantities with a token axis and
+// Layout conventions of the products in (3): quantities with a token axis and
 // a value or channel axis are computed transposed (accumulator rows = value or
 // channel, columns = tokens), so per-token scalars are one value per lane and
 // the tiles go to LDS as row-major [token][*] with 8-byte writes; an operand
 // whose contraction runs over tokens is then read from such an array with
 // transpose reads.
+#include "fwd_bf16_kernel.h"
 #include "launch.h"
 #include "mfma_common.h"
 
-#include <mutex>
+#include <atomic>
 #include <type_traits>
 
 namespace gdn {
@@ -67,7 +69,7 @@ __device__ __forceinline__ void store_bf4(bf16* p, f32x4 d) {
 }
 
 // ===========================================================================
-// (2) prep: one workgroup (4 waves) per (chunk, head, batch).
+// (1) prep: one workgroup (4 waves) per (chunk, head, batch).
 // The key and query tiles are dead once the Gram is built, so Tm takes their
 // place: 53 KB at K = 128, three workgroups per CU.
 template <int KD>
@@ -236,9 +238,9 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 }
 
 // ===========================================================================
-// (3) reverse walk: one workgroup per (32 value rows, head, batch).  Waves 0
+// (2) reverse walk: one workgroup per (32 value rows, head, batch).  Waves 0
 // and 1 carry dS^T for rows v0 + 16 w .. + 15 (tile cb: lane (g, s) holds
-// dS[v0 + 16 w + s][16 cb + 4g + e]); waves 2 and 3 stage the next chunk (in
+// dS[v0 + 16 w + s][16 cb + 4g + e]); the staging waves load the next chunk (in
 // reverse order) into the other LDS slot.
 // Per chunk with dS' the gradient of the chunk-end state:
 //   W = K dS'^T,  dU = diag(D) W + P^T dO,  dR = Tm^T dU,
@@ -255,16 +257,19 @@ struct alignas(16) WalkSlot {
   float gamn[4];
 };
 
-template <int KD>
-__global__ void __launch_bounds__(256)
-bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                    const bf16* __restrict__ d_o, const float* __restrict__ d_sfinal,
-                    float* __restrict__ d_s0, const unsigned char* __restrict__ rec,
-                    bf16* __restrict__ ws_dS, int T, int H, int V) {
+// The walk for one (32 value rows, head, batch) item, bid of nblk: waves 0 and 1
+// carry the state gradient, the next NSW waves stage the chunks, and any further
+// waves only keep the barrier count (every wave reaches each barrier).
+template <int KD, int NSW>
+__device__ __forceinline__ void
+dstate_body(WalkSlot<KD>* slot, const int bid, const int nblk,
+            const bf16* __restrict__ q, const bf16* __restrict__ k,
+            const bf16* __restrict__ d_o, const float* __restrict__ d_sfinal,
+            float* __restrict__ d_s0, const unsigned char* __restrict__ rec,
+            bf16* __restrict__ ws_dS, int T, int H, int V) {
   using SL = WalkSlot<KD>;
   constexpr int LDK = SL::LDK;
   constexpr int KS = KD / 32, NCB = KD / 16;
-  __shared__ SL slot[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ls = lane & 15, lg = lane >> 4;
@@ -272,9 +277,8 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // workgroup ids go to different XCDs, so the value slices of one (batch, head),
   // which read the same keys, queries and records, get ids equal modulo 8 (same
   // XCD, shared L2)
-  int item = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  int item = bid;
+  if ((nblk & 7) == 0) item = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int nsl = V / 32, bh = item / nsl;
   const int v0 = (item - bh * nsl) * 32, h = bh % H, b = bh / H;
   const int NT = (T + kC - 1) / kC;
@@ -354,25 +358,26 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
         *reinterpret_cast<f32x4*>(&d_s0[sbase + (size_t)ls * KD + 16 * cb + 4 * lg]) = dS[cb];
-  } else {
+  } else if (wave < 2 + NSW) {
     // ============================= staging waves =============================
     // Chunk c is loaded into registers two iterations before it is written to
     // LDS, in one of two register sets (alternating; the loop is unrolled by
-    // two so that each set keeps its registers); 128 staging lanes.  Every load
-    // is unconditional (past the end of the sequence a row reads the chunk's
-    // first row, past the first chunk the load repeats chunk 0) and the values
-    // are zeroed where needed only when staged, so the wait before staging a
-    // set leaves the other set's loads in flight.
-    constexpr int NSL = 128;
+    // two so that each set keeps its registers); 64 NSW staging lanes.  Every
+    // load is unconditional (past the end of the sequence a row reads the
+    // chunk's first row, past the first chunk the load repeats chunk 0) and the
+    // values are zeroed where needed only when staged, so the wait before
+    // staging a set leaves the other set's loads in flight.
+    constexpr int NSL = 64 * NSW;
     constexpr int NKP = kC * KD / 8;              // 16-byte pieces of a key tile
     constexpr int KPL = NKP / NSL;
     constexpr int NMP = kC * kC / 8;              // pieces of a C x C tile
     constexpr int MPL = NMP / NSL;
-    static_assert(NKP % NSL == 0 && NMP % NSL == 0, "staging pieces");
+    constexpr int DPL = kC * 4 / NSL;             // dO pieces (token, 8 values)
+    static_assert(NKP % NSL == 0 && NMP % NSL == 0 && kC * 4 % NSL == 0, "staging pieces");
     const int sl = tid - 128;
     struct Regs {
-      bf16x8 k[KPL], q[KPL], tm[MPL], p[MPL], dof[2];
-      float g[2], gl, gn, bt;
+      bf16x8 k[KPL], q[KPL], tm[MPL], p[MPL], dof[DPL];
+      float g[DPL], gl, gn, bt;
     };
     auto load = [&](int c, Regs& R) {
       c = c > 0 ? c : 0;
@@ -391,9 +396,9 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         R.tm[j] = *reinterpret_cast<const bf16x8*>(rc + kRecTm + 16 * p);
         R.p[j] = *reinterpret_cast<const bf16x8*>(rc + kRecP + 16 * p);
       }
-      // dO pieces: piece p = sl + 128 j is token p / 4, values 8 (p % 4) .. + 7
+      // dO pieces: piece p = sl + NSL j is token p / 4, values 8 (p % 4) .. + 7
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < DPL; ++j) {
         const int p = sl + NSL * j, dr = p >> 2;
         R.dof[j] = *reinterpret_cast<const bf16x8*>(
             d_o + ((size_t)b * T + t0 + (dr < n ? dr : 0)) * tokv + (size_t)h * V + v0 + 8 * (p & 3));
@@ -425,7 +430,7 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         *reinterpret_cast<bf16x8*>(&s.p[r * kLDC + c8]) = R.p[j];
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < DPL; ++j) {
         const int p = sl + NSL * j, dr = p >> 2, c8 = 8 * (p & 3);
         const bf16x8 dof = dr < n ? R.dof[j] : zero8();
         const float gm = __builtin_amdgcn_exp2f(R.g[j]);
@@ -462,11 +467,42 @@ bwd16_dstate_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     if (j <= NT - 1) step(j, R1);
     lds_barrier();   // the chain's last chunk
+  } else {
+    // ========================= barrier-only waves =========================
+    for (int c = NT - 1; c >= 0; --c) lds_barrier();
   }
 }
 
+// (2) both sequential walks of the backward in one launch (neither needs the
+// other): workgroups [0, nwalk) run the reverse walk above (waves 2-5 stage,
+// 6-7 only keep the barrier count), the rest the forward kernel's states-only
+// body with 32 value rows (the chunk-start states, rounded to bf16).  One
+// workgroup per CU either way (their LDS is one union).  When nwalk is a
+// multiple of 8 both halves keep their XCD-aware numbering (id mod 8 is the
+// XCD).
+template <int KD>
+__global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd16_walks_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                   const bf16* __restrict__ d_o, const float* __restrict__ alpha,
+                   const float* __restrict__ beta, const float* __restrict__ s0,
+                   const float* __restrict__ d_sfinal, float* __restrict__ d_s0,
+                   const unsigned char* __restrict__ rec, bf16* __restrict__ ws_S,
+                   bf16* __restrict__ ws_dS, int T, int H, int V, int nwalk) {
+  __shared__ union {
+    WalkSlot<KD> slot[2];
+    Smem<KD, 32, 64> fwd;
+  } u;
+  const int bid = blockIdx.x;
+  if (bid < nwalk)
+    dstate_body<KD, 4>(u.slot, bid, nwalk, q, k, d_o, d_sfinal, d_s0, rec, ws_dS, T, H, V);
+  else
+    fwd_bf16_body<KD, 32, 64, false>(u.fwd, bid - nwalk, (int)gridDim.x - nwalk, q, k, v, alpha, beta,
+                                     s0, nullptr, nullptr, nullptr, ws_S, nullptr, T, H, KD, V, kC,
+                                     V / 32);
+}
+
 // ===========================================================================
-// (4) token gradients: one workgroup (8 waves) per CU, each taking (chunk, head,
+// (3) token gradients: one workgroup (8 waves) per CU, each taking (chunk, head,
 // batch) items in turn.  Per item the value axis is walked in slices of VSL
 // columns; dP, dA and the S / dS' parts of dQ and dK accumulate in registers
 // across slices.
@@ -985,54 +1021,32 @@ size_t bwd_bf16_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int6
 
 namespace {
 
-// A second stream per device, created on first use and kept for the life of the
-// process, with the two events of a fork / join.  The chunk-start states and the
-// reverse walk are independent sequential walks of 96 workgroups each; run side
-// by side they share the chip instead of taking turns.  The device is the one
-// the caller's stream belongs to; each device has its own lock, held while a call
-// creates its side stream or enqueues its fork / join sequence (the events are
-// reused by every call on that device).
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-  int cus = 0;   // compute units of the device (0: not queried yet)
-  std::mutex mu;
-};
+// Compute units of the device a stream belongs to (the persistent token-gradient
+// grid is one workgroup per CU), queried once per device and cached; 256 (an
+// MI355X) if the query fails.
 constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
 
-int stream_device(hipStream_t stream) {
+int device_cus(hipStream_t stream) {
   int dev = -1;
   if (stream) {
     hipDevice_t d;
-    if (hipStreamGetDevice(stream, &d) != hipSuccess) return -1;
-    dev = static_cast<int>(d);
+    if (hipStreamGetDevice(stream, &d) == hipSuccess) dev = static_cast<int>(d);
   } else if (hipGetDevice(&dev) != hipSuccess) {
-    return -1;
+    dev = -1;
   }
-  return dev >= 0 && dev < kMaxDevices ? dev : -1;
-}
-
-// Called with g_side[dev].mu held.  The stream and events are created on `dev`
-// (made current for the creation, the caller's current device restored after).
-SideStream* side_stream(int dev) {
-  if (dev < 0) return nullptr;
-  SideStream& sd = g_side[dev];
-  if (!sd.s && !sd.failed) {
-    int cur = -1;
-    bool ok = hipGetDevice(&cur) == hipSuccess && (cur == dev || hipSetDevice(dev) == hipSuccess);
-    ok = ok && hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess &&
-         hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) == hipSuccess &&
-         hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) == hipSuccess;
-    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
-    if (!ok) {
-      sd.failed = true;   // keep going on the caller's stream alone
-      (void)hipGetLastError();
-      return nullptr;
-    }
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return sd.failed ? nullptr : &sd;
+  int nc = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      nc <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev < kMaxDevices) g_cus[dev].store(nc, std::memory_order_relaxed);
+  return nc;
 }
 
 }  // namespace
@@ -1044,65 +1058,26 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   bf16* ws_S = reinterpret_cast<bf16*>(a.workspace);
   bf16* ws_dS = ws_S + (size_t)a.B * a.H * NT * a.V * a.K;
   unsigned char* rec = reinterpret_cast<unsigned char*>(ws_dS + (size_t)a.B * a.H * NT * a.V * a.K);
-  // (1) chunk-start states (launched after prep, below)
-  FwdArgs f;
-  f.q = a.q;
-  f.k = a.k;
-  f.v = a.v;
-  f.alpha = a.alpha;
-  f.beta = a.beta;
-  f.s0 = a.s0;
-  f.o = nullptr;
-  f.s_final = nullptr;
-  f.B = a.B;
-  f.T = a.T;
-  f.H = a.H;
-  f.K = a.K;
-  f.V = a.V;
-  f.chunk = kC;
-  f.vs = 32;
-  f.s_ckpt_bf16 = ws_S;
-  const int dev = stream_device(stream);
-  std::unique_lock<std::mutex> lock;
-  if (dev >= 0) lock = std::unique_lock<std::mutex>(g_side[dev].mu);
-  SideStream* sd = side_stream(dev);
   const bf16* q = static_cast<const bf16*>(a.q);
   const bf16* k = static_cast<const bf16*>(a.k);
   const bf16* v = static_cast<const bf16*>(a.v);
   const bf16* d_o = static_cast<const bf16*>(a.d_o);
-  int cus = dev >= 0 ? g_side[dev].cus : 0;
-  if (cus <= 0) {
-    int d = dev, nc = 0;
-    if ((d >= 0 || hipGetDevice(&d) == hipSuccess) &&
-        hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, d) == hipSuccess && nc > 0) {
-      cus = nc;
-      if (dev >= 0) g_side[dev].cus = nc;   // under the device's lock
-    } else {
-      cus = 256;
-    }
-  }
+  const int cus = device_cus(stream);
   const long items_local = (long)NT * a.H * a.B;
   const int grid_local = (int)(items_local < cus ? items_local : cus);
   auto run = [&](auto kc) -> hipError_t {
     constexpr int KD = decltype(kc)::value;
-    // (2) prep first, with the whole GPU; then (1) on the side stream beside (3):
-    // the two long walks have one workgroup per CU each and fit side by side
+    // the records first, with the whole GPU; then the two sequential walks in
+    // one launch (one workgroup per CU each, side by side); then the token
+    // gradients.  All three on the caller's stream.
     hipLaunchKernelGGL((bwd16_prep_kernel<KD>), dim3(NT * a.H * a.B), dim3(256), 0, stream, q, k, a.alpha,
                        a.beta, rec, a.T, a.H);
     hipError_t r;
     if ((r = hipGetLastError()) != hipSuccess) return r;
-    hipStream_t st_states = stream;
-    if (sd) {
-      if ((r = hipEventRecord(sd->fork, stream)) != hipSuccess) return r;
-      if ((r = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return r;
-      st_states = sd->s;
-    }
-    if ((r = launch_fwd_bf16(f, st_states)) != hipSuccess) return r;
-    if (sd && (r = hipEventRecord(sd->join, sd->s)) != hipSuccess) return r;
-    hipLaunchKernelGGL((bwd16_dstate_kernel<KD>), dim3(a.B * a.H * (a.V / 32)), dim3(256), 0, stream, q, k,
-                       d_o, a.d_sfinal, a.d_s0, rec, ws_dS, a.T, a.H, a.V);
+    const int nwalk = a.B * a.H * (a.V / 32);
+    hipLaunchKernelGGL((bwd16_walks_kernel<KD>), dim3(2 * nwalk), dim3(512), 0, stream, q, k, v, d_o,
+                       a.alpha, a.beta, a.s0, a.d_sfinal, a.d_s0, rec, ws_S, ws_dS, a.T, a.H, a.V, nwalk);
     if ((r = hipGetLastError()) != hipSuccess) return r;
-    if (sd && (r = hipStreamWaitEvent(stream, sd->join, 0)) != hipSuccess) return r;   // states ready
     auto local = [&](auto vc) -> hipError_t {
       constexpr int VD = decltype(vc)::value;
       // one workgroup per CU (the kernel's LDS allows no more), each walking
