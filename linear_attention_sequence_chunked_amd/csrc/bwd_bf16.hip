@@ -70,8 +70,10 @@ __device__ __forceinline__ void store_bf4(bf16* p, f32x4 d) {
 
 // ===========================================================================
 // (1) prep: one workgroup (4 waves) per (chunk, head, batch).
-// The key and query tiles are dead once the Gram is built, so Tm takes their
-// place: 53 KB at K = 128, three workgroups per CU.
+// The key and query tiles are dead once the Gram is built, so A and Tm take
+// their place (A is held in registers until every wave is done with the
+// tiles): 36.5 KB at K = 128, so that three workgroups fit in a CU (768 chunks
+// in one round on 256 CUs).
 template <int KD>
 struct alignas(16) PrepSmem {
   static constexpr int LDK = KD + 16;   // 32 bytes modulo 64: conflict-free fragment reads
@@ -79,9 +81,11 @@ struct alignas(16) PrepSmem {
     struct {
       bf16 k[kC * LDK], q[kC * LDK];   // [token][channel], read by the Gram only
     } in;
-    float x[kC][kC + 4];             // Tm (lower); upper blocks hold level scratch
+    struct {
+      float x[kC][kC + 4];   // Tm (lower); upper blocks hold level scratch
+      float a[kC][kC + 4];   // A = diag(beta) M, strictly lower
+    } s;
   } u;
-  float a[kC][kC + 4];             // A = diag(beta) M, strictly lower
   float g[kC], bt[kC];
 };
 
@@ -142,20 +146,37 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     reinterpret_cast<float*>(dst + kRecG)[lane] = g;
     reinterpret_cast<float*>(dst + kRecB)[lane] = bt;
   }
-  __syncthreads();
+  lds_barrier();
 
   // Gram tiles, balanced over the waves: waves 0 and 1 build A for token-block
   // rows {0, 3} and {1, 2}, waves 2 and 3 build P for the same rows (five tiles
-  // each).  A (strict) goes to fp32 LDS, P to the record;
+  // each).  P goes to the record, A (strict) to fp32 LDS over the dead key and
+  // query tiles once every wave has passed the barrier after the products;
   // the tiles above the diagonal are written as zeros.
   const int ls = lane & 15, lg = lane >> 4;
   {
     const bool isP = wave >= 2;
     const int ra = (wave & 1) ? 1 : 0, rb = (wave & 1) ? 2 : 3;
     const bf16* ab = isP ? sm.u.in.q : sm.u.in.k;
+    // the lane's gates, read once: rows 16 w + 4 lg + e of its two token-block
+    // rows, columns 16 tc + ls (no LDS read waits inside the element loop)
+    float gr[2][4], br[2][4], gc[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int w = half == 0 ? ra : rb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gr[half][e] = sm.g[16 * w + 4 * lg + e];
+        br[half][e] = sm.bt[16 * w + 4 * lg + e];
+      }
+    }
+#pragma unroll
+    for (int tc = 0; tc < 4; ++tc) gc[tc] = sm.g[16 * tc + ls];
+    float av[2][4][4];   // decayed Gram entries: P, or A = diag(beta) M
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int w = half == 0 ? ra : rb;   // token-block row
+#pragma unroll
       for (int tc = 0; tc < 4; ++tc) {
         f32x4 acc = zero4();
         if (tc <= w) {
@@ -165,22 +186,37 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
         // accumulator: row r = 16 w + 4 lg + e, column i = 16 tc + ls
         const int i = 16 * tc + ls;
-        const float gi = sm.g[i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * w + 4 * lg + e;
-          const float dec = __builtin_amdgcn_exp2f(i <= r ? sm.g[r] - gi : -INFINITY);
-          if (isP) {
-            rp[r * kC + i] = (bf16)(dec * acc[e]);
-          } else {
-            const float m = i < r ? dec * acc[e] : 0.0f;
-            sm.a[r][i] = sm.bt[r] * m;
-          }
+          const float dec = __builtin_amdgcn_exp2f(i <= r ? gr[half][e] - gc[tc] : -INFINITY);
+          av[half][tc][e] = isP ? dec * acc[e] : br[half][e] * (i < r ? dec * acc[e] : 0.0f);
         }
       }
     }
+    if (isP) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int w = half == 0 ? ra : rb;
+#pragma unroll
+        for (int tc = 0; tc < 4; ++tc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rp[(16 * w + 4 * lg + e) * kC + 16 * tc + ls] = (bf16)av[half][tc][e];
+      }
+    }
+    lds_barrier();   // the key and query tiles are dead
+    if (!isP) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int w = half == 0 ? ra : rb;
+#pragma unroll
+        for (int tc = 0; tc < 4; ++tc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.u.s.a[16 * w + 4 * lg + e][16 * tc + ls] = av[half][tc][e];
+      }
+    }
   }
-  __syncthreads();
+  lds_barrier();
 
   // Tm = (I + A)^-1 in fp32, by 16 x 16 blocks.
   // Diagonal blocks by forward substitution, one lane per (block, column):
@@ -188,18 +224,29 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   if (wave == 0) {
     const int bb = lg, j = 16 * bb + ls;
     float xv[16];
+    // the block's rows as four 16-byte reads each, row r + 1 requested while
+    // row r is substituted
+    auto row = [&](int r, f32x4 (&dst)[4]) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) dst[m] = *reinterpret_cast<const f32x4*>(&sm.u.s.a[16 * bb + r][16 * bb + 4 * m]);
+    };
+    f32x4 ra0[4], ra1[4];
+    row(1, ra1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      f32x4 (&cur)[4] = (r & 1) ? ra1 : ra0;
+      f32x4 (&nxt)[4] = (r & 1) ? ra0 : ra1;
+      if (r >= 1 && r + 1 < 16) row(r + 1, nxt);
       const int rr = 16 * bb + r;
       float s = 0.0f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s = fmaf(sm.a[rr][16 * bb + i], xv[i], s);
+      for (int i = 0; i < r; ++i) s = fmaf(cur[i >> 2][i & 3], xv[i], s);
       xv[r] = rr < j ? 0.0f : (rr == j ? 1.0f : -s);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sm.u.x[16 * bb + r][j] = xv[r];
+    for (int r = 0; r < 16; ++r) sm.u.s.x[16 * bb + r][j] = xv[r];
   }
-  __syncthreads();
+  lds_barrier();
   // Off-diagonal blocks by levels d = i - j: X_ij = -T_ii (sum_{j <= m < i} A_im T_mj),
   // in fp32 on the matrix cores (16 x 16 x 4 per instruction: lane (s, g) gives
   // the left operand's row s and the right operand's column s at reduction index
@@ -212,27 +259,27 @@ bwd16_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const int j = wave, i = wave + d;
       f32x4 x = zero4();
       for (int m0 = 16 * j; m0 < 16 * i; m0 += 4)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.a[16 * i + ls][m0 + lg], sm.u.x[m0 + lg][16 * j + ls], x,
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.s.a[16 * i + ls][m0 + lg], sm.u.s.x[m0 + lg][16 * j + ls], x,
                                                  0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.u.x[16 * j + 4 * lg + e][16 * i + ls] = x[e];
+      for (int e = 0; e < 4; ++e) sm.u.s.x[16 * j + 4 * lg + e][16 * i + ls] = x[e];
       // T_ii is lower triangular: its upper entries are zeros
       f32x4 y = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < 16; k0 += 4)
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.x[16 * i + ls][16 * i + k0 + lg],
-                                                 sm.u.x[16 * j + k0 + lg][16 * i + ls], y, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.s.x[16 * i + ls][16 * i + k0 + lg],
+                                                 sm.u.s.x[16 * j + k0 + lg][16 * i + ls], y, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.u.x[16 * i + 4 * lg + e][16 * j + ls] = -y[e];
+      for (int e = 0; e < 4; ++e) sm.u.s.x[16 * i + 4 * lg + e][16 * j + ls] = -y[e];
     }
-    __syncthreads();
+    lds_barrier();
   }
   // Tm to the record as bf16, zeros above the diagonal
   for (int p = tid; p < kC * kC / 8; p += 256) {
     const int r = p / (kC / 8), c8 = (p % (kC / 8)) * 8;
     float xr[8];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) xr[jj] = c8 + jj <= r ? sm.u.x[r][c8 + jj] : 0.0f;
+    for (int jj = 0; jj < 8; ++jj) xr[jj] = c8 + jj <= r ? sm.u.s.x[r][c8 + jj] : 0.0f;
     *reinterpret_cast<bf16x8*>(rtm + 8 * p) = to_bf8(xr);
   }
 }
