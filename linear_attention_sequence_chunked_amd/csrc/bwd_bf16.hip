@@ -572,7 +572,8 @@ struct alignas(16) LocalSmem {
       float xp[kC][kC + 4], xa[kC][kC + 4]; // dP o P and dA o M, [row][col]
     } fin;
   } u;
-  float g[kC], bt[kC];
+  alignas(16) float g[kC];
+  float bt[kC];
   float red[4][16][16];                // per-token row sums of the slice tiles
   float dgs[kC], dbs[kC], dus[kC];     // per-token gate gradients, D_r U_r.W_r
   float dot[8];                        // <dS', S> partials per wave
@@ -915,6 +916,9 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         // lane: i = 16 ibk + 4 lg + e, r = 16 rbk + ls
         const int r = 16 * rbk + ls;
         const float gr = sm.g[r], br = sm.bt[r];
+        // gates of the lane's four i, read before the products (no LDS waits
+        // inside the element loop)
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(&sm.g[16 * ibk + 4 * lg]);
         // Gram tile in the same layout: G[i][r] = k_i . q_r (dP jobs) or
         // k_i . k_r (dA jobs), exact bf16 products summed in fp32
         const bf16* gsrc = j < 10 ? sm.q : sm.k;
@@ -927,7 +931,7 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 16 * ibk + 4 * lg + e;
-            const float ee = __builtin_amdgcn_exp2f(i <= r ? gr - sm.g[i] : -INFINITY);
+            const float ee = __builtin_amdgcn_exp2f(i <= r ? gr - gi[e] : -INFINITY);
             const float dp = i <= r ? pa[u][e] : 0.0f;
             val[e] = dp * ee;
             prod[e] = dp * (ee * gram[e]);   // dP o P, P = E o (Q K^T)
@@ -938,7 +942,7 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 16 * ibk + 4 * lg + e;
-            const float ee = __builtin_amdgcn_exp2f(i < r ? gr - sm.g[i] : -INFINITY);
+            const float ee = __builtin_amdgcn_exp2f(i < r ? gr - gi[e] : -INFINITY);
             const float da = i < r ? -pa[u][e] : 0.0f;
             val[e] = da * br * ee;
             prod[e] = da * (ee * gram[e]);   // dA o M, M = E o (K K^T), strictly lower
@@ -985,13 +989,29 @@ bwd16_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     {
       const int r = tid >> 3, q8 = tid & 7;
       float sp = 0.0f, sa = 0.0f, cp = 0.0f, ca = 0.0f;
-      for (int i = q8; i < r; i += 8) {
-        sp += sm.u.fin.xp[r][i];
-        sa += sm.u.fin.xa[r][i];
+      // row sums over i = q8 + 8 m < r, column sums over rr = rr0 + 8 m < C: all
+      // reads issued first (clamped indices), then added in order where valid
+      const int rr0 = r + 1 + ((q8 - r - 1) & 7);
+      float vxp[8], vxa[8], wxp[8], wxa[8], wbt[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int i = min(q8 + 8 * m, kC - 1), rr = min(rr0 + 8 * m, kC - 1);
+        vxp[m] = sm.u.fin.xp[r][i];
+        vxa[m] = sm.u.fin.xa[r][i];
+        wxp[m] = sm.u.fin.xp[rr][r];
+        wxa[m] = sm.u.fin.xa[rr][r];
+        wbt[m] = sm.bt[rr];
       }
-      for (int rr = r + 1 + ((q8 - r - 1) & 7); rr < kC; rr += 8) {
-        cp += sm.u.fin.xp[rr][r];
-        ca += sm.bt[rr] * sm.u.fin.xa[rr][r];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (q8 + 8 * m < r) {
+          sp += vxp[m];
+          sa += vxa[m];
+        }
+        if (rr0 + 8 * m < kC) {
+          cp += wxp[m];
+          ca += wbt[m] * wxa[m];
+        }
       }
 #pragma unroll
       for (int m = 1; m < 8; m <<= 1) {
