@@ -159,6 +159,14 @@ def test_bwd_mfma_more_chunks_than_compute_units():
     check(inp, 64, TOL[torch.bfloat16], "more chunks than CUs")
 
 
+def test_bwd_mfma_walks_exceed_compute_units():
+    # the two sequential walks share one launch of 2 x B*H*V/32 workgroups: here
+    # 2 x 138 = 276 > 256 CUs (some wait for a free CU) and 138 is not a multiple
+    # of 8 (neither half uses the XCD-aware numbering)
+    inp = make_inputs(3, 150, 23, 64, 64, dtype=torch.bfloat16, seed=655, s0_std=0.05, with_do=True)
+    check(inp, 64, TOL[torch.bfloat16], "walks launch larger than the GPU")
+
+
 def test_bwd_writes_preallocated_results():
     inp = make_inputs(2, 150, 2, 64, 32, dtype=torch.bfloat16, seed=660, s0_std=0.05, with_do=True)
     g = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
