@@ -18,6 +18,17 @@ constexpr int kThreads = 64 * kWaves;
 // Ragged batches of up to this many sequences start their longest sequences first.
 constexpr int kLongestFirstMax = 128;
 
+// Row stride (elements) of the CP x CP bf16 tiles P^T and Tm^T.  At CP = 64,
+// 160-byte rows: the 8-byte transposed accumulator stores of a 16 x 16 tile then
+// take fewer LDS cycles than at 144 bytes (rows stay 16-byte aligned for the
+// diagonal blocks' 16-byte row writes).
+__host__ __device__ constexpr int tile_ld(int cp) { return cp == 64 ? cp + 16 : cp + 8; }
+
+// The fp32 diagonal A blocks are stored transposed, 16 floats per row, with the
+// four 16-byte quads of row c rotated by c / 4: quad u of row c sits at
+// ad_quad(u, c).  The 16 lanes of one store then cover all 64 banks.
+__host__ __device__ constexpr int ad_quad(int u, int c) { return 4 * ((u + (c >> 2)) & 3); }
+
 template <int KD, int VS, int CP>
 struct alignas(16) Smem {
   static constexpr int NTB = CP / 16;
@@ -25,7 +36,7 @@ struct alignas(16) Smem {
   // keeps the 16-byte fragment reads (lanes 0-7 and 16-23 served together, rows
   // s and pieces g) on distinct banks: 2x the read rate of an 8-element pad
   static constexpr int LDK = KD + 16;
-  static constexpr int LDC = CP + 8;   // CP x CP tiles
+  static constexpr int LDC = tile_ld(CP);  // CP x CP tiles
   static constexpr int LDA = 24;       // packed 16-wide A^T blocks
   static constexpr int APK = (NTB == 4 ? 96 : 16) * LDA;
   bf16 k[3][CP * LDK];                 // keys [token][channel], padded rows
@@ -66,7 +77,7 @@ struct alignas(16) Smem {
 template <int CP>
 __device__ __forceinline__ void levels_part(bf16* tt, const bf16* ap, int lane, int part) {
   constexpr int NTB = CP / 16;
-  constexpr int LDC = CP + 8, LDA = 24;
+  constexpr int LDC = tile_ld(CP), LDA = 24;
   if constexpr (NTB == 4) {
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
@@ -178,7 +189,7 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
   if (DP) pw = pin(lds(sm.pt[c % 2]) + ls * LDC + 4 * lg);
   if (DA) {
     aw = pin(lds(sm.ap[c % 2]) + ls * LDA + 4 * lg);
-    adw = pin(lds(sm.ad) + ls * 16 + 4 * lg);
+    adw = pin(lds(sm.ad) + ls * 16 + ad_quad(lg, ls));
   }
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
@@ -646,7 +657,7 @@ fwd_bf16_body(Smem<KD, VS, CP>& sm, const int bid, const int nblk,
           if (r < 15) {
             f32x4 col[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) col[u] = *reinterpret_cast<const f32x4*>(&Lt[r * 16 + 4 * u]);
+            for (int u = 0; u < 4; ++u) col[u] = *reinterpret_cast<const f32x4*>(&Lt[r * 16 + ad_quad(u, r)]);
 #pragma unroll
             for (int rr = r + 1; rr < 16; ++rr) acc[rr] = fmaf(col[rr >> 2][rr & 3], xv[r], acc[rr]);
           }
