@@ -666,6 +666,23 @@ def main():
                             "token_heads_per_s": ns1 * T / dt1},
                "cpu_model": cpu_model()}
 
+    # The bound is the roof the arithmetic intensity reaches first: bf16 inputs
+    # (134 FLOP/B at d = 128) sit below the bf16 ridge (2.5 PFLOP/s / 8 TB/s =
+    # 312 FLOP/B) and are HBM-bound; float32 inputs move twice the bytes but run
+    # on the fp32 matrix cores, whose ridge (157.3 TFLOP/s / 8 TB/s = 19.7 FLOP/B)
+    # they exceed, so their roof is the fp32 MFMA peak.
+    hbm = {"achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": achieved_gbs / HBM_PEAK_GBS}
+    if aflops / abytes > peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                "frac": tflops / peak, "hbm": hbm}
+    else:
+        roof = dict(bound="hbm", **hbm)
+    roof.update({"traffic": traffic, "kernel_ms": kern_ms, "kernel_ms_pct": pcts,
+                 "kernel_ms_launches": int(per_launch.size), "algorithmic_bytes": abytes,
+                 "arithmetic_intensity": aflops / abytes,
+                 "copy_gbs": copy_gbs, "frac_of_copy": achieved_gbs / copy_gbs})
+
     # the headline metric names the training shape; other workloads and the
     # segment-parallel call get a metric that names what was timed
     if w.name == "train_bf16" and args.segments == 1:
@@ -692,11 +709,7 @@ def main():
                                                             if args.segments > 1 else ""),
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": K,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel_ms": kern_ms, "kernel_ms_pct": pcts, "kernel_ms_launches": int(per_launch.size),
-                     "algorithmic_bytes": abytes,
-                     "copy_gbs": copy_gbs, "frac_of_copy": achieved_gbs / copy_gbs},
+        "roofline": roof,
         "mfma": {"tflops_algorithmic": tflops, "peak_tflops": peak,
                  "peak_dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
                  "frac": tflops / peak, "algorithmic_flops": aflops,
