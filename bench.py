@@ -34,6 +34,20 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "fwd_bf16_train_B8T4096H6_hbm_tr
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
 
 
+def pick_roof(flops, nbytes, kern_ms, peak_tflops):
+    """Roofline object for one launch of kern_ms: the roof the arithmetic
+    intensity (flops / nbytes) reaches first, HBM below the ridge
+    peak_tflops / HBM peak, the matrix cores above it (then with the HBM
+    figures under "hbm")."""
+    gbs = nbytes / (kern_ms / 1e3) / 1e9
+    hbm = {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+    if flops / nbytes > peak_tflops * 1e12 / (HBM_PEAK_GBS * 1e9):
+        tf = flops / (kern_ms / 1e3) / 1e12
+        return {"bound": "mfma", "achieved": tf, "peak": peak_tflops, "unit": "TFLOP/s",
+                "frac": tf / peak_tflops, "hbm": hbm}
+    return dict(bound="hbm", **hbm)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -671,13 +685,7 @@ def main():
     # 312 FLOP/B) and are HBM-bound; float32 inputs move twice the bytes but run
     # on the fp32 matrix cores, whose ridge (157.3 TFLOP/s / 8 TB/s = 19.7 FLOP/B)
     # they exceed, so their roof is the fp32 MFMA peak.
-    hbm = {"achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": achieved_gbs / HBM_PEAK_GBS}
-    if aflops / abytes > peak * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-                "frac": tflops / peak, "hbm": hbm}
-    else:
-        roof = dict(bound="hbm", **hbm)
+    roof = pick_roof(aflops, abytes, kern_ms, peak)
     roof.update({"traffic": traffic, "kernel_ms": kern_ms, "kernel_ms_pct": pcts,
                  "kernel_ms_launches": int(per_launch.size), "algorithmic_bytes": abytes,
                  "arithmetic_intensity": aflops / abytes,

@@ -294,3 +294,28 @@ def test_noalloc_segmented_rejects_calls_beyond_its_static_scratch():
     assert ncall(segments=0) == gdn.GDN_ERROR_INVALID_VALUE
     assert ncall(K=48) == gdn.GDN_ERROR_NOT_SUPPORTED
     assert ncall(segments=4, null="q") == gdn.GDN_ERROR_INVALID_VALUE
+
+
+def test_bench_roof_follows_arithmetic_intensity():
+    # bf16 inputs at d = 128 carry 134 FLOP per byte, below the bf16 ridge (2.5 PFLOP/s
+    # over 8 TB/s, 312 FLOP/B): HBM-bound.  fp32 inputs move twice the bytes (68 FLOP/B)
+    # but sit above the fp32 ridge (157.3 TFLOP/s over 8 TB/s, 19.7 FLOP/B): their roof
+    # is the fp32 matrix cores.
+    import bench
+    B, T, H, K, V, C = 8, 4096, 6, 128, 128, 64
+    flops = bench.algorithmic_flops(B, T, H, K, V, C)
+    # per token-head: (3C-1)K + 2CV + 6KV + C^2/3 = 24,448 + 16,384 + 98,304 + 1,365.3
+    assert abs(flops / (B * T * H) - 140501.333) < 1e-3
+    for esz, peak, bound in ((2, bench.BF16_PEAK_TFLOPS, "hbm"), (4, bench.F32_PEAK_TFLOPS, "mfma")):
+        nbytes = bench.algorithmic_bytes(B, T, H, K, V, esz=esz)
+        r = bench.pick_roof(flops, nbytes, 0.1, peak)
+        assert r["bound"] == bound
+        if bound == "hbm":
+            assert r["unit"] == "GB/s" and abs(r["achieved"] - nbytes / 1e-4 / 1e9) < 1e-6
+        else:
+            assert r["unit"] == "TFLOP/s" and r["peak"] == peak
+            assert abs(r["frac"] - flops / 1e-4 / 1e12 / peak) < 1e-12
+            assert r["hbm"]["unit"] == "GB/s"
+    # the headline workload's algorithmic bytes: 1032 B per token-head plus the
+    # fp32 final state
+    assert bench.algorithmic_bytes(B, T, H, K, V, esz=2) == 1032 * B * T * H + B * H * V * K * 4
