@@ -18,16 +18,26 @@ constexpr int kThreads = 64 * kWaves;
 // Ragged batches of up to this many sequences start their longest sequences first.
 constexpr int kLongestFirstMax = 128;
 
-// Row stride (elements) of the CP x CP bf16 tiles P^T and Tm^T.  At CP = 64,
-// 160-byte rows: the 8-byte transposed accumulator stores of a 16 x 16 tile then
-// take fewer LDS cycles than at 144 bytes (rows stay 16-byte aligned for the
-// diagonal blocks' 16-byte row writes).
+// Row stride (elements) of the CP x CP bf16 tiles P^T and Tm^T: 160-byte rows
+// at CP = 64 (16-byte aligned for the diagonal blocks' row writes; the
+// transpose reads of 4 rows x 32 bytes then fall on distinct banks).
 __host__ __device__ constexpr int tile_ld(int cp) { return cp == 64 ? cp + 16 : cp + 8; }
 
+// P^T is written by 8-byte transposed accumulator stores (16 lanes: 16 rows, one
+// 8-byte chunk each) and read by 8-byte transpose reads (16 lanes: 4 rows x 4
+// chunks), nothing wider, so its 8-byte chunks are swizzled within each 16-column
+// tile: chunk j of row i sits at chunk j ^ ((i / 4) % 4) of the tile.  Rows i and
+// i + 4 then put the same chunk on different banks, and both access patterns are
+// conflict-free.  p_chunk gives the swizzled chunk (in elements) for tile-local
+// chunk j (0..3) of row i.
+__host__ __device__ constexpr int p_chunk(int j, int i) { return 4 * (j ^ ((i >> 2) & 3)); }
+
 // The fp32 diagonal A blocks are stored transposed, 16 floats per row, with the
-// four 16-byte quads of row c rotated by c / 4: quad u of row c sits at
-// ad_quad(u, c).  The 16 lanes of one store then cover all 64 banks.
-__host__ __device__ constexpr int ad_quad(int u, int c) { return 4 * ((u + (c >> 2)) & 3); }
+// four 16-byte quads of row c permuted: quad u of row c sits at ad_quad(u, c).
+// The permutation differs for any two of the rows a 16-byte store serves at once
+// (c, c + 4, c + 8, c + 12, and c, c + 2, c + 4, c + 6), so the stores are
+// conflict-free.
+__host__ __device__ constexpr int ad_quad(int u, int c) { return 4 * ((u ^ ((c >> 1) ^ (c >> 3))) & 3); }
 
 template <int KD, int VS, int CP>
 struct alignas(16) Smem {
@@ -186,7 +196,7 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
   lbf16* pw = nullptr;
   lbf16* aw = nullptr;
   lf32* adw = nullptr;
-  if (DP) pw = pin(lds(sm.pt[c % 2]) + ls * LDC + 4 * lg);
+  if (DP) pw = pin(lds(sm.pt[c % 2]) + ls * LDC + p_chunk(lg, ls));  // row 16 tc + ls, chunk lg
   if (DA) {
     aw = pin(lds(sm.ap[c % 2]) + ls * LDA + 4 * lg);
     adw = pin(lds(sm.ad) + ls * 16 + ad_quad(lg, ls));
@@ -565,7 +575,8 @@ fwd_bf16_body(Smem<KD, VS, CP>& sm, const int bid, const int nblk,
       if constexpr (NCB > 1) load_kt(1, kt[1]);
       // ---- phase B: U = Tm R, O = diag(gam) Z + P U, S^T <- gam_n S^T + K^T Up
       const lbf16* tc = pin(lds(sm.tt[x % 2]) + cols_lane_tau(LDC, lane, 4));
-      const lbf16* pc = tc + (&sm.pt[0][0] - &sm.tt[0][0]);
+      // P^T is swizzled (p_chunk): rows 4g + s/4 (+ multiples of 16), chunk s % 4
+      const lbf16* pc = pin(lds(sm.pt[x % 2]) + (4 * lg + (ls >> 2)) * LDC + p_chunk(ls & 3, 4 * lg));
       bf16x8 tf[NTB][CS], pf[NTB][CS];
       f32x4 dnv[NTB];
 #pragma unroll
