@@ -87,7 +87,53 @@ int pick_vs(int B, int H, int V) {
   return (long)B * H * (V / 32) >= 192 ? 32 : 16;
 }
 
+// Segment end states N (workgroups [0, nN): values, zero start, V rows) and segment
+// transitions A (the rest: no values, identity starts, K rows) of the
+// segment-parallel forward, both states only, in one launch.  64 value rows per
+// workgroup share each chunk's Gram and solve between four chain waves, so the two
+// passes take about as many workgroups as one pass at 32 rows; the layout has no
+// query or P rings (SQ = false), which leaves room for the 64-row value ring.
+template <int KD>
+__global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+seg_states_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                  const float* __restrict__ alpha, const float* __restrict__ beta,
+                  const float* __restrict__ ident, float* __restrict__ n_final,
+                  float* __restrict__ a_final, const int* __restrict__ cu, int T, int H, int V,
+                  int nN) {
+  __shared__ Smem<KD, 64, 64, false> sm;
+  const int bid = blockIdx.x;
+  // q is never read by the states-only body (no queries are staged)
+  if (bid < nN)
+    fwd_bf16_body<KD, 64, 64, false, false>(sm, bid, nN, k, k, v, alpha, beta, nullptr, nullptr,
+                                            n_final, nullptr, nullptr, cu, T, H, KD, V, 64, V / 64);
+  else
+    fwd_bf16_body<KD, 64, 64, false, false>(sm, bid - nN, (int)gridDim.x - nN, k, k, nullptr, alpha,
+                                            beta, ident, nullptr, a_final, nullptr, nullptr, cu, T, H,
+                                            KD, KD, 64, KD / 64);
+}
+
+template <int KD>
+hipError_t launch_seg_states(const FwdArgs& a, const float* ident, float* a_final, hipStream_t stream) {
+  const int nN = a.B * a.H * (a.V / 64), nA = a.B * a.H * (KD / 64);
+  hipLaunchKernelGGL((seg_states_kernel<KD>), dim3(nN + nA), dim3(kThreads), 0, stream,
+                     static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v), a.alpha, a.beta,
+                     ident, a.s_final, a_final, a.cu_seqlens, a.T, a.H, a.V, nN);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool fwd_bf16_seg_states_supported(int K, int V, int chunk) {
+  return (K == 64 || K == 128) && (V == 64 || V == 128) && chunk == 64;
+}
+
+hipError_t launch_fwd_bf16_seg_states(const FwdArgs& a, const float* ident, float* a_final,
+                                      hipStream_t stream) {
+  if (!fwd_bf16_seg_states_supported(a.K, a.V, a.chunk) || !a.cu_seqlens || !a.v || a.s0)
+    return hipErrorInvalidValue;
+  return a.K == 64 ? launch_seg_states<64>(a, ident, a_final, stream)
+                   : launch_seg_states<128>(a, ident, a_final, stream);
+}
 
 int fwd_bf16_value_slice(int B, int H, int V) { return pick_vs(B, H, V); }
 

@@ -39,7 +39,9 @@ __host__ __device__ constexpr int p_chunk(int j, int i) { return 4 * (j ^ ((i >>
 // conflict-free.
 __host__ __device__ constexpr int ad_quad(int u, int c) { return 4 * ((u ^ ((c >> 1) ^ (c >> 3))) & 3); }
 
-template <int KD, int VS, int CP>
+// SQ = false: a states-only layout without the query and P rings (the
+// instance with 64 value rows needs that room for its value ring).
+template <int KD, int VS, int CP, bool SQ = true>
 struct alignas(16) Smem {
   static constexpr int NTB = CP / 16;
   // key and query rows: KD + 16 elements, a stride of 32 bytes modulo 64, which
@@ -50,7 +52,7 @@ struct alignas(16) Smem {
   static constexpr int LDA = 24;       // packed 16-wide A^T blocks
   static constexpr int APK = (NTB == 4 ? 96 : 16) * LDA;
   bf16 k[3][CP * LDK];                 // keys [token][channel], padded rows
-  bf16 q[2][CP * LDK];                 // queries, padded rows
+  bf16 q[2][SQ ? CP * LDK : 8];        // queries, padded rows
   // value slice [token][v]; rows of 96 bytes keep the transpose reads of 8
   // consecutive token rows on distinct banks
   static constexpr int LDV = (VS == 16 || VS == 32) ? 48 : VS + 16;
@@ -64,7 +66,7 @@ struct alignas(16) Smem {
   } gt[3];
   // offsets (in floats) of the gate vectors from gl within one slot
   static constexpr int GAM = CP, BETA = 2 * CP, BG = 3 * CP, DN = 4 * CP;
-  bf16 pt[2][CP * LDC];                // P^T: pt[i][r]
+  bf16 pt[2][SQ ? CP * LDC : 8];                // P^T: pt[i][r]
   bf16 tt[2][CP * LDC];                // Tm^T: tt[j][i]; upper blocks zero
   bf16 ap[2][APK];                     // off-diagonal A^T blocks used by the levels
   // diagonal A blocks, fp32, transposed [c][r]; blocks ADS floats apart so the
@@ -250,15 +252,16 @@ __device__ __forceinline__ void gram_rows(SM& sm, int c, int lane) {
 
 // WO: the output o is produced.  Without it (states only: o == NULL) queries,
 // P, Z and O are skipped entirely.
-template <int KD, int VS, int CP, bool WO>
+template <int KD, int VS, int CP, bool WO, bool SQ = true>
 __device__ __forceinline__ void
-fwd_bf16_body(Smem<KD, VS, CP>& sm, const int bid, const int nblk,
+fwd_bf16_body(Smem<KD, VS, CP, SQ>& sm, const int bid, const int nblk,
               const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const float* __restrict__ alpha, const float* __restrict__ beta,
               const float* __restrict__ s0, bf16* __restrict__ o, float* __restrict__ s_final,
               float* __restrict__ s_ckpt, bf16* __restrict__ s_ckpt_h, const int* __restrict__ cu,
               int T, int H, int K, int V, int C, int nslice) {
-  using SM = Smem<KD, VS, CP>;
+  using SM = Smem<KD, VS, CP, SQ>;
+  static_assert(SQ || !WO, "outputs need the query and P rings");
   constexpr int LDC = SM::LDC;
   constexpr int NTB = CP / 16;          // token blocks per chunk tile
   constexpr int NCB = KD / 16;          // key-channel blocks
@@ -344,7 +347,7 @@ fwd_bf16_body(Smem<KD, VS, CP>& sm, const int bid, const int nblk,
 
   // ---- zero the P and Tm rings: their upper blocks are read as zeros
   for (int i = tid; i < 2 * CP * LDC; i += kThreads) {
-    (&sm.pt[0][0])[i] = (bf16)0.0f;
+    if constexpr (SQ) (&sm.pt[0][0])[i] = (bf16)0.0f;
     (&sm.tt[0][0])[i] = (bf16)0.0f;
   }
 
@@ -702,7 +705,11 @@ fwd_bf16_body(Smem<KD, VS, CP>& sm, const int bid, const int nblk,
         // whose epilogue is the longer one, to those beside the levels and
         // diagonal waves (2-3% faster than the other way round).
         if (c >= 0 && c < NT) {
-          if constexpr (NTB == 4) {
+          if constexpr (NTB == 4 && !WO && NG == 2) {
+            // states only with two Gram waves (64 value rows): both build A
+            if (gw == 0) gram_rows<KD, CP, 0, 0, 3>(sm, c, lane);
+            else gram_rows<KD, CP, 0, 1, 2>(sm, c, lane);
+          } else if constexpr (NTB == 4) {
             switch (gw) {
               case 0: if constexpr (WO) gram_rows<KD, CP, 1, 0, 3>(sm, c, lane); break;
               case 1: if constexpr (WO) gram_rows<KD, CP, 1, 1, 2>(sm, c, lane); break;

@@ -122,6 +122,16 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
 
+// The two states-only passes of the segment-parallel forward in one bf16 launch
+// with 64 value rows per workgroup: `a` describes the N pass (values a.v, zero
+// start, end states to a.s_final, V rows), and the A pass runs beside it over the
+// same packed sequences with no values, start states `ident` and K rows, end
+// states to `a_final`.  Needs 64-token chunks and K, V in {64, 128}
+// (fwd_bf16_seg_states_supported); hipErrorInvalidValue otherwise.
+bool fwd_bf16_seg_states_supported(int K, int V, int chunk);
+hipError_t launch_fwd_bf16_seg_states(const FwdArgs& a, const float* ident, float* a_final,
+                                      hipStream_t stream);
+
 // Bfloat16 q/k/v/o: bf16 MFMA kernel with fp32 accumulation and fp32 state.
 // Returns hipErrorInvalidValue for a shape outside its compiled set.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

@@ -218,18 +218,25 @@ int64_t fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
   if (B * H > (INT64_C(1) << 24)) return 1;  // that many streams fill the GPU by themselves
   // Per-chunk times of the forward kernel (microseconds at 64-token chunks, from
   // kernel traces on MI355X): with outputs 1.97 (32 value rows per workgroup) or
-  // 1.71 (16 rows); states only 1.57 or 1.40.  Each pass also runs two
-  // pipeline-fill iterations and costs about 6 us of launch; the combine 1.8 us
-  // per segment step plus its launch.
+  // 1.71 (16 rows); states only 1.57 or 1.40, and 2.09 for the launch that runs
+  // both states-only passes with 64 rows per workgroup (64-token chunks, K and V
+  // in {64, 128}).  Each pass also runs two pipeline-fill iterations and costs
+  // about 6 us of launch; the combine 1.8 us per segment step plus its launch.
   const double scale = (double)chunk / 64.0;
   constexpr double kLaunch = 6.0;
+  auto rounds_of = [&](int64_t wgs) { return (double)((wgs + cus - 1) / cus); };
   auto pass = [&](int64_t streams, int64_t rows, int64_t nchunks, bool outputs) {
     if (streams > (INT64_C(1) << 24)) return 1e30;  // beyond any useful segment count
     const int vs = fwd_bf16_value_slice((int)streams, (int)H, (int)rows);
     const int64_t wgs = streams * H * ((rows + vs - 1) / vs);
-    const int64_t rounds = (wgs + cus - 1) / cus;
     const double per = outputs ? (vs == 32 ? 1.97 : 1.71) : (vs == 32 ? 1.57 : 1.40);
-    return (double)rounds * (double)(nchunks + 2) * per * scale + kLaunch;
+    return rounds_of(wgs) * (double)(nchunks + 2) * per * scale + kLaunch;
+  };
+  const bool merged = fwd_bf16_seg_states_supported((int)K, (int)V, (int)chunk);
+  auto states = [&](int64_t streams, int64_t nchunks) {
+    if (!merged) return pass(streams, V, nchunks, false) + pass(streams, K, nchunks, false);
+    if (streams > (INT64_C(1) << 24)) return 1e30;
+    return rounds_of(streams * H * (V / 64 + K / 64)) * (double)(nchunks + 2) * 2.09 + kLaunch;
   };
   const int64_t nch = (T + chunk - 1) / chunk;
   double best = pass(B, V, nch, true);
@@ -237,8 +244,7 @@ int64_t fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
   // at least four chunks per segment, at most 256 segments
   for (int64_t P = 2; P <= 256 && 4 * P <= nch; ++P) {
     const int64_t L = ((T + P - 1) / P + chunk - 1) / chunk;  // chunks per segment
-    const double t = pass(B * P, V, L, false) + pass(B * P, K, L, false) + pass(B * P, V, L, true) +
-                     1.8 * (double)(P - 1) + kLaunch;
+    const double t = states(B * P, L) + pass(B * P, V, L, true) + 1.8 * (double)(P - 1) + kLaunch;
     if (t < best) {
       best = t;
       best_p = P;
@@ -325,12 +331,17 @@ hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int P, void* worksp
   f.s0 = nullptr;
   f.s_final = Nseg;
   f.s_ckpt = nullptr;
-  if ((e = fwd(f)) != hipSuccess) return e;
-  f.v = nullptr;
-  f.V = a.K;
-  f.s0 = ident;
-  f.s_final = Aseg;
-  if ((e = fwd(f)) != hipSuccess) return e;
+  if (bf16 && fwd_bf16_seg_states_supported(a.K, a.V, a.chunk)) {
+    // both passes in one launch, 64 value rows per workgroup
+    if ((e = launch_fwd_bf16_seg_states(f, ident, Aseg, stream)) != hipSuccess) return e;
+  } else {
+    if ((e = fwd(f)) != hipSuccess) return e;
+    f.v = nullptr;
+    f.V = a.K;
+    f.s0 = ident;
+    f.s_final = Aseg;
+    if ((e = fwd(f)) != hipSuccess) return e;
+  }
 
   // 2. true segment starts, in segment order per stream
   {

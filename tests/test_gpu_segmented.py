@@ -36,6 +36,11 @@ CASES = [
     (1, 777, 2, 16, 64, 16, torch.float32, 0.3, 7),
     (2, 500, 2, 128, 128, 64, torch.float32, 0.05, 1),    # the plain path
     (2, 300, 2, 64, 16, 32, torch.float32, 0.2, 2),       # one transition
+    # bf16, 64-token chunks, K and V in {64, 128}: both states-only passes in one
+    # launch with 64 value rows per workgroup
+    (2, 700, 3, 64, 128, 64, torch.bfloat16, 0.1, 5),
+    (1, 500, 2, 64, 64, 64, torch.bfloat16, None, 3),
+    (3, 450, 2, 128, 64, 64, torch.bfloat16, 0.05, 2),
 ]
 
 
@@ -108,3 +113,20 @@ def test_segment_count_from_the_hint():
     torch.cuda.synchronize()
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
     assert_parity("hinted", {"o": (o, ro), "final_state": (sf, rs)}, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("K,V,P", [(64, 64, 6), (128, 128, 9), (128, 64, 4)])
+def test_segmented_weak_decay_bf16_merged_passes(K, V, P):
+    # the bf16 states-only passes (N and A in one launch): with alpha in (0.995, 1)
+    # every segment's output depends on the transitions of the segments before it
+    inp = make_inputs(2, 1100, 2, K, V, dtype=torch.bfloat16, seed=640 + K + V, s0_std=0.3)
+    g = torch.Generator().manual_seed(641)
+    inp["alpha"] = 1.0 - 0.005 * torch.rand(inp["alpha"].shape, generator=g)
+    inp["beta"] = 0.1 * torch.rand(inp["beta"].shape, generator=g)
+    print("case weak decay bf16 K%d V%d P%d" % (K, V, P), flush=True)
+    gd = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
+    o, sf = chunk_fwd_segmented(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"],
+                                gd["initial_state"], chunk=64, segments=P)
+    torch.cuda.synchronize()
+    ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
+    assert_parity("weak decay bf16", {"o": (o, ro), "final_state": (sf, rs)}, TOL[torch.bfloat16])
