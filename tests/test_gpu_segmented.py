@@ -71,12 +71,16 @@ def test_segmented_state_in_place_and_close_to_plain():
     assert rel_l2(s2, s1.double().cpu().numpy()) <= 1e-2
 
 
-def test_long_context_workload_segmented():
+@pytest.mark.parametrize("P", [4, 8, 2])
+def test_long_context_workload_segmented(P):
+    # the full long-context workload; its two states-only passes run in one launch of
+    # 16 P (V/64 + K/64) workgroups: 256 at P = 4, 512 (more than the CUs) at P = 8
     w = WORKLOADS["long_bf16"]
     inp = workload_inputs(w)
+    print("case long-context segmented P=%d" % P, flush=True)
     g = {n: (t.to(DEV) if t is not None else None) for n, t in inp.items()}
     o, sf = chunk_fwd_segmented(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["initial_state"],
-                                chunk=w.chunk, segments=4)
+                                chunk=w.chunk, segments=P)
     torch.cuda.synchronize()
     ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
     assert_parity("long segmented", {"o": (o, ro), "final_state": (sf, rs)}, 2e-2)
