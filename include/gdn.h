@@ -25,9 +25,10 @@
  *  - All pointers are DEVICE pointers (memory from hipMalloc or a torch CUDA
  *    tensor on the current device), except where stated.  The caller owns every
  *    buffer; the library allocates no device memory for these calls, with one
- *    exception: the float32 forward (gdn_chunk_fwd and gdn_chunk_fwd_varlen with
- *    GDN_DTYPE_F32) takes a stream-ordered scratch of per-chunk factors from a
- *    library-owned memory pool on the stream's device (see gdn_chunk_fwd).
+ *    exception: the float32 forward (gdn_chunk_fwd, gdn_chunk_fwd_varlen and
+ *    gdn_chunk_fwd_segmented with GDN_DTYPE_F32) takes a stream-ordered scratch of
+ *    per-chunk factors from a library-owned memory pool on the stream's device
+ *    (see gdn_chunk_fwd); gdn_chunk_fwd_segmented_noalloc never allocates.
  *  - Tensors are dense, contiguous and row-major, each at least 16-byte aligned:
  *        q, k            [B, T, H, K]   element type `dtype`
  *        v, o            [B, T, H, V]   element type `dtype`
@@ -202,7 +203,9 @@ GDN_API size_t gdn_chunk_fwd_segmented_workspace_size(int64_t B, int64_t T, int6
  *      final state).
  *
  * For bfloat16 inputs with 64-token chunks and K, V in {64, 128} the two
- * state passes of step 1 run in one launch.
+ * state passes of step 1 run in one launch.  Float32 inputs run every pass on the
+ * fp32 matrix cores, with the per-chunk factors of gdn_chunk_fwd (from the
+ * library's pool, see gdn_chunk_fwd).
  *
  * State passing between chunks is the chunk recurrence of "Sparse Delta Memory:
  * layer and kernels", section "What the layer computes", applied between
@@ -249,7 +252,11 @@ GDN_API gdn_status_t gdn_chunk_fwd_segmented(const void *q, const void *k, const
  * it and give wrong results.  Calls in one stream's order are safe.
  *
  *   arguments      as for gdn_chunk_fwd_segmented, without workspace and
- *                  workspace_bytes; results identical (bitwise) to it
+ *                  workspace_bytes; results identical (bitwise) to it for
+ *                  bfloat16 inputs.  Float32 inputs run on the scalar fp32
+ *                  kernel here (the other entry points' fp32 matrix-core path
+ *                  draws its per-chunk factors from a pool), so they agree with
+ *                  gdn_chunk_fwd_segmented to rounding (within 1e-5 relative L2).
  */
 GDN_API gdn_status_t gdn_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
                                              const float *alpha, const float *beta,

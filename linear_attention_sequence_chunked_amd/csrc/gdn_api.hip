@@ -75,11 +75,14 @@ namespace {
 
 // Shared body of the dense and packed forward entry points.  The token tensors
 // hold NTOK = Bt * T token rows (Bt = B dense, 1 packed); states hold B rows.
+// may_allocate = false (the allocation-free entry point): float32 inputs take the
+// scalar kernel, which needs no scratch, instead of the matrix-core path with its
+// pooled factors.
 gdn_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
                             const float* beta, const int32_t* cu_seqlens, const float* initial_state,
                             void* o, float* final_state, int64_t B, int64_t Bt, int64_t T,
                             int64_t H, int64_t K, int64_t V, int64_t chunk, gdn_dtype_t dtype,
-                            void* stream) {
+                            void* stream, bool may_allocate = true) {
   if (!q || !k || !v || !alpha || !beta || !o) return GDN_ERROR_INVALID_VALUE;
   const void* ptrs[] = {q, k, v, alpha, beta, initial_state, o, final_state};
   for (const void* p : ptrs)
@@ -128,7 +131,9 @@ gdn_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
   a.chunk = static_cast<int>(chunk);
   a.cu_seqlens = cu_seqlens;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = dtype == GDN_DTYPE_F32 ? gdn::launch_fwd_f32(a, s) : gdn::launch_fwd_bf16(a, s);
+  hipError_t err = dtype == GDN_DTYPE_BF16 ? gdn::launch_fwd_bf16(a, s)
+                   : may_allocate          ? gdn::launch_fwd_f32(a, s)
+                                           : gdn::launch_fwd_f32_scalar(a, s);
   return err == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH;
 }
 
@@ -188,7 +193,7 @@ gdn_status_t segmented_impl(const void* q, const void* k, const void* v, const f
   if (segments <= 0) return GDN_ERROR_INVALID_VALUE;
   if (segments == 1)
     return chunk_fwd_impl(q, k, v, alpha, beta, nullptr, initial_state, o, final_state, B, B, T,
-                          H, K, V, chunk, dtype, stream);
+                          H, K, V, chunk, dtype, stream, /*may_allocate=*/!noalloc);
   if (!noalloc && (!workspace || !aligned16(workspace))) return GDN_ERROR_INVALID_VALUE;
   // shape checks of the dense call, plus the B * segments packed states
   const gdn_status_t st = check_shape(B, T, H, K, V, chunk, dtype);

@@ -100,8 +100,11 @@ size_t fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K,
 // plain call is expected to be fastest).
 int64_t fwd_segments_hint(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, int64_t chunk,
                           int64_t cus);
+// Float32 inputs run the three passes on the fp32 matrix cores, whose per-chunk
+// factors come from the library's stream-ordered pool, unless may_allocate is false
+// (then the scalar fp32 kernel, which needs no scratch).
 hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int segments, void* workspace,
-                                hipStream_t stream);
+                                hipStream_t stream, bool may_allocate = true);
 // The same with the library's per-device static scratch of kSegmentedScratchBytes
 // instead of a caller workspace (no allocation; calls that overlap on one device
 // race on it).  hipErrorInvalidValue when the call needs more than that.

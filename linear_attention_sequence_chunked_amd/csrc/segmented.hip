@@ -302,11 +302,11 @@ hipError_t launch_fwd_segmented_noalloc(const FwdArgs& a, bool bf16, int P, hipS
   void* ws = nullptr;
   const hipError_t e = segmented_scratch(dev, &ws);
   if (e != hipSuccess) return e;
-  return launch_fwd_segmented(a, bf16, P, ws, stream);
+  return launch_fwd_segmented(a, bf16, P, ws, stream, /*may_allocate=*/false);
 }
 
 hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int P, void* workspace,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool may_allocate) {
   const SegLayout g = seg_layout(a.B, a.T, a.H, a.K, a.V, a.chunk, P);
   char* ws = static_cast<char*>(workspace);
   int* cu = reinterpret_cast<int*>(ws + g.cu_off);
@@ -315,7 +315,12 @@ hipError_t launch_fwd_segmented(const FwdArgs& a, bool bf16, int P, void* worksp
   float* Nseg = reinterpret_cast<float*>(ws + g.N_off);
   float* start = reinterpret_cast<float*>(ws + g.start_off);
   float* ends = reinterpret_cast<float*>(ws + g.ends_off);
-  auto fwd = [&](const FwdArgs& f) { return bf16 ? launch_fwd_bf16(f, stream) : launch_fwd_f32_scalar(f, stream); };
+  // float32 passes: the matrix-core forward (factors from the library's stream-ordered
+  // pool) when the call may allocate, else the scalar kernel (no scratch)
+  auto fwd = [&](const FwdArgs& f) {
+    if (bf16) return launch_fwd_bf16(f, stream);
+    return may_allocate ? launch_fwd_f32(f, stream) : launch_fwd_f32_scalar(f, stream);
+  };
   hipError_t e;
 
   hipLaunchKernelGGL(seg_init_kernel, dim3(256), dim3(kThreads), 0, stream, cu, ident, a.B, a.T,

@@ -2,9 +2,11 @@
 against the segmented forward with a caller workspace, through the C ABI.
 
 Two calls in a row share the library's static scratch, the second with a
-smaller input: each must equal the workspace call bitwise (same kernels, same
-arithmetic) and meet the oracle's bar (1e-5 float32, 2e-2 bfloat16 relative L2,
-whole tensor and every local block).  The result of the first call is checked
+smaller input: each must equal the workspace call (bitwise for bfloat16: same
+kernels, same arithmetic; within 1e-5 relative L2 for float32, where the
+workspace call runs on the fp32 matrix cores with pooled factors and the
+allocation-free call on the scalar fp32 kernel) and meet the oracle's bar (1e-5
+float32, 2e-2 bfloat16 relative L2, whole tensor and every local block).  The result of the first call is checked
 after the second has run, so a second call that wrote into the first call's
 outputs, or read stale scratch, would show.
 """
@@ -45,8 +47,13 @@ def test_noalloc_matches_workspace_call_twice_in_a_row(dt, C):
     got_s = chunk_fwd_segmented_noalloc(*args(gs), chunk=C, segments=5)
     torch.cuda.synchronize()
     for name, got, ref in (("first", got_b, ref_b), ("second", got_s, ref_s)):
-        assert torch.equal(got[0], ref[0]), name
-        assert torch.equal(got[1], ref[1]), name
+        if dt == torch.bfloat16:
+            assert torch.equal(got[0], ref[0]), name
+            assert torch.equal(got[1], ref[1]), name
+        else:
+            for x, y in zip(got, ref):
+                err = float((x.double() - y.double()).norm() / y.double().norm())
+                assert err <= 1e-5, (name, err)
     for inp, got in ((big, got_b), (small, got_s)):
         ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
                             inp["initial_state"])
@@ -82,3 +89,15 @@ def test_noalloc_refuses_more_than_its_scratch():
     torch.cuda.synchronize()
     ref = chunk_fwd_segmented(*args(g), chunk=16, segments=4)
     assert torch.equal(o, ref[0]) and torch.equal(s, ref[1])
+
+
+def test_noalloc_single_segment_float32_allocates_nothing_and_matches():
+    # one segment is the plain call; without allocation float32 takes the scalar
+    # kernel (the plain call's matrix-core path draws pooled factors)
+    inp = make_inputs(2, 500, 3, 64, 64, dtype=torch.float32, seed=2330, s0_std=0.1)
+    print("case noalloc float32 single segment", flush=True)
+    g = dev(inp)
+    o, s = chunk_fwd_segmented_noalloc(*args(g), chunk=32, segments=1)
+    torch.cuda.synchronize()
+    ro, rs = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["initial_state"])
+    assert_parity("noalloc single segment", {"o": (o, ro), "final_state": (s, rs)}, 1e-5)
