@@ -680,13 +680,22 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   f.V = a.V;
   f.chunk = C;
   float* ws_R = ws_F + (size_t)a.B * a.H * NT * factor_floats(C);  // float32: the records
+  bool walked = false;  // float32: (1) and (2b) ran in one launch
   if constexpr (sizeof(TIn) == 4) {
     // float32: the matrix-core forward in its states-only mode, its per-chunk
     // records after the factors in the workspace; its chunk-parallel launch
-    // writes the factors (2a) as well
+    // writes the factors (2a) as well.  Where it can, the walk that writes the
+    // chunk-start states runs in one launch with the reverse walk (2b), which
+    // needs only the records.
     f.s_ckpt = ws_S;
     f.factors = ws_F;
-    e = launch_fwd_f32_records(f, ws_R, stream);
+    if (bwd_f32_walks_supported(a.K, a.V, C)) {
+      e = launch_fwd_f32_record_only(f, ws_R, stream);
+      if (e == hipSuccess) e = launch_bwd_f32_walks(a, C, ws_R, ws_S, ws_dS, stream);
+      walked = true;
+    } else {
+      e = launch_fwd_f32_records(f, ws_R, stream);
+    }
   } else {
     e = launch_fwd_states(f, true, ws_S, stream);
   }
@@ -704,7 +713,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   }
   // (2b) reverse walk (float32: on the matrix cores, from the recompute's records)
   if constexpr (sizeof(TIn) == 4) {
-    if ((e = launch_bwd_f32_dstate(a, C, ws_R, ws_dS, stream)) != hipSuccess) return e;
+    if (!walked && (e = launch_bwd_f32_dstate(a, C, ws_R, ws_dS, stream)) != hipSuccess) return e;
   } else {
     const int VS = 16;
     const size_t LK = a.K + 1, LV = VS + 1;

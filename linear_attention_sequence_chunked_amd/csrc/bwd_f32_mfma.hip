@@ -13,6 +13,9 @@
 // owners' accumulators; P^T and Tm_b^T operands are column reads of the record's
 // blocks in LDS, the Q and K operands of the update column reads of the chunk's
 // tiles.
+#include <type_traits>
+
+#include "f32_chain.h"
 #include "f32_mfma.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -30,12 +33,34 @@ using namespace f32mfma;
 // under a branch (rows past the end read the chunk's first row; their dO rows
 // are staged as zeros, and the record's zero P columns and beta = 0 keep the
 // other junk rows out of dR and the update).
+//
+// The walk is a device function over a caller-declared LDS block (DstateLds) and
+// a block index; f32_dstate_kernel launches it alone, f32_walks_kernel beside the
+// forward walk that recomputes the chunk-start states.
 template <int KD, int C, int NG>
-__global__ void __launch_bounds__(64 * NG * (C / 16), 1)
-f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                  const float* __restrict__ d_o, const float* __restrict__ d_sfinal,
-                  float* __restrict__ d_s0, const float* __restrict__ rec,
-                  float* __restrict__ ws_dS, int B, int T, int H, int V) {
+struct DstateLds {
+  static constexpr int LS = KD + 4;
+  static constexpr int LC = C + 4;
+  struct Grp {
+    float sS[16 * LS];                       // dS' [v][k]
+    float sdO[2][16 * LC];                   // dO^T [v][t]
+    float sdU[16 * LC];                      // dU^T [v][t]
+    float sdR[16 * LC];                      // (-beta gam dR)^T [v][t]
+  };
+  alignas(16) float sK[2][C * LS];
+  alignas(16) float sQ[2][C * LS];
+  alignas(16) float sRec[2][Rec<C>::kFloats];
+  alignas(16) Grp grp[NG];
+};
+
+template <int KD, int C, int NG>
+__device__ __forceinline__ void dstate_walk(DstateLds<KD, C, NG>& L, int bid,
+                                            const float* __restrict__ q,
+                                            const float* __restrict__ k,
+                                            const float* __restrict__ d_o,
+                                            const float* __restrict__ d_sfinal,
+                                            float* __restrict__ d_s0, const float* __restrict__ rec,
+                                            float* __restrict__ ws_dS, int B, int T, int H, int V) {
   constexpr int NB = C / 16;
   constexpr int NTH = 64 * NG * NB;
   constexpr int KQ = KD / 16;
@@ -48,16 +73,11 @@ f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
   static_assert(RF % 4 == 0, "record pieces");
   constexpr int RP = RF / 4;                 // float4 pieces of a record
   constexpr int RPT = (RP + NTH - 1) / NTH;
-  struct Grp {
-    float sS[16 * LS];                       // dS' [v][k]
-    float sdO[2][16 * LC];                   // dO^T [v][t]
-    float sdU[16 * LC];                      // dU^T [v][t]
-    float sdR[16 * LC];                      // (-beta gam dR)^T [v][t]
-  };
-  __shared__ __attribute__((aligned(16))) float sK[2][C * LS];
-  __shared__ __attribute__((aligned(16))) float sQ[2][C * LS];
-  __shared__ __attribute__((aligned(16))) float sRec[2][RF];
-  __shared__ __attribute__((aligned(16))) Grp grp[NG];
+  using Grp = typename DstateLds<KD, C, NG>::Grp;
+  auto& sK = L.sK;
+  auto& sQ = L.sQ;
+  auto& sRec = L.sRec;
+  auto& grp = L.grp;
 
   const int tid = threadIdx.x, lane = tid & 63, wg = tid >> 6;
   const int gi = wg / NB, w = wg - gi * NB;
@@ -66,7 +86,7 @@ f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
   // the workgroups of one (batch, head) share an XCD, so its records and tiles
   // are fetched into one L2
   const int nvs = V / (16 * NG), streams = B * H;
-  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int xcd = bid & 7, jx = bid >> 3;
   const int stream = xcd + 8 * (jx / nvs);
   if (stream >= streams) return;
   const int v0 = 16 * NG * (jx - (jx / nvs) * nvs) + 16 * gi;
@@ -232,6 +252,44 @@ f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
       if (kap < KQ) st4(d_s0 + sbase + 16 * kap + 4 * g, S[m]);
     }
   }
+}
+
+template <int KD, int C, int NG>
+__global__ void __launch_bounds__(64 * NG * (C / 16), 1)
+f32_dstate_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                  const float* __restrict__ d_o, const float* __restrict__ d_sfinal,
+                  float* __restrict__ d_s0, const float* __restrict__ rec,
+                  float* __restrict__ ws_dS, int B, int T, int H, int V) {
+  __shared__ DstateLds<KD, C, NG> lds;
+  dstate_walk<KD, C, NG>(lds, blockIdx.x, q, k, d_o, d_sfinal, d_s0, rec, ws_dS, B, T, H, V);
+}
+
+// Both sequential walks of the backward in one launch, each at two value groups
+// (32 value rows) per workgroup: blocks [0, nd) walk the chunks in reverse for
+// the state gradients, blocks [nd, nd + nf) walk them forward for the chunk-start
+// states (checkpoints, no outputs).  The two are independent given the records,
+// and neither fills the chip at the shapes the backward is used on, so running
+// them side by side takes about the longer of the two instead of their sum.  nd
+// is a multiple of 8, so both keep their XCD-aware block mapping.  The LDS is
+// the union of the two walks' blocks.
+template <int KD, int C>
+__global__ void __launch_bounds__(128 * (C / 16), 1)
+f32_walks_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                 const float* __restrict__ v, const float* __restrict__ s0,
+                 float* __restrict__ s_ckpt, const float* __restrict__ d_o,
+                 const float* __restrict__ d_sfinal, float* __restrict__ d_s0,
+                 const float* __restrict__ rec, float* __restrict__ ws_dS, int B, int T, int H,
+                 int V, int NT, int nd) {
+  __shared__ union Lds {
+    ChainLds<KD, C, 2, false> fwd;
+    DstateLds<KD, C, 2> rev;
+  } lds;
+  const int bid = blockIdx.x;
+  if (bid < nd)
+    dstate_walk<KD, C, 2>(lds.rev, bid, q, k, d_o, d_sfinal, d_s0, rec, ws_dS, B, T, H, V);
+  else
+    chain_walk<KD, C, 2, false, true, true>(lds.fwd, bid - nd, q, k, v, s0, nullptr, nullptr,
+                                            s_ckpt, rec, nullptr, B, T, H, V, NT);
 }
 
 // ---------------------------------------------------------------------------
@@ -728,6 +786,19 @@ hipError_t launch_kc(const BwdArgs& a, const float* rec, float* ws_dS, hipStream
   return hipGetLastError();
 }
 
+template <int KD, int C>
+hipError_t launch_walks_kc(const BwdArgs& a, const float* rec, float* ws_S, float* ws_dS,
+                           hipStream_t stream) {
+  const long groups = ((long)a.B * a.H + 7) / 8;
+  const int nd = (int)(8 * groups * (a.V / 32));
+  const int NT = (a.T + C - 1) / C;
+  hipLaunchKernelGGL((f32_walks_kernel<KD, C>), dim3(2 * nd), dim3(128 * (C / 16)), 0, stream,
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                     static_cast<const float*>(a.v), a.s0, ws_S, static_cast<const float*>(a.d_o),
+                     a.d_sfinal, a.d_s0, rec, ws_dS, a.B, a.T, a.H, a.V, NT, nd);
+  return hipGetLastError();
+}
+
 template <int KD>
 hipError_t launch_k(const BwdArgs& a, int C, const float* rec, float* ws_dS, hipStream_t stream) {
   if (C == 16) return launch_kc<KD, 16>(a, rec, ws_dS, stream);
@@ -760,6 +831,28 @@ hipError_t launch_bwd_f32_local(const BwdArgs& a, int chunk, const float* ws_S, 
     case 32: return launch_local_k<32>(a, chunk, ws_S, ws_dS, ws_F, stream);
     case 64: return launch_local_k<64>(a, chunk, ws_S, ws_dS, ws_F, stream);
     case 128: return launch_local_k<128>(a, chunk, ws_S, ws_dS, ws_F, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool bwd_f32_walks_supported(int K, int V, int chunk) {
+  return (K == 16 || K == 32 || K == 64 || K == 128) && V > 0 && V % 32 == 0 && V <= 128 &&
+         (chunk == 16 || chunk == 32);
+}
+
+hipError_t launch_bwd_f32_walks(const BwdArgs& a, int chunk, const float* rec, float* ws_S,
+                                float* ws_dS, hipStream_t stream) {
+  if (!bwd_f32_walks_supported(a.K, a.V, chunk)) return hipErrorInvalidValue;
+  auto by_c = [&](auto kc) -> hipError_t {
+    constexpr int KD = decltype(kc)::value;
+    if (chunk == 16) return launch_walks_kc<KD, 16>(a, rec, ws_S, ws_dS, stream);
+    return launch_walks_kc<KD, 32>(a, rec, ws_S, ws_dS, stream);
+  };
+  switch (a.K) {
+    case 16: return by_c(std::integral_constant<int, 16>());
+    case 32: return by_c(std::integral_constant<int, 32>());
+    case 64: return by_c(std::integral_constant<int, 64>());
+    case 128: return by_c(std::integral_constant<int, 128>());
   }
   return hipErrorInvalidValue;
 }

@@ -40,6 +40,8 @@ struct FwdArgs {
 // (fwd_f32_record_bytes(a) bytes, 16-byte aligned).
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32_records(const FwdArgs& a, float* rec, hipStream_t stream);
+// The chunk-parallel record launch alone (the walk left to the caller).
+hipError_t launch_fwd_f32_record_only(const FwdArgs& a, float* rec, hipStream_t stream);
 size_t fwd_f32_record_bytes(const FwdArgs& a);
 bool fwd_f32_mfma_supported(int K, int V, int chunk);
 // Float32 q/k/v/o: scalar fp32 kernel (exact fp32 products and sums), no scratch.
@@ -78,6 +80,13 @@ hipError_t launch_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 // every chunk's end-state gradient to ws_dS [B, H, NT, V, K] and d_s0.
 hipError_t launch_bwd_f32_dstate(const BwdArgs& a, int chunk, const float* rec, float* ws_dS,
                                  hipStream_t stream);
+// Both float32 walks in one launch: the reverse walk above and the forward walk
+// that writes the chunk-start states to ws_S [B, H, NT, V, K], from the records
+// launch_fwd_f32_record_only wrote for the same chunks.  For V a multiple of 32
+// and chunk 16 or 32 (bwd_f32_walks_supported).
+bool bwd_f32_walks_supported(int K, int V, int chunk);
+hipError_t launch_bwd_f32_walks(const BwdArgs& a, int chunk, const float* rec, float* ws_S,
+                                float* ws_dS, hipStream_t stream);
 // Float32 token gradients on the matrix cores, from the chunk-start states, the
 // end-state gradients and the float32 prep's factors (M, P, Tm, gates).
 hipError_t launch_bwd_f32_local(const BwdArgs& a, int chunk, const float* ws_S, const float* ws_dS,

@@ -62,6 +62,9 @@ BWD_SWEEP = [
     (1, 130, 2, 64, 32, 32, torch.float32, 0.1),
     (1, 200, 2, 128, 128, 64, torch.float32, 0.05),
     (2, 50, 2, 16, 64, 32, torch.float32, 0.3),
+    # 16-token chunks through the one-launch walks; more workgroups than CUs there
+    (2, 70, 3, 64, 64, 16, torch.float32, 0.2),
+    (8, 96, 6, 128, 128, 32, torch.float32, None),
     (1, 1, 2, 128, 128, 64, torch.bfloat16, 0.1),
     (1, 63, 2, 128, 128, 64, torch.bfloat16, None),
     (2, 65, 3, 128, 128, 64, torch.bfloat16, 0.02),
