@@ -342,8 +342,9 @@ GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int
  * operands and float32 accumulation, everything else float32 (K or V = 16: the
  * float32 path).  Every sum has a fixed order,
  * so results are bitwise reproducible; dq, dk, dv are rounded to dtype once.
- * All work is enqueued on `stream` alone (the MFMA path: three launches; its
- * two independent sequential walks share the second one).  No output may
+ * All work is enqueued on `stream` alone (three launches on both matrix-core
+ * paths, bf16 and float32 with V a multiple of 32: the two independent
+ * sequential walks share the second one).  No output may
  * overlap any other buffer (inputs, other outputs, workspace).  Errors as for
  * gdn_chunk_fwd; a workspace smaller than required is GDN_ERROR_INVALID_VALUE.
  */
